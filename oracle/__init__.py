@@ -1,0 +1,165 @@
+"""CPU oracle for masked (block-sparse) attention -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the benchmark's
+``cpu_baseline`` leg may import this package. It shares no code with the GPU
+path (``block_sparse_attention_fwd_amd``) and never imports it; the two meet
+only in the seeded input generators of ``workloads``.
+
+The arithmetic lives in ``oracle.c`` (plain fp64 C, OpenMP over rows); this
+file only builds it and marshals arguments. See ``oracle.c`` for what is
+computed and which passage of the source pages each rule follows.
+
+Parity pins (what the oracle is checked against, in ``tests/``): brute force
+with ``math.fsum`` on tiny inputs, a library attention routine (PyTorch CPU
+float64 scaled-dot-product attention with a boolean mask built independently),
+the definition's invariants (masked key == deleted key, block mask == its
+element expansion, key/value permutation invariance, token-permutation
+equivariance of temporal-major heads), closed forms (one kept key, constant V,
+empty row, score shift, query/key rescale) and closed-form pair counts of the
+video patterns. No function of this oracle is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+
+def build(src: str = _SRC, out: str = _LIB) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP). Returns the library path."""
+    cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-shared", "-fPIC", src, "-o", out + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+class OmMask(ctypes.Structure):
+    _fields_ = [
+        ("kind", ctypes.c_int32), ("B", ctypes.c_int32), ("H", ctypes.c_int32),
+        ("L", ctypes.c_int64),
+        ("bq", ctypes.c_int32), ("bk", ctypes.c_int32),
+        ("block_u8", ctypes.c_void_p), ("block_bits", ctypes.c_void_p),
+        ("row_ptr", ctypes.c_void_p), ("col_idx", ctypes.c_void_p),
+        ("head_pattern", ctypes.c_void_p),
+        ("anchor", ctypes.c_int32), ("radius", ctypes.c_int32),
+        ("T", ctypes.c_int32), ("Hg", ctypes.c_int32), ("Wg", ctypes.c_int32),
+        ("head_layout", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def lib(path: str = _LIB):
+    global _lib
+    if _lib is not None and path == _LIB:
+        return _lib
+    if not os.path.exists(path):
+        build(out=path)
+    L = ctypes.CDLL(path)
+    L.om_row_keys.restype = ctypes.c_int64
+    L.om_row_keys.argtypes = [ctypes.POINTER(OmMask), ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p]
+    L.om_attend.restype = None
+    L.om_attend.argtypes = [ctypes.POINTER(OmMask), ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    L.om_count_pairs.restype = ctypes.c_int64
+    L.om_count_pairs.argtypes = [ctypes.POINTER(OmMask), ctypes.c_int32, ctypes.c_int32]
+    L.om_block_union.restype = None
+    L.om_block_union.argtypes = [ctypes.POINTER(OmMask), ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                                 ctypes.c_void_p]
+    if path == _LIB:
+        _lib = L
+    return L
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+class Mask:
+    """Oracle-side view of a workload's logical mask (keeps arrays alive)."""
+
+    def __init__(self, w, bits: bool = False):
+        self.keep = []
+        m = OmMask()
+        m.kind = 2 if (bits and w.kind == 1) else w.kind
+        m.B, m.H, m.L = w.B, w.H, w.L
+        m.bq, m.bk = w.bq, w.bk
+        if w.kind == 1:
+            if bits:
+                arr = np.ascontiguousarray(w.block_bits())
+                m.block_bits = _ptr(arr)
+            else:
+                arr = np.ascontiguousarray(w.block, dtype=np.uint8)
+                m.block_u8 = _ptr(arr)
+            self.keep.append(arr)
+        if w.kind == 3:
+            rp = np.ascontiguousarray(w.row_ptr, dtype=np.int64)
+            ci = np.ascontiguousarray(w.col_idx, dtype=np.int32)
+            m.row_ptr, m.col_idx = _ptr(rp), _ptr(ci)
+            self.keep += [rp, ci]
+        if w.kind == 4:
+            hp = np.ascontiguousarray(w.head_pattern, dtype=np.uint8)
+            m.head_pattern = _ptr(hp)
+            self.keep.append(hp)
+        m.anchor, m.radius = w.anchor, w.radius
+        m.T, m.Hg, m.Wg = w.T, w.Hg, w.Wg
+        if w.head_layout is not None:
+            hl = np.ascontiguousarray(w.head_layout, dtype=np.uint8)
+            m.head_layout = _ptr(hl)
+            self.keep.append(hl)
+        self.m = m
+        self.L = w.L
+        self.H = w.H
+        self.B = w.B
+
+
+_DT = {np.dtype(np.uint16): 0, np.dtype(np.float32): 1, np.dtype(np.float64): 2}
+
+
+def attend(w, Q, K, V, rows=None, lib_path: str = _LIB, bits: bool = False, return_counts: bool = False):
+    """fp64 attention output. rows: flat row ids (b*H + h)*L + q (default all).
+    Returns [nrows][d] float64 (and per-row kept counts if asked)."""
+    L_ = lib(lib_path)
+    mk = Mask(w, bits=bits)
+    Q = np.ascontiguousarray(Q)
+    K = np.ascontiguousarray(K)
+    V = np.ascontiguousarray(V)
+    assert Q.dtype == K.dtype == V.dtype and Q.dtype in _DT
+    d = Q.shape[-1]
+    if rows is None:
+        rows = np.arange(w.B * w.H * w.L, dtype=np.int64)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    out = np.zeros((rows.size, d), np.float64)
+    cnt = np.zeros(rows.size, np.int64)
+    L_.om_attend(ctypes.byref(mk.m), d, _DT[Q.dtype], _ptr(Q), _ptr(K), _ptr(V), _ptr(rows), rows.size, _ptr(out),
+                 _ptr(cnt))
+    return (out, cnt) if return_counts else out
+
+
+def row_keys(w, b, h, q, lib_path: str = _LIB):
+    L_ = lib(lib_path)
+    mk = Mask(w)
+    buf = np.zeros(max(1, w.L), np.int32)
+    n = L_.om_row_keys(ctypes.byref(mk.m), b, h, q, _ptr(buf))
+    return buf[:n].copy()
+
+
+def count_pairs(w, b=0, h=0, lib_path: str = _LIB) -> int:
+    L_ = lib(lib_path)
+    mk = Mask(w)
+    return int(L_.om_count_pairs(ctypes.byref(mk.m), b, h))
+
+
+def block_union(w, b, h, blk, M=64, lib_path: str = _LIB):
+    L_ = lib(lib_path)
+    mk = Mask(w)
+    used = np.zeros(w.L, np.uint8)
+    L_.om_block_union(ctypes.byref(mk.m), b, h, blk, M, _ptr(used))
+    return used
