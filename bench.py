@@ -1,0 +1,220 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-sparse attention forward on one MI355X.
+
+Workload: Sparse VideoGen head routing -- B=1, 24 heads (12 spatial: same
+frame + frame 0; 12 temporal: same pixel +/-2 in y and x, every frame),
+L = 20,280 tokens (13 frames x 30x52), d = 128, bf16 Q/K/V ~ N(0,1) from
+fixed seeds. Run "B" (the headline) keeps the spatial heads frame-major and
+permutes the temporal heads to temporal-major order; run "A" is all
+frame-major and is reported beside it.
+
+One step = one BSA call for a fresh mask: bsa_plan (host mapping, regime
+lookup, task organisation, upload) + bsa_forward (the GPU kernel), with
+Q/K/V/O resident in HBM. Kernel time is measured with HIP events on the
+launch stream; effective TFLOP/s counts 4*d flops per kept (query, key) pair,
+with the kept pairs counted by the CPU oracle's own mask expansion.
+
+Prints one JSON line.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+sys.path.insert(0, os.path.join(ROOT, "tests"))
+
+MI355X_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
+MI355X_HBM_PEAK_GBS = 8000.0
+METRIC = "ms per BSA call; effective TFLOP/s on kept pairs and % of MI355X bf16 MFMA peak"
+KERNEL_SRC = os.path.join(ROOT, "block_sparse_attention_fwd_amd", "csrc", "attn_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_svg_runB.json")
+
+
+def kernel_hash():
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def time_run(w, Q, K, V, steps, warmup):
+    import torch
+
+    import block_sparse_attention_fwd_amd as bsa
+    from bsa_helpers import plan_workload
+    from gpu_util import to_device_bf16
+
+    q, k, v = to_device_bf16(Q), to_device_bf16(K), to_device_bf16(V)
+    o = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    # whole-path steps: plan + forward (plans kept alive until the timed region ends)
+    for _ in range(warmup):
+        p = plan_workload(w)
+        bsa.forward(p, q, k, v, o, stream)
+    torch.cuda.synchronize()
+    plans, ev = [], []
+    plan_s = 0.0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        tp = time.perf_counter()
+        p = plan_workload(w)
+        plan_s += time.perf_counter() - tp
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        bsa.forward(p, q, k, v, o, stream)
+        e1.record(stream)
+        plans.append(p)
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    step_ms = (t1 - t0) * 1e3 / steps
+    kern_ms_inline = sum(a.elapsed_time(b) for a, b in ev) / steps
+    info = plans[-1].info()
+    del plans
+
+    # forward-only launches back to back on a reused plan (kernel throughput)
+    p = plan_workload(w)
+    for _ in range(3):
+        bsa.forward(p, q, k, v, o, stream)
+    torch.cuda.synchronize()
+    ev = []
+    for _ in range(max(steps, 10)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        bsa.forward(p, q, k, v, o, stream)
+        e1.record(stream)
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    fwd = sorted(a.elapsed_time(b) for a, b in ev)
+    fwd_ms = sum(fwd) / len(fwd)
+    return {"step_ms": step_ms, "plan_ms": plan_s * 1e3 / steps, "fwd_ms": fwd_ms, "fwd_ms_median": fwd[len(fwd) // 2],
+            "fwd_ms_inline": kern_ms_inline, "plan_info": info}, o
+
+
+def parity_sample(w, Q, K, V, o):
+    import numpy as np
+
+    from gpu_util import compare, sample_rows
+    O = o.float().cpu().numpy().astype(np.float64)
+    rows = sample_rows(w, per_head=8)
+    mx, mean = compare(w, Q, K, V, O, rows=rows, label="bench sample")
+    return {"rows": int(rows.size), "max_abs": mx, "mean_abs": mean}
+
+
+def cpu_baseline(w, Q, K, V, P_total, rows_per_head):
+    import numpy as np
+
+    import oracle
+    g = np.random.default_rng(123)
+    rows = np.concatenate([h * w.L + g.choice(w.L, rows_per_head, replace=False) for h in range(w.H)]).astype(np.int64)
+    oracle.lib()
+    t0 = time.perf_counter()
+    _, cnt = oracle.attend(w, Q, K, V, rows=rows, return_counts=True)
+    dt = time.perf_counter() - t0
+    P_sample = int(cnt.sum())
+    ms_per_call = dt * 1e3 * P_total / P_sample
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": ms_per_call, "unit": "ms", "cores": cores, "kind": "oracle",
+            "sample": f"{rows.size} random query rows ({rows_per_head} per head, all 24 heads), {P_sample} kept pairs "
+                      f"in {dt:.2f} s, scaled by total/sampled kept pairs ({P_total}/{P_sample})",
+            "effective_gflops": 4 * w.d * P_sample / dt / 1e9}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-rows-per-head", type=int, default=512)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-parity", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE {world}); heads would be sharded across GPUs with no exchange, see DESIGN.md.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import oracle
+    import workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    wA, wB = wl.svg("A"), wl.svg("B")
+    log("[bench] generating inputs")
+    Q, K, V = wl.make_qkv(wB)
+    log("[bench] counting kept pairs with the oracle")
+    per_pattern = {}
+    P = 0
+    for h in range(wB.H):
+        pat = int(wB.head_pattern[h])
+        if pat not in per_pattern:
+            per_pattern[pat] = oracle.count_pairs(wB, 0, h)
+        P += per_pattern[pat]
+    flops = 4 * wB.d * P
+
+    res = {}
+    for name, w in (("A", wA), ("B", wB)):
+        log(f"[bench] run {name}: warmup {args.warmup}, steps {args.steps}")
+        r, o = time_run(w, Q, K, V, args.steps, args.warmup)
+        if not args.no_parity:
+            r["parity"] = parity_sample(w, Q, K, V, o)
+        r["effective_tflops_step"] = flops / (r["step_ms"] * 1e-3) / 1e12
+        r["effective_tflops_fwd"] = flops / (r["fwd_ms"] * 1e-3) / 1e12
+        r["pct_bf16_peak_fwd"] = 100.0 * r["effective_tflops_fwd"] / MI355X_BF16_PEAK_TFLOPS
+        res[name] = r
+        log(f"[bench] run {name}: {json.dumps(r)}")
+
+    B = res["B"]
+    achieved = flops / (B["fwd_ms"] * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        t = json.load(open(TRAFFIC_FILE))
+        if t.get("kernel_sha") == kernel_hash():
+            traffic = t["bytes_per_launch"]
+    out = {
+        "metric": METRIC,
+        "value": round(B["step_ms"], 4),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(B["step_ms"], 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "svg-head-routing run B (spatial heads frame-major, temporal heads temporal-major)",
+                   "B": 1, "H": 24, "L": wB.L, "frames": wB.T, "grid": [wB.Hg, wB.Wg], "d": wB.d,
+                   "heads": "12 spatial (same frame + frame 0), 12 temporal (|dy|,|dx| <= 2, all frames)",
+                   "kept_pairs": P, "step": "bsa_plan + bsa_forward"},
+        "fwd_ms": round(B["fwd_ms"], 4),
+        "plan_ms": round(B["plan_ms"], 4),
+        "effective_tflops_step": round(B["effective_tflops_step"], 2),
+        "effective_tflops_fwd": round(B["effective_tflops_fwd"], 2),
+        "pct_bf16_peak_fwd": round(B["pct_bf16_peak_fwd"], 2),
+        "run_A": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in res["A"].items() if k != "plan_info"},
+        "run_B_plan": B["plan_info"],
+        "parity": B.get("parity"),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MI355X_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MI355X_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+                     "kernel": "bsa_fwd_bf16<4,128>", "flops_per_launch": flops},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on a row sample")
+        out["cpu_baseline"] = cpu_baseline(wB, Q, K, V, P, args.cpu_rows_per_head)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

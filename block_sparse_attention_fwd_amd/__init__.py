@@ -1,0 +1,226 @@
+"""Python binding of the gfx950 block-sparse attention library (libbsa.so).
+
+Argument marshalling only: every step of the forward pass runs in the
+library's host planner and HIP kernels. PyTorch tensors are accepted for the
+device buffers (only their data pointers and the stream handle are used); the
+logical mask is host memory (numpy arrays).
+
+The names follow the C ABI in ``include/bsa.h``:
+``plan`` (bsa_plan), ``forward`` (bsa_forward), ``Plan.info``
+(bsa_plan_info), ``Plan.coverage`` (bsa_plan_coverage).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbsa.so")
+
+# enums of bsa.h
+OK, ERR_INVALID_ARGUMENT, ERR_INVALID_MASK, ERR_UNSUPPORTED, ERR_OUT_OF_MEMORY, ERR_HIP, ERR_INTERNAL = range(7)
+MASK_BLOCK_U8, MASK_BLOCK_BITS, MASK_SLICE_CSR, MASK_VIDEO = 1, 2, 3, 4
+PAT_DENSE, PAT_SPATIAL, PAT_TEMPORAL = 0, 1, 2
+LAYOUT_FRAME_MAJOR, LAYOUT_TEMPORAL_MAJOR = 0, 1
+DTYPE_BF16, DTYPE_F32 = 0, 1
+TILE_FULL, TILE_PARTIAL = 0, 1
+PRED_NONE, PRED_SUBBLOCK, PRED_VIDEO, PRED_LIST = 0, 1, 2, 3
+
+EXPORTED = ["bsa_abi_version", "bsa_plan_opts_default", "bsa_plan", "bsa_forward", "bsa_plan_destroy",
+            "bsa_plan_info", "bsa_plan_coverage", "bsa_regime_count", "bsa_regime_info", "bsa_status_str",
+            "bsa_last_error"]
+
+
+class MaskDesc(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("data", ctypes.c_void_p), ("row_ptr", ctypes.c_void_p),
+                ("col_idx", ctypes.c_void_p), ("head_pattern", ctypes.c_void_p), ("anchor_frame", ctypes.c_int32),
+                ("radius", ctypes.c_int32)]
+
+
+class PlanOpts(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("T", ctypes.c_int32), ("Hg", ctypes.c_int32), ("Wg", ctypes.c_int32),
+                ("head_layout", ctypes.c_void_p), ("force_regime", ctypes.c_int32), ("lut_path", ctypes.c_char_p),
+                ("device", ctypes.c_int32)]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("regime", ctypes.c_int32), ("tile_q", ctypes.c_int32), ("tile_k", ctypes.c_int32),
+                ("gather", ctypes.c_int32), ("tasks", ctypes.c_int64), ("tiles_full", ctypes.c_int64),
+                ("tiles_partial", ctypes.c_int64), ("tiles_empty", ctypes.c_int64), ("gather_rows", ctypes.c_int64),
+                ("executed_pairs", ctypes.c_double), ("device_bytes", ctypes.c_int64), ("plan_ns", ctypes.c_int64)]
+
+    def as_dict(self):
+        return {k: getattr(self, k) for k, _ in self._fields_}
+
+
+class RegimeDesc(ctypes.Structure):
+    _fields_ = [("family", ctypes.c_int32), ("tile_q", ctypes.c_int32), ("tile_k", ctypes.c_int32),
+                ("waves", ctypes.c_int32)]
+
+
+class TileRecord(ctypes.Structure):
+    _fields_ = [("q0", ctypes.c_int64), ("q1", ctypes.c_int64), ("kind", ctypes.c_int32),
+                ("predicate", ctypes.c_int32), ("k0", ctypes.c_int64), ("k1", ctypes.c_int64),
+                ("keys", ctypes.POINTER(ctypes.c_int32)), ("nkeys", ctypes.c_int64), ("sub_bits", ctypes.c_uint32),
+                ("sub_q", ctypes.c_int32), ("sub_k", ctypes.c_int32)]
+
+
+SINK = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p, ctypes.POINTER(TileRecord))
+
+_lib = None
+
+
+def lib(path: str = LIB_PATH):
+    """Load libbsa.so; raises if it has not been built (there is no fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build() (no CPU fallback exists)")
+    L = ctypes.CDLL(path)
+    L.bsa_abi_version.restype = ctypes.c_int32
+    L.bsa_plan_opts_default.argtypes = [ctypes.POINTER(PlanOpts)]
+    L.bsa_plan.restype = ctypes.c_int32
+    L.bsa_plan.argtypes = [ctypes.POINTER(MaskDesc), ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+                           ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(PlanOpts), ctypes.POINTER(ctypes.c_void_p)]
+    L.bsa_forward.restype = ctypes.c_int32
+    L.bsa_forward.argtypes = [ctypes.c_void_p] * 6
+    L.bsa_plan_destroy.argtypes = [ctypes.c_void_p]
+    L.bsa_plan_info.restype = ctypes.c_int32
+    L.bsa_plan_info.argtypes = [ctypes.c_void_p, ctypes.POINTER(PlanInfo)]
+    L.bsa_plan_coverage.restype = ctypes.c_int32
+    L.bsa_plan_coverage.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, SINK, ctypes.c_void_p]
+    L.bsa_regime_count.restype = ctypes.c_int32
+    L.bsa_regime_info.restype = ctypes.c_int32
+    L.bsa_regime_info.argtypes = [ctypes.c_int32, ctypes.POINTER(RegimeDesc)]
+    L.bsa_status_str.restype = ctypes.c_char_p
+    L.bsa_status_str.argtypes = [ctypes.c_int32]
+    L.bsa_last_error.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+class BSAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def _check(status: int):
+    if status != OK:
+        raise BSAError(status, lib().bsa_last_error().decode())
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data
+
+
+def _dptr(t):
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+class Plan:
+    """An immutable execution plan (owns its host and device memory)."""
+
+    def __init__(self, handle: int, L: int, H: int, B: int):
+        self._h = handle
+        self.L, self.H, self.B = L, H, B
+
+    @property
+    def handle(self):
+        return self._h
+
+    def info(self) -> dict:
+        out = PlanInfo()
+        _check(lib().bsa_plan_info(self._h, ctypes.byref(out)))
+        return out.as_dict()
+
+    def coverage(self, b: int, h: int):
+        """Tile records of head (b, h) in task order, as dicts."""
+        recs = []
+
+        def sink(user, rp):
+            r = rp.contents
+            d = {"q0": r.q0, "q1": r.q1, "kind": r.kind, "predicate": r.predicate, "k0": r.k0, "k1": r.k1,
+                 "sub_bits": r.sub_bits, "sub_q": r.sub_q, "sub_k": r.sub_k}
+            if r.predicate == PRED_LIST:
+                d["keys"] = np.ctypeslib.as_array(r.keys, shape=(r.nkeys,)).copy() if r.nkeys else np.zeros(0, np.int32)
+            recs.append(d)
+            return 0
+
+        cb = SINK(sink)
+        _check(lib().bsa_plan_coverage(self._h, b, h, cb, None))
+        return recs
+
+    def close(self):
+        if self._h:
+            lib().bsa_plan_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def plan(kind: int, B: int, H: int, L: int, d: int, block_q: int, block_k: int, *, data=None, row_ptr=None,
+         col_idx=None, head_pattern=None, anchor_frame: int = 0, radius: int = 2, dtype: int = DTYPE_BF16,
+         T: int = 0, Hg: int = 0, Wg: int = 0, head_layout=None, force_regime: int = -1,
+         lut_path: Optional[str] = None, device: int = 0) -> Plan:
+    """bsa_plan: build a plan for a logical mask (host numpy arrays)."""
+    L_ = lib()
+    keep = []
+
+    def arr(x, dt):
+        if x is None:
+            return None
+        a = np.ascontiguousarray(x, dtype=dt)
+        keep.append(a)
+        return a
+
+    m = MaskDesc()
+    m.kind = kind
+    m.data = _ptr(arr(data, np.uint8 if kind == MASK_BLOCK_U8 else np.uint64))
+    m.row_ptr = _ptr(arr(row_ptr, np.int64))
+    m.col_idx = _ptr(arr(col_idx, np.int32))
+    m.head_pattern = _ptr(arr(head_pattern, np.uint8))
+    m.anchor_frame = anchor_frame
+    m.radius = radius
+    o = PlanOpts()
+    L_.bsa_plan_opts_default(ctypes.byref(o))
+    o.dtype = dtype
+    o.T, o.Hg, o.Wg = T, Hg, Wg
+    o.head_layout = _ptr(arr(head_layout, np.uint8))
+    o.force_regime = force_regime
+    o.lut_path = lut_path.encode() if lut_path else None
+    o.device = device
+    h = ctypes.c_void_p()
+    _check(L_.bsa_plan(ctypes.byref(m), B, H, L, d, block_q, block_k, ctypes.byref(o), ctypes.byref(h)))
+    return Plan(h.value, L, H, B)
+
+
+def forward(p: Plan, q, k, v, o, stream=None) -> None:
+    """bsa_forward: enqueue the forward pass on `stream` (torch stream, raw
+    hipStream_t as int, or None for the current torch stream)."""
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream().cuda_stream
+    elif not isinstance(stream, int):
+        stream = stream.cuda_stream
+    _check(lib().bsa_forward(p.handle, _dptr(q), _dptr(k), _dptr(v), _dptr(o), stream))
+
+
+def regimes():
+    L_ = lib()
+    out = []
+    for r in range(L_.bsa_regime_count()):
+        d = RegimeDesc()
+        _check(L_.bsa_regime_info(r, ctypes.byref(d)))
+        out.append({"family": d.family, "tile_q": d.tile_q, "tile_k": d.tile_k, "waves": d.waves})
+    return out

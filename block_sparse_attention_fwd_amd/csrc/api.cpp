@@ -1,0 +1,860 @@
+// Host side of the block-sparse attention library: the C ABI, logical-mask
+// ingest and validation, physical mapping of logical blocks onto tiles, the
+// profile-guided regime lookup, task organisation and the single upload of a
+// plan to the device.
+//
+// Method sources (cited by title and section):
+//  - Tessera (arXiv 2609.25869), abstract: logical masks decoupled from GPU
+//    execution; a physical mapping layer that retains, combines or subdivides
+//    logical blocks into physical tiles; a task organisation layer that groups
+//    tiles into GPU tasks for data reuse, parallelism and load/compute
+//    overlap; regime selection through a lookup table built by offline
+//    profiling, to keep preparation cheap.
+//  - Sparse VideoGen / Splash Attention summary ("Sparse VideoGen", "Splash
+//    Attention"): spatial/temporal head patterns, empty tiles skipped, exact
+//    coordinate masking on boundary tiles only, temporal-major token layout.
+//  - FG-Attn (arXiv 2509.16518), abstract: M x 1 slices whose selected keys
+//    are gathered into packed tiles.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <chrono>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <fstream>
+#include <memory>
+#include <new>
+#include <sstream>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "../../include/bsa.h"
+#include "plan_format.hpp"
+
+namespace bsa {
+hipError_t launch_forward(const KernelArgs &a, int waves, int d, int dtype, hipStream_t stream);
+}
+
+using namespace bsa;
+
+// ---------------------------------------------------------------------------
+// errors
+// ---------------------------------------------------------------------------
+
+static thread_local std::string g_last_error;
+
+static int32_t fail(int32_t status, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = std::string(bsa_status_str(status)) + ": " + buf;
+    return status;
+}
+
+extern "C" const char *bsa_status_str(int32_t s)
+{
+    switch (s) {
+    case BSA_OK: return "BSA_OK";
+    case BSA_ERR_INVALID_ARGUMENT: return "BSA_ERR_INVALID_ARGUMENT";
+    case BSA_ERR_INVALID_MASK: return "BSA_ERR_INVALID_MASK";
+    case BSA_ERR_UNSUPPORTED: return "BSA_ERR_UNSUPPORTED";
+    case BSA_ERR_OUT_OF_MEMORY: return "BSA_ERR_OUT_OF_MEMORY";
+    case BSA_ERR_HIP: return "BSA_ERR_HIP";
+    case BSA_ERR_INTERNAL: return "BSA_ERR_INTERNAL";
+    default: return "BSA_ERR_UNKNOWN";
+    }
+}
+
+extern "C" const char *bsa_last_error(void) { return g_last_error.c_str(); }
+
+extern "C" int32_t bsa_abi_version(void) { return BSA_ABI_VERSION; }
+
+// ---------------------------------------------------------------------------
+// regimes and the lookup table
+// ---------------------------------------------------------------------------
+
+struct Regime {
+    int family;  // 0 = contiguous / permuted key tiles, 1 = gathered key lists
+    int tile_q;
+    int waves;
+};
+
+static const Regime kRegimes[] = {
+    {0, 128, 4},  // 0: 128 x 64 tiles
+    {0, 64, 2},   // 1: 64 x 64 tiles
+    {1, 64, 2},   // 2: 64-query gather tiles
+    {1, 128, 4},  // 3: 128-query gather tiles
+};
+static const int kNumRegimes = (int)(sizeof kRegimes / sizeof kRegimes[0]);
+
+extern "C" int32_t bsa_regime_count(void) { return kNumRegimes; }
+
+extern "C" int32_t bsa_regime_info(int32_t r, bsa_regime_desc_t *out)
+{
+    if (!out || r < 0 || r >= kNumRegimes) return fail(BSA_ERR_INVALID_ARGUMENT, "regime %d out of range", r);
+    out->family = kRegimes[r].family;
+    out->tile_q = kRegimes[r].tile_q;
+    out->tile_k = kTileK;
+    out->waves = kRegimes[r].waves;
+    return BSA_OK;
+}
+
+// Lookup-table rule: first matching line wins. Fields:
+//   kind block_q block_k density_lo density_hi L_lo L_hi regime
+// kind is block|slice|video; block sizes may be '*'.
+struct LutRule {
+    int kind;  // BSA_MASK_BLOCK_U8 (both block kinds), SLICE, VIDEO
+    int bq, bk;  // 0 = any
+    double dlo, dhi;
+    int64_t Llo, Lhi;
+    int regime;
+};
+
+#include "lut_default.inc"  // defines kDefaultLut (text of lut/gfx950.lut)
+
+static bool parse_lut(const std::string &text, std::vector<LutRule> &rules, std::string &err)
+{
+    std::istringstream in(text);
+    std::string line;
+    int ln = 0;
+    while (std::getline(in, line)) {
+        ++ln;
+        auto hash = line.find('#');
+        if (hash != std::string::npos) line.resize(hash);
+        std::istringstream ls(line);
+        std::string kind, bq, bk;
+        LutRule r{};
+        if (!(ls >> kind)) continue;
+        if (!(ls >> bq >> bk >> r.dlo >> r.dhi >> r.Llo >> r.Lhi >> r.regime)) {
+            err = "lookup table line " + std::to_string(ln) + " malformed";
+            return false;
+        }
+        if (kind == "block") r.kind = BSA_MASK_BLOCK_U8;
+        else if (kind == "slice") r.kind = BSA_MASK_SLICE_CSR;
+        else if (kind == "video") r.kind = BSA_MASK_VIDEO;
+        else { err = "lookup table line " + std::to_string(ln) + ": unknown kind " + kind; return false; }
+        r.bq = bq == "*" ? 0 : std::atoi(bq.c_str());
+        r.bk = bk == "*" ? 0 : std::atoi(bk.c_str());
+        if (r.regime < 0 || r.regime >= kNumRegimes) {
+            err = "lookup table line " + std::to_string(ln) + ": regime out of range";
+            return false;
+        }
+        rules.push_back(r);
+    }
+    return true;
+}
+
+// ---------------------------------------------------------------------------
+// the plan object
+// ---------------------------------------------------------------------------
+
+struct bsa_plan_s {
+    int32_t B = 0, H = 0, d = 0, dtype = 0;
+    int64_t L = 0;
+    int32_t kind = 0, block_q = 0, block_k = 0;
+    int32_t regime = 0;
+    int32_t T = 0, Hg = 0, Wg = 0, anchor = 0, radius = 0;
+    int32_t bq_shift = 0, bk_shift = 0, nsk = 1, sub_q = 0, sub_k = 0;
+    int32_t mode = 0;
+    std::vector<uint8_t> head_layout, head_pattern;
+    std::vector<Task> tasks;
+    std::vector<TileRec> tiles;
+    std::vector<int32_t> gidx;
+    std::vector<uint32_t> head_flags;
+    // statistics
+    int64_t tiles_full = 0, tiles_partial = 0, tiles_empty = 0, gather_rows = 0;
+    int64_t plan_ns = 0;
+    // device copy
+    int32_t device = -1;
+    void *dev = nullptr;
+    size_t dev_bytes = 0;
+    const Task *d_tasks = nullptr;
+    const TileRec *d_tiles = nullptr;
+    const int32_t *d_gidx = nullptr;
+    const uint32_t *d_head_flags = nullptr;
+};
+
+static int ilog2(int v)
+{
+    int s = 0;
+    while ((1 << s) < v) ++s;
+    return s;
+}
+static bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+// ---------------------------------------------------------------------------
+// video-pattern tile classification (exact-safe: EMPTY and FULL are claimed
+// only when true for every pair; anything else is PARTIAL and masked exactly
+// on the device)
+// ---------------------------------------------------------------------------
+
+namespace {
+
+struct Geo {
+    int64_t L, T, HW, W;
+};
+
+struct Rect {
+    int64_t y0, y1, x0, x1;
+};
+
+// Frames covered by logical positions [lo, hi] of a head, as a 64-bit set
+// (T <= 64) or as "all" when it cannot be represented exactly.
+struct FrameSet {
+    bool all;
+    uint64_t bits;
+};
+
+inline FrameSet frames_of(const Geo &g, bool tm, int64_t lo, int64_t hi)
+{
+    FrameSet f{false, 0};
+    if (g.T > 64) { f.all = true; return f; }
+    if (!tm) {
+        int64_t a = lo / g.HW, b = hi / g.HW;
+        for (int64_t t = a; t <= b; ++t) f.bits |= 1ull << t;
+        return f;
+    }
+    int64_t n = hi - lo + 1;
+    if (n >= g.T) { f.bits = g.T == 64 ? ~0ull : ((1ull << g.T) - 1); return f; }
+    for (int64_t i = 0; i < n; ++i) f.bits |= 1ull << ((lo + i) % g.T);
+    return f;
+}
+
+inline void range_rects(const Geo &g, int64_t p0, int64_t p1, std::vector<Rect> &out)
+{
+    int64_t y0 = p0 / g.W, x0 = p0 % g.W, y1 = p1 / g.W, x1 = p1 % g.W;
+    if (y0 == y1) { out.push_back({y0, y0, x0, x1}); return; }
+    out.push_back({y0, y0, x0, g.W - 1});
+    if (y1 > y0 + 1) out.push_back({y0 + 1, y1 - 1, 0, g.W - 1});
+    out.push_back({y1, y1, 0, x1});
+}
+
+// Pixels covered by logical positions [lo, hi] of a head.
+inline void pixel_rects(const Geo &g, bool tm, int64_t lo, int64_t hi, std::vector<Rect> &out)
+{
+    out.clear();
+    if (tm) { range_rects(g, lo / g.T, hi / g.T, out); return; }
+    if (hi - lo + 1 >= g.HW) { range_rects(g, 0, g.HW - 1, out); return; }
+    int64_t p0 = lo % g.HW, p1 = hi % g.HW;
+    if (p0 <= p1) range_rects(g, p0, p1, out);
+    else { range_rects(g, p0, g.HW - 1, out); range_rects(g, 0, p1, out); }
+}
+
+inline int64_t gap(int64_t a0, int64_t a1, int64_t b0, int64_t b1) { return std::max<int64_t>({0, b0 - a1, a0 - b1}); }
+inline int64_t span(int64_t a0, int64_t a1, int64_t b0, int64_t b1) { return std::max(a1 - b0, b1 - a0); }
+
+enum { kEmpty = 0, kFull = 1, kPart = 2 };
+
+struct VideoTileSets {
+    FrameSet f;
+    std::vector<Rect> r;
+};
+
+inline int classify_video(int pattern, int64_t anchor, int64_t radius, const VideoTileSets &q, const VideoTileSets &k,
+                          bool key_crop)
+{
+    bool any, all;
+    if (pattern == BSA_PAT_DENSE) {
+        any = all = true;
+    } else if (pattern == BSA_PAT_SPATIAL) {
+        if (q.f.all || k.f.all) {
+            any = true;
+            all = false;
+        } else {
+            bool a_in_k = anchor < 64 && ((k.f.bits >> anchor) & 1);
+            any = (q.f.bits & k.f.bits) != 0 || a_in_k;
+            // every key frame must be the anchor, or the single query frame
+            all = true;
+            uint64_t kb = k.f.bits;
+            bool q_single = q.f.bits && !(q.f.bits & (q.f.bits - 1));
+            while (kb) {
+                int t = __builtin_ctzll(kb);
+                kb &= kb - 1;
+                if (t == anchor) continue;
+                if (!(q_single && ((q.f.bits >> t) & 1))) { all = false; break; }
+            }
+        }
+    } else {
+        any = false;
+        all = true;
+        for (const Rect &a : q.r)
+            for (const Rect &b : k.r) {
+                if (std::max(gap(a.y0, a.y1, b.y0, b.y1), gap(a.x0, a.x1, b.x0, b.x1)) <= radius) any = true;
+                if (std::max(span(a.y0, a.y1, b.y0, b.y1), span(a.x0, a.x1, b.x0, b.x1)) > radius) all = false;
+            }
+    }
+    if (!any) return kEmpty;
+    if (all && !key_crop) return kFull;
+    return kPart;
+}
+
+// Per-head output of the mapping, later concatenated.
+struct HeadOut {
+    std::vector<Task> tasks;
+    std::vector<TileRec> tiles;  // k0/offsets relative to this head's gidx block
+    std::vector<int32_t> gidx;
+    int64_t full = 0, part = 0, empty = 0, grows = 0;
+    int32_t status = BSA_OK;
+    std::string err;
+};
+
+template <class F>
+void parallel_for(int64_t n, F &&f)
+{
+    unsigned hc = std::thread::hardware_concurrency();
+    int nt = (int)std::min<int64_t>(n, std::max(1u, std::min(hc, 32u)));
+    if (nt <= 1) {
+        for (int64_t i = 0; i < n; ++i) f(i);
+        return;
+    }
+    std::atomic<int64_t> next{0};
+    std::vector<std::thread> th;
+    for (int t = 0; t < nt; ++t)
+        th.emplace_back([&] {
+            for (int64_t i; (i = next.fetch_add(1)) < n;) f(i);
+        });
+    for (auto &x : th) x.join();
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// physical mapping per head
+// ---------------------------------------------------------------------------
+
+// BLOCK masks: retain (bq = tile_q, bk = tile_k), combine (smaller logical
+// blocks merged into one tile, kept sub-blocks recorded as bits) or subdivide
+// (larger logical blocks split over several tiles).
+static void map_block_head(const bsa_plan_s &p, const bsa_mask_desc_t &m, int b, int h, int BQ, HeadOut &out)
+{
+    const int64_t L = p.L;
+    const int64_t nqb = (L + p.block_q - 1) / p.block_q, nkb = (L + p.block_k - 1) / p.block_k;
+    const int64_t nqt = (L + BQ - 1) / BQ, nkt = (L + kTileK - 1) / kTileK;
+    const int bqe = std::min(p.block_q, BQ), bke = std::min(p.block_k, kTileK);
+    const int nsq = BQ / bqe, nsk = kTileK / bke;
+    const int64_t bh = (int64_t)b * p.H + h;
+    const int64_t words = (nkb + 63) / 64;
+    const uint8_t *u8 = m.kind == BSA_MASK_BLOCK_U8 ? (const uint8_t *)m.data + bh * nqb * nkb : nullptr;
+    const uint64_t *bits = m.kind == BSA_MASK_BLOCK_BITS ? (const uint64_t *)m.data + bh * nqb * words : nullptr;
+    std::vector<uint32_t> acc(nkt, 0);
+    out.tasks.reserve(nqt);
+    for (int64_t tq = 0; tq < nqt; ++tq) {
+        const int64_t q0 = tq * BQ, q1 = std::min<int64_t>(q0 + BQ, L);
+        const int64_t qb0 = q0 / p.block_q, qb1 = (q1 - 1) / p.block_q;
+        std::fill(acc.begin(), acc.end(), 0u);
+        for (int64_t qb = qb0; qb <= qb1; ++qb) {
+            const int sq = (int)((qb * p.block_q - q0) / bqe) < 0 ? 0 : (int)((qb * p.block_q - q0) / bqe);
+            auto mark = [&](int64_t kb) {
+                const int64_t k_lo = kb * p.block_k, k_hi = std::min<int64_t>(k_lo + p.block_k, L) - 1;
+                for (int64_t tk = k_lo / kTileK; tk <= k_hi / kTileK; ++tk) {
+                    int sk = p.block_k <= kTileK ? (int)((k_lo - tk * kTileK) / bke) : 0;
+                    acc[tk] |= 1u << (sq * nsk + sk);
+                }
+            };
+            if (u8) {
+                const uint8_t *row = u8 + qb * nkb;
+                for (int64_t kb = 0; kb < nkb; ++kb)
+                    if (row[kb]) mark(kb);
+            } else {
+                const uint64_t *row = bits + qb * words;
+                for (int64_t w = 0; w < words; ++w)
+                    for (uint64_t x = row[w]; x; x &= x - 1) mark(w * 64 + __builtin_ctzll(x));
+            }
+        }
+        const int nsq_valid = (int)std::min<int64_t>(nsq, (q1 - 1 - q0) / bqe + 1);
+        Task t{(int32_t)bh, (int32_t)q0, (int32_t)out.tiles.size(), 0};
+        for (int64_t tk = 0; tk < nkt; ++tk) {
+            if (!acc[tk]) { ++out.empty; continue; }
+            const int64_t k0 = tk * kTileK, k1 = std::min<int64_t>(k0 + kTileK, L);
+            const int nsk_valid = (int)std::min<int64_t>(nsk, (k1 - 1 - k0) / bke + 1);
+            uint32_t want = 0;
+            for (int sq = 0; sq < nsq_valid; ++sq)
+                for (int sk = 0; sk < nsk_valid; ++sk) want |= 1u << (sq * nsk + sk);
+            const bool full = (acc[tk] & want) == want && k0 + kTileK <= L;
+            out.tiles.push_back({(int32_t)k0, acc[tk] | (full ? 0u : kPartial)});
+            if (full) ++out.full; else ++out.part;
+        }
+        t.te = (int32_t)out.tiles.size();
+        out.tasks.push_back(t);
+    }
+}
+
+// VIDEO masks: classify every (query tile, key tile) of the head's layout.
+static void map_video_head(const bsa_plan_s &p, int b, int h, int BQ, HeadOut &out)
+{
+    const int64_t L = p.L;
+    const Geo g{L, p.T, (int64_t)p.Hg * p.Wg, p.Wg};
+    const bool tm = p.head_layout[h] == BSA_LAYOUT_TEMPORAL_MAJOR;
+    const int pat = p.head_pattern[h];
+    const int64_t nqt = (L + BQ - 1) / BQ, nkt = (L + kTileK - 1) / kTileK;
+    const int64_t bh = (int64_t)b * p.H + h;
+    std::vector<VideoTileSets> ks(nkt);
+    for (int64_t tk = 0; tk < nkt; ++tk) {
+        int64_t k0 = tk * kTileK, k1 = std::min<int64_t>(k0 + kTileK, L);
+        if (pat == BSA_PAT_SPATIAL) ks[tk].f = frames_of(g, tm, k0, k1 - 1);
+        if (pat == BSA_PAT_TEMPORAL) pixel_rects(g, tm, k0, k1 - 1, ks[tk].r);
+    }
+    VideoTileSets qs;
+    out.tasks.reserve(nqt);
+    for (int64_t tq = 0; tq < nqt; ++tq) {
+        const int64_t q0 = tq * BQ, q1 = std::min<int64_t>(q0 + BQ, L);
+        if (pat == BSA_PAT_SPATIAL) qs.f = frames_of(g, tm, q0, q1 - 1);
+        if (pat == BSA_PAT_TEMPORAL) pixel_rects(g, tm, q0, q1 - 1, qs.r);
+        Task t{(int32_t)bh, (int32_t)q0, (int32_t)out.tiles.size(), 0};
+        for (int64_t tk = 0; tk < nkt; ++tk) {
+            const int64_t k0 = tk * kTileK;
+            int c = classify_video(pat, p.anchor, p.radius, qs, ks[tk], k0 + kTileK > L);
+            if (c == kEmpty) { ++out.empty; continue; }
+            out.tiles.push_back({(int32_t)k0, c == kFull ? 0u : kPartial});
+            if (c == kFull) ++out.full; else ++out.part;
+        }
+        t.te = (int32_t)out.tiles.size();
+        out.tasks.push_back(t);
+    }
+}
+
+// SLICE masks: each M-query block's sorted key list packed into gather tiles
+// of kTileK keys; only the last tile of a list can be short (masked).
+static void map_slice_head(const bsa_plan_s &p, const bsa_mask_desc_t &m, int b, int h, HeadOut &out)
+{
+    const int64_t L = p.L, M = p.block_q, nqb = (L + M - 1) / M;
+    const int64_t bh = (int64_t)b * p.H + h;
+    const int64_t base = m.row_ptr[bh * nqb];
+    const int64_t n_all = m.row_ptr[bh * nqb + nqb] - base;
+    out.gidx.assign(m.col_idx + base, m.col_idx + base + n_all);
+    out.grows = n_all;
+    for (int64_t i = 0; i < nqb; ++i) {
+        const int64_t s = m.row_ptr[bh * nqb + i] - base, e = m.row_ptr[bh * nqb + i + 1] - base;
+        Task t{(int32_t)bh, (int32_t)(i * M), (int32_t)out.tiles.size(), 0};
+        for (int64_t o = s; o < e; o += kTileK) {
+            uint32_t cnt = (uint32_t)std::min<int64_t>(kTileK, e - o);
+            out.tiles.push_back({(int32_t)o, cnt | (cnt < (uint32_t)kTileK ? kPartial : 0u)});
+            if (cnt < (uint32_t)kTileK) ++out.part; else ++out.full;
+        }
+        t.te = (int32_t)out.tiles.size();
+        out.tasks.push_back(t);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// validation (mask ingest)
+// ---------------------------------------------------------------------------
+
+static int32_t validate(const bsa_mask_desc_t *m, int32_t B, int32_t H, int64_t L, int32_t d, int32_t bq, int32_t bk,
+                        const bsa_plan_opts_t &o)
+{
+    if (!m) return fail(BSA_ERR_INVALID_ARGUMENT, "logical_mask is NULL");
+    if (B < 1 || H < 1 || L < 1) return fail(BSA_ERR_INVALID_ARGUMENT, "B, H, L must be >= 1 (got %d, %d, %lld)", B, H, (long long)L);
+    if (L > (1ll << 30)) return fail(BSA_ERR_UNSUPPORTED, "L = %lld exceeds 2^30", (long long)L);
+    if ((int64_t)B * H * L * 128 > (1ll << 31) * 64ll)
+        ;  // sizes are addressed with 64-bit arithmetic in the kernel; nothing to check here
+    if (d != 64 && d != 128) return fail(BSA_ERR_UNSUPPORTED, "head dim d = %d (supported: 64, 128)", d);
+    if (o.dtype != BSA_DTYPE_BF16 && o.dtype != BSA_DTYPE_F32) return fail(BSA_ERR_INVALID_ARGUMENT, "dtype %d", o.dtype);
+    if (o.dtype == BSA_DTYPE_F32) return fail(BSA_ERR_UNSUPPORTED, "fp32 plans are not built in this version");
+    const bool has_geo = o.T || o.Hg || o.Wg;
+    if (has_geo) {
+        if (o.T < 1 || o.Hg < 1 || o.Wg < 1 || (int64_t)o.T * o.Hg * o.Wg != L)
+            return fail(BSA_ERR_INVALID_ARGUMENT, "video geometry %d x %d x %d does not match L = %lld", o.T, o.Hg, o.Wg, (long long)L);
+        if (o.T > 2046 || o.Hg > 512 || o.Wg > 512)
+            return fail(BSA_ERR_UNSUPPORTED, "video geometry beyond T <= 2046, Hg <= 512, Wg <= 512");
+    }
+    if (o.head_layout) {
+        for (int h = 0; h < H; ++h) {
+            if (o.head_layout[h] > 1) return fail(BSA_ERR_INVALID_ARGUMENT, "head_layout[%d] = %d", h, o.head_layout[h]);
+            if (o.head_layout[h] == BSA_LAYOUT_TEMPORAL_MAJOR && !has_geo)
+                return fail(BSA_ERR_INVALID_ARGUMENT, "temporal-major head %d needs the video geometry", h);
+        }
+    }
+    if (o.force_regime < -1 || o.force_regime >= kNumRegimes)
+        return fail(BSA_ERR_INVALID_ARGUMENT, "force_regime %d out of range", o.force_regime);
+    switch (m->kind) {
+    case BSA_MASK_BLOCK_U8:
+    case BSA_MASK_BLOCK_BITS:
+        if (!m->data) return fail(BSA_ERR_INVALID_ARGUMENT, "block mask data is NULL");
+        if (!is_pow2(bq) || !is_pow2(bk) || bq < 32 || bk < 32 || bq > 1024 || bk > 1024)
+            return fail(BSA_ERR_UNSUPPORTED, "block shape %d x %d (supported: powers of two in [32, 1024])", bq, bk);
+        if (m->kind == BSA_MASK_BLOCK_BITS) {
+            const int64_t nqb = (L + bq - 1) / bq, nkb = (L + bk - 1) / bk, words = (nkb + 63) / 64;
+            if (nkb % 64) {
+                const uint64_t stray = ~0ull << (nkb % 64);
+                const uint64_t *w = (const uint64_t *)m->data;
+                for (int64_t r = 0; r < (int64_t)B * H * nqb; ++r)
+                    if (w[r * words + words - 1] & stray)
+                        return fail(BSA_ERR_INVALID_MASK, "bit row %lld has bits beyond key block %lld", (long long)r, (long long)nkb);
+            }
+        }
+        return BSA_OK;
+    case BSA_MASK_SLICE_CSR: {
+        if (!m->row_ptr || !m->col_idx) return fail(BSA_ERR_INVALID_ARGUMENT, "slice row_ptr/col_idx is NULL");
+        if (bk != 1) return fail(BSA_ERR_INVALID_ARGUMENT, "slice masks need block_k = 1 (got %d)", bk);
+        if (bq != 64 && bq != 128) return fail(BSA_ERR_UNSUPPORTED, "slice block M = %d (supported: 64, 128)", bq);
+        const int64_t nl = (int64_t)B * H * ((L + bq - 1) / bq);
+        if (m->row_ptr[0] != 0) return fail(BSA_ERR_INVALID_MASK, "row_ptr[0] = %lld, expected 0", (long long)m->row_ptr[0]);
+        for (int64_t i = 0; i < nl; ++i)
+            if (m->row_ptr[i + 1] < m->row_ptr[i]) return fail(BSA_ERR_INVALID_MASK, "row_ptr decreases at %lld", (long long)i);
+        if (m->row_ptr[nl] > (1ll << 31) - 1) return fail(BSA_ERR_UNSUPPORTED, "more than 2^31 - 1 slice keys");
+        std::atomic<int64_t> bad{-1};
+        parallel_for((nl + 1023) / 1024, [&](int64_t c) {
+            for (int64_t i = c * 1024; i < std::min(nl, c * 1024 + 1024); ++i)
+                for (int64_t e = m->row_ptr[i]; e < m->row_ptr[i + 1]; ++e) {
+                    int32_t k = m->col_idx[e];
+                    if (k < 0 || k >= L || (e > m->row_ptr[i] && k <= m->col_idx[e - 1])) {
+                        int64_t x = -1;
+                        bad.compare_exchange_strong(x, i);
+                        return;
+                    }
+                }
+        });
+        if (bad.load() >= 0)
+            return fail(BSA_ERR_INVALID_MASK, "slice list %lld is not strictly increasing within [0, L)", (long long)bad.load());
+        return BSA_OK;
+    }
+    case BSA_MASK_VIDEO:
+        if (!m->head_pattern) return fail(BSA_ERR_INVALID_ARGUMENT, "video head_pattern is NULL");
+        if (bq != 1 || bk != 1) return fail(BSA_ERR_INVALID_ARGUMENT, "video masks need block 1 x 1 (got %d x %d)", bq, bk);
+        if (!has_geo) return fail(BSA_ERR_INVALID_ARGUMENT, "video masks need the geometry T, Hg, Wg");
+        for (int h = 0; h < H; ++h)
+            if (m->head_pattern[h] > BSA_PAT_TEMPORAL)
+                return fail(BSA_ERR_INVALID_MASK, "head_pattern[%d] = %d", h, m->head_pattern[h]);
+        if (m->anchor_frame < 0 || m->anchor_frame >= o.T) return fail(BSA_ERR_INVALID_MASK, "anchor frame %d outside [0, %d)", m->anchor_frame, o.T);
+        if (m->radius < 0 || m->radius > 256) return fail(BSA_ERR_INVALID_MASK, "radius %d outside [0, 256]", m->radius);
+        return BSA_OK;
+    default:
+        return fail(BSA_ERR_INVALID_ARGUMENT, "unknown mask kind %d", m->kind);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// regime selection
+// ---------------------------------------------------------------------------
+
+static double mask_density(const bsa_mask_desc_t &m, int32_t B, int32_t H, int64_t L, int32_t bq, int32_t bk)
+{
+    if (m.kind == BSA_MASK_SLICE_CSR) {
+        const int64_t nl = (int64_t)B * H * ((L + bq - 1) / bq);
+        return (double)m.row_ptr[nl] / ((double)nl * (double)L);
+    }
+    if (m.kind == BSA_MASK_VIDEO) return -1.0;
+    const int64_t nqb = (L + bq - 1) / bq, nkb = (L + bk - 1) / bk;
+    const int64_t rows = (int64_t)B * H * nqb;
+    std::vector<int64_t> cnt(rows, 0);
+    if (m.kind == BSA_MASK_BLOCK_U8) {
+        const uint8_t *u = (const uint8_t *)m.data;
+        parallel_for(rows, [&](int64_t r) {
+            int64_t c = 0;
+            for (int64_t j = 0; j < nkb; ++j) c += u[r * nkb + j] != 0;
+            cnt[r] = c;
+        });
+    } else {
+        const int64_t words = (nkb + 63) / 64;
+        const uint64_t *w = (const uint64_t *)m.data;
+        parallel_for(rows, [&](int64_t r) {
+            int64_t c = 0;
+            for (int64_t j = 0; j < words; ++j) c += __builtin_popcountll(w[r * words + j]);
+            cnt[r] = c;
+        });
+    }
+    int64_t total = 0;
+    for (int64_t c : cnt) total += c;
+    return (double)total / ((double)rows * (double)nkb);
+}
+
+static int32_t choose_regime(const bsa_mask_desc_t &m, int32_t B, int32_t H, int64_t L, int32_t bq, int32_t bk,
+                             const bsa_plan_opts_t &o, int *regime)
+{
+    if (o.force_regime >= 0) {
+        *regime = o.force_regime;
+    } else {
+        std::vector<LutRule> rules;
+        std::string err, text = kDefaultLut;
+        if (o.lut_path) {
+            std::ifstream f(o.lut_path);
+            if (!f) return fail(BSA_ERR_INVALID_ARGUMENT, "cannot read lookup table %s", o.lut_path);
+            std::stringstream ss;
+            ss << f.rdbuf();
+            text = ss.str();
+        }
+        if (!parse_lut(text, rules, err)) return fail(BSA_ERR_INVALID_ARGUMENT, "%s", err.c_str());
+        const int kind = m.kind == BSA_MASK_BLOCK_BITS ? BSA_MASK_BLOCK_U8 : m.kind;
+        const double dens = mask_density(m, B, H, L, bq, bk);
+        *regime = -1;
+        for (const LutRule &r : rules) {
+            if (r.kind != kind) continue;
+            if (r.bq && r.bq != bq) continue;
+            if (r.bk && r.bk != bk) continue;
+            if (dens >= 0 && (dens < r.dlo || dens > r.dhi)) continue;
+            if (L < r.Llo || L > r.Lhi) continue;
+            *regime = r.regime;
+            break;
+        }
+        if (*regime < 0) *regime = m.kind == BSA_MASK_SLICE_CSR ? (bq == 128 ? 3 : 2) : 0;
+    }
+    const Regime &R = kRegimes[*regime];
+    const bool slice = m.kind == BSA_MASK_SLICE_CSR;
+    if (slice != (R.family == 1))
+        return fail(BSA_ERR_UNSUPPORTED, "regime %d (%s) cannot run %s masks", *regime, R.family ? "gather" : "tile",
+                    slice ? "slice" : "block/video");
+    if (slice && R.tile_q != bq) return fail(BSA_ERR_UNSUPPORTED, "gather regime %d has %d-query tiles, mask has M = %d", *regime, R.tile_q, bq);
+    return BSA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// task organisation
+// ---------------------------------------------------------------------------
+
+// One task per (batch, head, query tile) -- also for query tiles without any
+// key tile, so that every output row is written. Tasks are ordered longest
+// first (LPT) so the tail of the grid holds the cheapest work.
+static void organise_tasks(bsa_plan_s &p, std::vector<HeadOut> &heads)
+{
+    size_t nt = 0, nr = 0, ng = 0;
+    for (auto &h : heads) { nt += h.tasks.size(); nr += h.tiles.size(); ng += h.gidx.size(); }
+    p.tasks.reserve(nt);
+    p.tiles.reserve(nr);
+    p.gidx.reserve(ng);
+    for (auto &h : heads) {
+        const int32_t toff = (int32_t)p.tiles.size(), goff = (int32_t)p.gidx.size();
+        for (Task t : h.tasks) { t.tb += toff; t.te += toff; p.tasks.push_back(t); }
+        for (TileRec r : h.tiles) {
+            if (p.mode == kModeGather) r.k0 += goff;
+            p.tiles.push_back(r);
+        }
+        p.gidx.insert(p.gidx.end(), h.gidx.begin(), h.gidx.end());
+        p.tiles_full += h.full;
+        p.tiles_partial += h.part;
+        p.tiles_empty += h.empty;
+        p.gather_rows += h.grows;
+        std::vector<Task>().swap(h.tasks);
+        std::vector<TileRec>().swap(h.tiles);
+        std::vector<int32_t>().swap(h.gidx);
+    }
+    std::stable_sort(p.tasks.begin(), p.tasks.end(), [](const Task &a, const Task &b) { return (a.te - a.tb) > (b.te - b.tb); });
+}
+
+// ---------------------------------------------------------------------------
+// device upload
+// ---------------------------------------------------------------------------
+
+static size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static int32_t upload(bsa_plan_s &p)
+{
+    if (p.device < 0) return BSA_OK;
+    hipError_t e = hipSetDevice(p.device);
+    if (e != hipSuccess) return fail(BSA_ERR_HIP, "hipSetDevice(%d): %s", p.device, hipGetErrorString(e));
+    const size_t s_tasks = align_up(std::max<size_t>(1, p.tasks.size()) * sizeof(Task));
+    const size_t s_tiles = align_up(std::max<size_t>(1, p.tiles.size()) * sizeof(TileRec));
+    const size_t s_gidx = align_up(std::max<size_t>(1, p.gidx.size()) * sizeof(int32_t));
+    const size_t s_flags = align_up(p.head_flags.size() * sizeof(uint32_t));
+    p.dev_bytes = s_tasks + s_tiles + s_gidx + s_flags;
+    e = hipMalloc(&p.dev, p.dev_bytes);
+    if (e != hipSuccess) {
+        p.dev = nullptr;
+        return fail(e == hipErrorOutOfMemory ? BSA_ERR_OUT_OF_MEMORY : BSA_ERR_HIP, "hipMalloc(%zu): %s", p.dev_bytes,
+                    hipGetErrorString(e));
+    }
+    std::vector<uint8_t> host(p.dev_bytes, 0);
+    size_t off = 0;
+    auto put = [&](const void *src, size_t n, size_t sz) {
+        if (n) std::memcpy(host.data() + off, src, n);
+        size_t at = off;
+        off += sz;
+        return at;
+    };
+    size_t o_tasks = put(p.tasks.data(), p.tasks.size() * sizeof(Task), s_tasks);
+    size_t o_tiles = put(p.tiles.data(), p.tiles.size() * sizeof(TileRec), s_tiles);
+    size_t o_gidx = put(p.gidx.data(), p.gidx.size() * sizeof(int32_t), s_gidx);
+    size_t o_flags = put(p.head_flags.data(), p.head_flags.size() * sizeof(uint32_t), s_flags);
+    e = hipMemcpy(p.dev, host.data(), p.dev_bytes, hipMemcpyHostToDevice);
+    if (e != hipSuccess) return fail(BSA_ERR_HIP, "plan upload: %s", hipGetErrorString(e));
+    char *base = (char *)p.dev;
+    p.d_tasks = (const Task *)(base + o_tasks);
+    p.d_tiles = (const TileRec *)(base + o_tiles);
+    p.d_gidx = (const int32_t *)(base + o_gidx);
+    p.d_head_flags = (const uint32_t *)(base + o_flags);
+    return BSA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// C entry points
+// ---------------------------------------------------------------------------
+
+extern "C" void bsa_plan_opts_default(bsa_plan_opts_t *o)
+{
+    if (!o) return;
+    std::memset(o, 0, sizeof *o);
+    o->dtype = BSA_DTYPE_BF16;
+    o->force_regime = -1;
+    o->device = 0;
+}
+
+extern "C" int32_t bsa_plan(const bsa_mask_desc_t *logical_mask, int32_t B, int32_t H, int64_t L, int32_t d,
+                            int32_t block_q, int32_t block_k, const bsa_plan_opts_t *opts, bsa_plan_t *out_plan)
+{
+    if (!out_plan) return fail(BSA_ERR_INVALID_ARGUMENT, "out_plan is NULL");
+    *out_plan = nullptr;
+    const auto t_start = std::chrono::steady_clock::now();
+    try {
+        bsa_plan_opts_t o;
+        bsa_plan_opts_default(&o);
+        if (opts) o = *opts;
+        int32_t st = validate(logical_mask, B, H, L, d, block_q, block_k, o);
+        if (st != BSA_OK) return st;
+        if (std::getenv("BSA_TEST_FAIL_ALLOC")) return fail(BSA_ERR_OUT_OF_MEMORY, "simulated allocation failure");
+        const bsa_mask_desc_t &m = *logical_mask;
+        int regime = 0;
+        st = choose_regime(m, B, H, L, block_q, block_k, o, &regime);
+        if (st != BSA_OK) return st;
+
+        std::unique_ptr<bsa_plan_s> p(new bsa_plan_s);
+        p->B = B; p->H = H; p->L = L; p->d = d; p->dtype = o.dtype;
+        p->kind = m.kind; p->block_q = block_q; p->block_k = block_k;
+        p->regime = regime;
+        p->T = o.T; p->Hg = o.Hg; p->Wg = o.Wg;
+        p->anchor = m.anchor_frame; p->radius = m.radius;
+        p->device = o.device;
+        p->head_layout.assign(H, 0);
+        if (o.head_layout) p->head_layout.assign(o.head_layout, o.head_layout + H);
+        p->head_pattern.assign(H, 0);
+        if (m.kind == BSA_MASK_VIDEO) p->head_pattern.assign(m.head_pattern, m.head_pattern + H);
+        const Regime &R = kRegimes[regime];
+        p->mode = m.kind == BSA_MASK_VIDEO ? kModeVideo : (m.kind == BSA_MASK_SLICE_CSR ? kModeGather : kModeBlock);
+        if (p->mode == kModeBlock) {
+            p->sub_q = std::min(block_q, R.tile_q);
+            p->sub_k = std::min(block_k, kTileK);
+            p->bq_shift = ilog2(p->sub_q);
+            p->bk_shift = ilog2(p->sub_k);
+            p->nsk = kTileK / p->sub_k;
+        }
+        p->head_flags.resize(H);
+        for (int h = 0; h < H; ++h)
+            p->head_flags[h] = (p->head_layout[h] ? kHeadTemporalMajor : 0u) | ((uint32_t)p->head_pattern[h] << kHeadPatShift);
+
+        std::vector<HeadOut> heads((size_t)B * H);
+        parallel_for((int64_t)B * H, [&](int64_t bh) {
+            const int b = (int)(bh / H), h = (int)(bh % H);
+            if (p->mode == kModeBlock) map_block_head(*p, m, b, h, R.tile_q, heads[bh]);
+            else if (p->mode == kModeVideo) map_video_head(*p, b, h, R.tile_q, heads[bh]);
+            else map_slice_head(*p, m, b, h, heads[bh]);
+        });
+        size_t total_tiles = 0;
+        for (auto &h : heads) total_tiles += h.tiles.size();
+        if (total_tiles >= (size_t)INT32_MAX) return fail(BSA_ERR_UNSUPPORTED, "plan has more than 2^31 tiles");
+        organise_tasks(*p, heads);
+        st = upload(*p);
+        if (st != BSA_OK) {
+            if (p->dev) (void)hipFree(p->dev);
+            return st;
+        }
+        p->plan_ns = std::chrono::duration_cast<std::chrono::nanoseconds>(std::chrono::steady_clock::now() - t_start).count();
+        *out_plan = p.release();
+        return BSA_OK;
+    } catch (const std::bad_alloc &) {
+        return fail(BSA_ERR_OUT_OF_MEMORY, "host allocation failed while planning");
+    } catch (const std::exception &ex) {
+        return fail(BSA_ERR_INTERNAL, "%s", ex.what());
+    }
+}
+
+extern "C" void bsa_plan_destroy(bsa_plan_t p)
+{
+    if (!p) return;
+    if (p->dev) {
+        int cur = 0;
+        (void)hipGetDevice(&cur);
+        (void)hipSetDevice(p->device);
+        (void)hipFree(p->dev);
+        (void)hipSetDevice(cur);
+    }
+    delete p;
+}
+
+extern "C" int32_t bsa_forward(bsa_plan_t p, const void *Q, const void *K, const void *V, void *O, void *stream)
+{
+    if (!p) return fail(BSA_ERR_INVALID_ARGUMENT, "plan is NULL");
+    if (p->device < 0 || !p->dev) return fail(BSA_ERR_INVALID_ARGUMENT, "plan was built host-only (device = -1)");
+    if (!Q || !K || !V || !O) return fail(BSA_ERR_INVALID_ARGUMENT, "Q, K, V and O must be non-NULL device pointers");
+    if (((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O) & 15)
+        return fail(BSA_ERR_INVALID_ARGUMENT, "Q, K, V and O must be 16-byte aligned");
+    if (p->tasks.empty()) return BSA_OK;
+    KernelArgs a{};
+    a.Q = Q; a.K = K; a.V = V; a.O = O;
+    a.tasks = p->d_tasks;
+    a.tiles = p->d_tiles;
+    a.gidx = p->d_gidx;
+    a.head_flags = p->d_head_flags;
+    a.ntasks = (int32_t)p->tasks.size();
+    a.H = p->H;
+    a.L = (int32_t)p->L;
+    a.T = p->T; a.HW = p->Hg * p->Wg; a.W = p->Wg;
+    a.anchor = p->anchor; a.radius = p->radius;
+    a.mode = p->mode;
+    a.bq_shift = p->bq_shift; a.bk_shift = p->bk_shift; a.nsk = p->nsk;
+    a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p->d));
+    int cur = 0;
+    (void)hipGetDevice(&cur);
+    if (cur != p->device) (void)hipSetDevice(p->device);
+    hipError_t e = launch_forward(a, kRegimes[p->regime].waves, p->d, p->dtype, (hipStream_t)stream);
+    if (cur != p->device) (void)hipSetDevice(cur);
+    if (e != hipSuccess) return fail(BSA_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
+    return BSA_OK;
+}
+
+extern "C" int32_t bsa_plan_info(bsa_plan_t p, bsa_plan_info_t *out)
+{
+    if (!p || !out) return fail(BSA_ERR_INVALID_ARGUMENT, "plan or out is NULL");
+    const Regime &R = kRegimes[p->regime];
+    out->regime = p->regime;
+    out->tile_q = R.tile_q;
+    out->tile_k = kTileK;
+    out->gather = R.family;
+    out->tasks = (int64_t)p->tasks.size();
+    out->tiles_full = p->tiles_full;
+    out->tiles_partial = p->tiles_partial;
+    out->tiles_empty = p->tiles_empty;
+    out->gather_rows = p->gather_rows;
+    out->executed_pairs = (double)(p->tiles_full + p->tiles_partial) * R.tile_q * kTileK;
+    out->device_bytes = (int64_t)p->dev_bytes;
+    out->plan_ns = p->plan_ns;
+    return BSA_OK;
+}
+
+extern "C" int32_t bsa_plan_coverage(bsa_plan_t p, int32_t b, int32_t h, bsa_cov_sink_t sink, void *user)
+{
+    if (!p || !sink) return fail(BSA_ERR_INVALID_ARGUMENT, "plan or sink is NULL");
+    if (b < 0 || b >= p->B || h < 0 || h >= p->H) return fail(BSA_ERR_INVALID_ARGUMENT, "head (%d, %d) out of range", b, h);
+    const Regime &R = kRegimes[p->regime];
+    const int32_t bh = b * p->H + h;
+    for (const Task &t : p->tasks) {
+        if (t.bh != bh) continue;
+        for (int32_t i = t.tb; i < t.te; ++i) {
+            const TileRec &r = p->tiles[i];
+            bsa_tile_record_t rec{};
+            rec.q0 = t.q0;
+            rec.q1 = std::min<int64_t>(t.q0 + R.tile_q, p->L);
+            rec.kind = (r.aux & kPartial) ? BSA_TILE_PARTIAL : BSA_TILE_FULL;
+            if (p->mode == kModeGather) {
+                rec.predicate = BSA_PRED_LIST;
+                rec.keys = p->gidx.data() + r.k0;
+                rec.nkeys = r.aux & kAuxMask;
+            } else {
+                rec.predicate = p->mode == kModeBlock ? BSA_PRED_SUBBLOCK : BSA_PRED_VIDEO;
+                rec.k0 = r.k0;
+                rec.k1 = std::min<int64_t>((int64_t)r.k0 + kTileK, p->L);
+                rec.sub_bits = r.aux & kAuxMask;
+                rec.sub_q = p->sub_q;
+                rec.sub_k = p->sub_k;
+            }
+            if (sink(user, &rec)) return BSA_OK;
+        }
+    }
+    return BSA_OK;
+}

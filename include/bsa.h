@@ -1,0 +1,212 @@
+/*
+ * bsa.h -- C ABI of the MI355X (gfx950) block-sparse attention forward library.
+ *
+ * The library computes softmax(Q K^T / sqrt(d)) V over exactly the query/key
+ * pairs a logical mask selects, for every (batch, head), on one GPU.
+ *
+ * Two calls carry the method (Tessera, arXiv 2609.25869, abstract: the
+ * logical mask that specifies which interactions to compute is decoupled from
+ * the GPU execution that computes them, and preparation cost must stay small
+ * next to the execution it saves):
+ *
+ *   bsa_plan    -- host side: validates the logical mask, maps it onto physical
+ *                  tiles (empty tiles dropped, exact masking only on partial
+ *                  tiles), selects an execution regime from a lookup table
+ *                  built by offline profiling, groups tiles into workgroup
+ *                  tasks and uploads the result to the device once.
+ *   bsa_forward -- device side: runs a plan on caller-owned Q, K, V, O.
+ *
+ * Conventions
+ *  - All functions are plain C, never throw, and report errors through their
+ *    return value; bsa_last_error() gives a thread-local message for the last
+ *    failing call of the calling thread.
+ *  - Tensors Q, K, V, O are caller-owned DEVICE pointers, contiguous
+ *    [B][H][L][d] in the plan's dtype (bf16 or fp32), rows in frame-major token
+ *    order (token i = t*Hg*Wg + y*Wg + x), 16-byte aligned. Q, K, V are only
+ *    read. O is fully overwritten, including rows with no kept key (zeros).
+ *  - Masks are HOST memory owned by the caller; bsa_plan copies what it needs,
+ *    so the caller may free the mask as soon as bsa_plan returns.
+ *  - A plan owns its host and device memory and is immutable; it may be used
+ *    by any number of bsa_forward calls on any streams of its device, also
+ *    concurrently. Destroy it only after the streams that use it are done.
+ */
+#ifndef BSA_H
+#define BSA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BSA_ABI_VERSION 1
+
+typedef struct bsa_plan_s *bsa_plan_t;
+
+/* Status codes (returned as int32_t). */
+enum {
+    BSA_OK = 0,
+    BSA_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad shape, bad option          */
+    BSA_ERR_INVALID_MASK = 2,     /* mask contents out of range / unsorted / dup   */
+    BSA_ERR_UNSUPPORTED = 3,      /* valid request this build does not implement   */
+    BSA_ERR_OUT_OF_MEMORY = 4,    /* host or device allocation failed              */
+    BSA_ERR_HIP = 5,              /* a HIP runtime call failed (message has it)    */
+    BSA_ERR_INTERNAL = 6
+};
+
+/* Logical mask kinds. */
+enum {
+    /* uint8 [B][H][ceil(L/block_q)][ceil(L/block_k)], nonzero = keep the whole
+     * block. Block i covers logical positions [i*b, min((i+1)*b, L)).
+     * Tessera abstract (blocks selected by a logical mask); FG-Attn
+     * (arXiv 2509.16518) abstract (M x M blocks, M = 64 typically). */
+    BSA_MASK_BLOCK_U8 = 1,
+    /* The same mask as uint64 bit rows [B][H][ceil(L/block_q)][ceil(nkb/64)]:
+     * key block j is bit (j % 64) of word j / 64. Bits at j >= nkb must be 0. */
+    BSA_MASK_BLOCK_BITS = 2,
+    /* M x 1 slices (FG-Attn abstract: each slice is the products of a block of
+     * M queries with one key): block_q = M, block_k = 1. row_ptr int64
+     * [B*H*ceil(L/M) + 1] (row_ptr[0] = 0, non-decreasing) indexes col_idx
+     * int32; each list is strictly increasing and within [0, L). All M
+     * queries of a block share the list. */
+    BSA_MASK_SLICE_CSR = 3,
+    /* Element-exact video patterns on token coordinates, one per head
+     * (Sparse VideoGen / Splash Attention summary, "Sparse VideoGen" and
+     * "Splash Attention": heads routed to spatial or temporal patterns, exact
+     * coordinate masking on boundary tiles). block_q = block_k = 1; needs
+     * the video geometry in the options. */
+    BSA_MASK_VIDEO = 4
+};
+
+/* Per-head video patterns (BSA_MASK_VIDEO). */
+enum {
+    BSA_PAT_DENSE = 0,    /* every key */
+    BSA_PAT_SPATIAL = 1,  /* key in the query's frame, or in the anchor frame     */
+    BSA_PAT_TEMPORAL = 2  /* |y_k - y_q| <= radius and |x_k - x_q| <= radius, any frame */
+};
+
+/* Per-head token layouts. A temporal-major head (Splash Attention section:
+ * token layouts permuted into temporal-major order for the temporal patterns)
+ * works on logical position j = p*T + t for the frame-major token
+ * i = t*Hg*Wg + p. Its BLOCK and SLICE mask indices are logical positions.
+ * The permutation is fused into load and store addressing: tensors stay
+ * frame-major in memory. */
+enum { BSA_LAYOUT_FRAME_MAJOR = 0, BSA_LAYOUT_TEMPORAL_MAJOR = 1 };
+
+enum { BSA_DTYPE_BF16 = 0, BSA_DTYPE_F32 = 1 };
+
+typedef struct {
+    int32_t kind;                  /* BSA_MASK_*                                   */
+    const void *data;              /* BLOCK_U8: uint8*, BLOCK_BITS: uint64*        */
+    const int64_t *row_ptr;        /* SLICE_CSR                                    */
+    const int32_t *col_idx;        /* SLICE_CSR                                    */
+    const uint8_t *head_pattern;   /* VIDEO: [H] BSA_PAT_*                         */
+    int32_t anchor_frame;          /* VIDEO spatial anchor frame (0 <= a < T)     */
+    int32_t radius;                /* VIDEO temporal Chebyshev radius (>= 0)      */
+} bsa_mask_desc_t;
+
+typedef struct {
+    int32_t dtype;                 /* BSA_DTYPE_*; default bf16                    */
+    int32_t T, Hg, Wg;             /* video geometry; T*Hg*Wg must equal L when a
+                                      VIDEO mask or a temporal-major head is used;
+                                      0 = none                                     */
+    const uint8_t *head_layout;    /* [H] BSA_LAYOUT_*; NULL = all frame-major     */
+    int32_t force_regime;          /* -1 = choose from the lookup table            */
+    const char *lut_path;          /* NULL = the table compiled into the library   */
+    int32_t device;                /* HIP device ordinal; -1 = host-only plan for
+                                      inspection (bsa_forward rejects it)          */
+} bsa_plan_opts_t;
+
+/* Fill *opts with the defaults listed above. */
+void bsa_plan_opts_default(bsa_plan_opts_t *opts);
+
+typedef struct {
+    int32_t regime;                /* regime id (see bsa_regime_info)              */
+    int32_t tile_q, tile_k;        /* physical tile shape                          */
+    int32_t gather;                /* 1 if key tiles are gathered row lists        */
+    int64_t tasks;                 /* workgroup tasks (one per query tile)         */
+    int64_t tiles_full;            /* key tiles computed without a mask            */
+    int64_t tiles_partial;         /* key tiles with exact masking                 */
+    int64_t tiles_empty;           /* (query tile, key tile) pairs skipped         */
+    int64_t gather_rows;           /* gathered key rows (gather regimes)           */
+    double executed_pairs;         /* tile_q * tile_k per computed tile            */
+    int64_t device_bytes;          /* device memory owned by the plan              */
+    int64_t plan_ns;               /* wall time of bsa_plan                         */
+} bsa_plan_info_t;
+
+typedef struct {
+    int32_t family;                /* 0 = contiguous/permuted tiles, 1 = gather    */
+    int32_t tile_q, tile_k;
+    int32_t waves;                 /* wavefronts per workgroup                     */
+} bsa_regime_desc_t;
+
+/* One physical tile of a plan, as computed by the device (test hook for
+ * checking that a plan covers every kept pair exactly once). Positions are
+ * logical positions of the head. */
+enum { BSA_TILE_FULL = 0, BSA_TILE_PARTIAL = 1 };
+enum { BSA_PRED_NONE = 0, BSA_PRED_SUBBLOCK = 1, BSA_PRED_VIDEO = 2, BSA_PRED_LIST = 3 };
+typedef struct {
+    int64_t q0, q1;                /* query positions [q0, q1), cropped to L       */
+    int32_t kind;                  /* BSA_TILE_*                                   */
+    int32_t predicate;             /* what a PARTIAL tile evaluates: BSA_PRED_*    */
+    int64_t k0, k1;                /* contiguous keys [k0, k1), cropped to L
+                                      (k1 - k0 < tile_k means positions >= L are
+                                      masked); unused for lists                  */
+    const int32_t *keys;           /* BSA_PRED_LIST: key positions, nkeys of them  */
+    int64_t nkeys;
+    uint32_t sub_bits;             /* BSA_PRED_SUBBLOCK: keep bit of sub-block
+                                      (sq * sub_nk + sk)                           */
+    int32_t sub_q, sub_k;          /* sub-block shape; sub_nk = tile_k / sub_k     */
+} bsa_tile_record_t;
+
+/* Return nonzero to stop the walk early. */
+typedef int (*bsa_cov_sink_t)(void *user, const bsa_tile_record_t *rec);
+
+int32_t bsa_abi_version(void);
+
+/*
+ * Build a plan for `logical_mask` over B x H heads of L tokens, head dim d
+ * (64 or 128), logical block shape block_q x block_k (BLOCK kinds: powers of
+ * two in [16, 512]; SLICE: block_q = M in {32, 64, 128}, block_k = 1; VIDEO:
+ * 1 x 1). opts may be NULL (defaults). On success *out_plan receives a new
+ * plan; on failure it is set to NULL and nothing is leaked.
+ * Errors: INVALID_ARGUMENT (null pointers, shapes, options, geometry),
+ * INVALID_MASK (contents), UNSUPPORTED (d, block shape, dtype), OUT_OF_MEMORY,
+ * HIP (device selection, allocation or upload failed).
+ */
+int32_t bsa_plan(const bsa_mask_desc_t *logical_mask, int32_t B, int32_t H, int64_t L, int32_t d,
+                 int32_t block_q, int32_t block_k, const bsa_plan_opts_t *opts, bsa_plan_t *out_plan);
+
+/*
+ * Enqueue the forward pass of `plan` on `stream` (a hipStream_t; NULL = the
+ * default stream of the plan's device). Q, K, V, O as described above. Never
+ * synchronises and never allocates; returns after the launch. Launch errors
+ * are reported (BSA_ERR_HIP); faults inside the kernel surface at the
+ * caller's next synchronisation of the stream.
+ * Errors: INVALID_ARGUMENT (null plan or pointer, misaligned pointer, host-only
+ * plan), HIP.
+ */
+int32_t bsa_forward(bsa_plan_t plan, const void *Q, const void *K, const void *V, void *O, void *stream);
+
+/* Free a plan (NULL is allowed). The caller guarantees no pending forward. */
+void bsa_plan_destroy(bsa_plan_t plan);
+
+/* Statistics of a plan. Errors: INVALID_ARGUMENT. */
+int32_t bsa_plan_info(bsa_plan_t plan, bsa_plan_info_t *out);
+
+/* Walk the tiles the device will compute for head (b, h), in task order.
+ * Errors: INVALID_ARGUMENT (null plan/sink, b or h out of range). */
+int32_t bsa_plan_coverage(bsa_plan_t plan, int32_t b, int32_t h, bsa_cov_sink_t sink, void *user);
+
+/* Number of execution regimes compiled in, and their shapes. */
+int32_t bsa_regime_count(void);
+int32_t bsa_regime_info(int32_t regime, bsa_regime_desc_t *out);
+
+const char *bsa_status_str(int32_t status);
+const char *bsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSA_H */

@@ -1,0 +1,24 @@
+"""Glue between the seeded workloads and the library binding (tests/bench)."""
+import numpy as np
+
+import block_sparse_attention_fwd_amd as bsa
+import workloads as wl
+
+
+def plan_workload(w, device=0, force_regime=-1, bits=False, lut_path=None):
+    kw = dict(T=w.T, Hg=w.Hg, Wg=w.Wg, head_layout=w.head_layout, force_regime=force_regime, device=device,
+              lut_path=lut_path)
+    if w.kind == wl.BLOCK:
+        if bits:
+            return bsa.plan(bsa.MASK_BLOCK_BITS, w.B, w.H, w.L, w.d, w.bq, w.bk, data=w.block_bits(), **kw)
+        return bsa.plan(bsa.MASK_BLOCK_U8, w.B, w.H, w.L, w.d, w.bq, w.bk, data=w.block, **kw)
+    if w.kind == wl.SLICE:
+        return bsa.plan(bsa.MASK_SLICE_CSR, w.B, w.H, w.L, w.d, w.bq, 1, row_ptr=w.row_ptr, col_idx=w.col_idx, **kw)
+    if w.kind == wl.VIDEO:
+        return bsa.plan(bsa.MASK_VIDEO, w.B, w.H, w.L, w.d, 1, 1, head_pattern=w.head_pattern,
+                        anchor_frame=w.anchor, radius=w.radius, **kw)
+    raise ValueError(w.kind)
+
+
+def tok_of_logical(T, HW):
+    return np.arange(T * HW).reshape(T, HW).T.reshape(-1)

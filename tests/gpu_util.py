@@ -1,0 +1,67 @@
+"""Helpers for GPU parity tests: device tensors from seeded host data, running
+the library through the C ABI, and comparing with the fp64 oracle."""
+import sys
+
+import numpy as np
+import torch
+
+import block_sparse_attention_fwd_amd as bsa
+import oracle
+import workloads as wl
+from bsa_helpers import plan_workload
+
+MAX_ABS = 1e-2   # bf16 inputs: max-abs error against the fp64 oracle
+MEAN_ABS = 1e-3  # bf16 inputs: mean-abs error against the fp64 oracle
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_device_bf16(x_u16: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(x_u16.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+
+
+def run_gpu(w, Q, K, V, force_regime=-1, plan=None, fill=float("nan")):
+    """Plan + forward on cuda:0; returns (O as float64 numpy [B][H][L][d], plan)."""
+    p = plan if plan is not None else plan_workload(w, device=0, force_regime=force_regime)
+    q, k, v = to_device_bf16(Q), to_device_bf16(K), to_device_bf16(V)
+    o = torch.full(q.shape, fill, dtype=torch.bfloat16, device="cuda:0")
+    bsa.forward(p, q, k, v, o)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().astype(np.float64), p
+
+
+def compare(w, Q, K, V, O_gpu, rows=None, label=""):
+    """Compare GPU output rows against the oracle. rows: flat row ids or None (all)."""
+    if rows is None:
+        rows = np.arange(w.B * w.H * w.L, dtype=np.int64)
+    ref, cnt = oracle.attend(w, Q, K, V, rows=rows, return_counts=True)
+    got = O_gpu.reshape(-1, w.d)[rows]
+    err = np.abs(got - ref)
+    mx, mean = float(err.max()), float(err.mean())
+    nan = int(np.isnan(got).sum())
+    zero_rows = cnt == 0
+    zero_ok = bool(np.all(got[zero_rows] == 0.0))
+    log(f"[parity] {label}: rows={rows.size} max_abs={mx:.3e} mean_abs={mean:.3e} nan={nan} "
+        f"empty_rows={int(zero_rows.sum())} empty_exact_zero={zero_ok}")
+    assert nan == 0, f"{label}: {nan} NaN outputs"
+    assert zero_ok, f"{label}: rows without kept keys are not exactly 0"
+    assert mx <= MAX_ABS, f"{label}: max-abs {mx}"
+    assert mean <= MEAN_ABS, f"{label}: mean-abs {mean}"
+    return mx, mean
+
+
+def sample_rows(w, per_head=64, seed=0, tile=128):
+    """Every row of each head's last (ragged) query tile plus random rows."""
+    g = np.random.default_rng(seed)
+    rows = []
+    for b in range(w.B):
+        for h in range(w.H):
+            base = (b * w.H + h) * w.L
+            last = (w.L - 1) // tile * tile
+            rows.append(base + np.arange(last, w.L))
+            rows.append(base + g.choice(w.L, per_head, replace=False))
+            rows.append(base + np.array([0, w.L - 1]))
+    return np.unique(np.concatenate(rows)).astype(np.int64)

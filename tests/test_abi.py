@@ -1,0 +1,129 @@
+"""The C-ABI library loads, exports every function include/bsa.h declares,
+and reports argument/mask errors with the documented status codes (CPU only:
+host-only plans, no GPU call)."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import block_sparse_attention_fwd_amd as bsa
+import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "bsa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(bsa_[a-z_]+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 10, names
+    L = bsa.lib()
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in bsa.h but not exported"
+    assert sorted(bsa.EXPORTED) == names
+
+
+def test_version_and_status_strings():
+    L = bsa.lib()
+    assert L.bsa_abi_version() == 1
+    assert L.bsa_status_str(bsa.ERR_INVALID_MASK) == b"BSA_ERR_INVALID_MASK"
+    assert L.bsa_status_str(99) == b"BSA_ERR_UNKNOWN"
+    assert len(bsa.regimes()) == L.bsa_regime_count() >= 3
+
+
+def _block(H=2, L=256, b=64, dens=0.5):
+    g = np.random.default_rng(0)
+    n = -(-L // b)
+    return (g.random((1, H, n, n)) < dens).astype(np.uint8)
+
+
+def expect(status, fn, *a, match=None, **k):
+    with pytest.raises(bsa.BSAError) as e:
+        fn(*a, **k)
+    assert e.value.status == status, str(e.value)
+    if match:
+        assert re.search(match, str(e.value)), str(e.value)
+
+
+def test_argument_errors():
+    m = _block()
+    P = bsa.plan
+    expect(bsa.ERR_INVALID_ARGUMENT, P, bsa.MASK_BLOCK_U8, 0, 2, 256, 64, 64, 64, data=m, device=-1)
+    expect(bsa.ERR_INVALID_ARGUMENT, P, bsa.MASK_BLOCK_U8, 1, 2, 256, 64, 64, 64, data=None, device=-1)
+    expect(bsa.ERR_UNSUPPORTED, P, bsa.MASK_BLOCK_U8, 1, 2, 256, 96, 64, 64, data=m, device=-1, match="head dim")
+    expect(bsa.ERR_UNSUPPORTED, P, bsa.MASK_BLOCK_U8, 1, 2, 256, 64, 48, 64, data=m, device=-1, match="block shape")
+    expect(bsa.ERR_INVALID_ARGUMENT, P, bsa.MASK_BLOCK_U8, 1, 2, 256, 64, 64, 64, data=m, T=3, Hg=3, Wg=3, device=-1,
+           match="geometry")
+    expect(bsa.ERR_INVALID_ARGUMENT, P, bsa.MASK_BLOCK_U8, 1, 2, 256, 64, 64, 64, data=m,
+           head_layout=np.array([0, 1], np.uint8), device=-1, match="temporal-major")
+    expect(bsa.ERR_INVALID_ARGUMENT, P, bsa.MASK_BLOCK_U8, 1, 2, 256, 64, 64, 64, data=m, force_regime=17, device=-1)
+    expect(bsa.ERR_UNSUPPORTED, P, bsa.MASK_BLOCK_U8, 1, 2, 256, 64, 64, 64, data=m, force_regime=2, device=-1,
+           match="cannot run")
+    expect(bsa.ERR_INVALID_ARGUMENT, P, 9, 1, 2, 256, 64, 64, 64, data=m, device=-1)
+
+
+def test_mask_errors():
+    L = 256
+    P = bsa.plan
+    rp = np.array([0, 3, 5, 5, 7, 9, 9, 9, 9], np.int64)
+    good = np.array([1, 5, 9, 0, 200, 3, 4, 7, 8], np.int32)
+    P(bsa.MASK_SLICE_CSR, 1, 2, L, 64, 64, 1, row_ptr=rp, col_idx=good, device=-1)
+    dup = good.copy(); dup[1] = 1
+    expect(bsa.ERR_INVALID_MASK, P, bsa.MASK_SLICE_CSR, 1, 2, L, 64, 64, 1, row_ptr=rp, col_idx=dup, device=-1)
+    unsorted = good.copy(); unsorted[3], unsorted[4] = 200, 0
+    expect(bsa.ERR_INVALID_MASK, P, bsa.MASK_SLICE_CSR, 1, 2, L, 64, 64, 1, row_ptr=rp, col_idx=unsorted, device=-1)
+    oob = good.copy(); oob[2] = L
+    expect(bsa.ERR_INVALID_MASK, P, bsa.MASK_SLICE_CSR, 1, 2, L, 64, 64, 1, row_ptr=rp, col_idx=oob, device=-1)
+    neg = good.copy(); neg[0] = -1
+    expect(bsa.ERR_INVALID_MASK, P, bsa.MASK_SLICE_CSR, 1, 2, L, 64, 64, 1, row_ptr=rp, col_idx=neg, device=-1)
+    badrp = rp.copy(); badrp[2] = 2
+    expect(bsa.ERR_INVALID_MASK, P, bsa.MASK_SLICE_CSR, 1, 2, L, 64, 64, 1, row_ptr=badrp, col_idx=good, device=-1)
+    expect(bsa.ERR_INVALID_ARGUMENT, P, bsa.MASK_SLICE_CSR, 1, 2, L, 64, 64, 2, row_ptr=rp, col_idx=good, device=-1)
+    # bit rows with bits beyond the last key block
+    w = wl.Workload("b", 0, 1, 1, 200, 64, bq=64, bk=64)
+    w.block = np.ones((1, 1, 4, 4), np.uint8)
+    bits = w.block_bits()
+    P(bsa.MASK_BLOCK_BITS, 1, 1, 200, 64, 64, 64, data=bits, device=-1)
+    bits[0, 0, 1, 0] |= np.uint64(1 << 7)
+    expect(bsa.ERR_INVALID_MASK, P, bsa.MASK_BLOCK_BITS, 1, 1, 200, 64, 64, 64, data=bits, device=-1)
+    # video: pattern / anchor / radius / geometry
+    hp = np.array([1, 2], np.uint8)
+    P(bsa.MASK_VIDEO, 1, 2, 240, 64, 1, 1, head_pattern=hp, T=4, Hg=6, Wg=10, device=-1)
+    expect(bsa.ERR_INVALID_MASK, P, bsa.MASK_VIDEO, 1, 2, 240, 64, 1, 1, head_pattern=np.array([1, 3], np.uint8),
+           T=4, Hg=6, Wg=10, device=-1)
+    expect(bsa.ERR_INVALID_MASK, P, bsa.MASK_VIDEO, 1, 2, 240, 64, 1, 1, head_pattern=hp, anchor_frame=4, T=4, Hg=6,
+           Wg=10, device=-1)
+    expect(bsa.ERR_INVALID_ARGUMENT, P, bsa.MASK_VIDEO, 1, 2, 240, 64, 1, 1, head_pattern=hp, device=-1)
+
+
+def test_forward_rejects_host_only_plan_and_null_pointers():
+    p = bsa.plan(bsa.MASK_BLOCK_U8, 1, 2, 256, 64, 64, 64, data=_block(), device=-1)
+    expect(bsa.ERR_INVALID_ARGUMENT, bsa.forward, p, 16, 16, 16, 16, stream=0, match="host-only")
+    L = bsa.lib()
+    assert L.bsa_forward(None, None, None, None, None, None) == bsa.ERR_INVALID_ARGUMENT
+    L.bsa_plan_destroy(None)  # NULL-safe
+
+
+def test_simulated_allocation_failure(monkeypatch):
+    monkeypatch.setenv("BSA_TEST_FAIL_ALLOC", "1")
+    expect(bsa.ERR_OUT_OF_MEMORY, bsa.plan, bsa.MASK_BLOCK_U8, 1, 2, 256, 64, 64, 64, data=_block(), device=-1)
+
+
+def test_lookup_table_file(tmp_path):
+    m = _block()
+    f = tmp_path / "lut.txt"
+    f.write_text("# test\nblock * * 0 1 0 99999 0\n")
+    p = bsa.plan(bsa.MASK_BLOCK_U8, 1, 2, 256, 64, 64, 64, data=m, lut_path=str(f), device=-1)
+    assert p.info()["regime"] == 0
+    f.write_text("block 64 64 0 1 0 99999 1\n")
+    assert bsa.plan(bsa.MASK_BLOCK_U8, 1, 2, 256, 64, 64, 64, data=m, lut_path=str(f), device=-1).info()["regime"] == 1
+    f.write_text("block 64 64 0 1\n")
+    expect(bsa.ERR_INVALID_ARGUMENT, bsa.plan, bsa.MASK_BLOCK_U8, 1, 2, 256, 64, 64, 64, data=m, lut_path=str(f),
+           device=-1, match="malformed")
+    expect(bsa.ERR_INVALID_ARGUMENT, bsa.plan, bsa.MASK_BLOCK_U8, 1, 2, 256, 64, 64, 64, data=m,
+           lut_path=str(tmp_path / "nope"), device=-1)

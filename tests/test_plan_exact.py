@@ -1,0 +1,166 @@
+"""The mask-to-tile plan is bit-exact: the pairs the device computes (FULL
+tiles whole, PARTIAL tiles through their predicate, gathered lists) are
+exactly the pairs the oracle's own mask expansion keeps, each exactly once.
+Host-only plans; no GPU needed."""
+import numpy as np
+import pytest
+
+import block_sparse_attention_fwd_amd as bsa
+import oracle
+import workloads as wl
+from brute import element_mask
+from bsa_helpers import plan_workload, tok_of_logical
+
+
+def coverage_counts(p, w, b, h):
+    """uint8 [L][L] over (query token, key token): times each pair is computed."""
+    L = w.L
+    cnt = np.zeros((L, L), np.uint16)
+    lay = w.layout()[h]
+    tok = tok_of_logical(w.T, w.Hg * w.Wg) if lay == wl.TEMPORAL_MAJOR else np.arange(L)
+    em_tok = element_mask(w, b, h) if w.kind == wl.VIDEO else None
+    for r in p.coverage(b, h):
+        qs = tok[r["q0"]:r["q1"]]
+        if r["predicate"] == bsa.PRED_LIST:
+            ks = tok[r["keys"]]
+            cnt[np.ix_(qs, ks)] += 1
+            continue
+        ks = tok[r["k0"]:r["k1"]]
+        if r["kind"] == bsa.TILE_FULL:
+            cnt[np.ix_(qs, ks)] += 1
+        elif r["predicate"] == bsa.PRED_SUBBLOCK:
+            sq, sk = r["sub_q"], r["sub_k"]
+            nsk = 64 // sk
+            for i, qt in enumerate(range(r["q0"], r["q1"])):
+                for j, kt in enumerate(range(r["k0"], r["k1"])):
+                    bit = ((qt - r["q0"]) // sq) * nsk + (kt - r["k0"]) // sk
+                    if (r["sub_bits"] >> bit) & 1:
+                        cnt[tok[qt], tok[kt]] += 1
+        elif r["predicate"] == bsa.PRED_VIDEO:
+            sub = em_tok[np.ix_(qs, ks)]
+            cnt[np.ix_(qs, ks)] += sub.astype(np.uint16)
+        else:
+            raise AssertionError(r)
+    return cnt
+
+
+def expected(w, b, h):
+    """0/1 [L][L] from the oracle's own expansion (om_row_keys)."""
+    L = w.L
+    m = np.zeros((L, L), np.uint16)
+    for q in range(L):
+        m[q, oracle.row_keys(w, b, h, q)] = 1
+    return m
+
+
+def small_cases():
+    out = []
+    g = np.random.default_rng(3)
+    # BLOCK: retain / combine / subdivide, ragged L, both layouts
+    for (bq, bk) in [(64, 64), (32, 32), (128, 128), (64, 256), (32, 128), (256, 32)]:
+        T, Hg, Wg = 3, 10, 11
+        L = T * Hg * Wg  # 330: ragged for every block size
+        w = wl.Workload(f"blk{bq}x{bk}", 7, 1, 2, L, 64, T, Hg, Wg, wl.BLOCK, bq, bk)
+        w.block = (g.random((1, 2, w.nqb, w.nkb)) < 0.4).astype(np.uint8)
+        w.block[0, 0, 0, :] = 1
+        w.head_layout = np.array([0, 1], np.uint8)
+        out.append(w)
+    # SLICE M = 64 and 128, both layouts, empty lists
+    for M in (64, 128):
+        T, Hg, Wg = 3, 10, 11
+        L = T * Hg * Wg
+        w = wl.Workload(f"slice{M}", 8, 1, 2, L, 64, T, Hg, Wg, wl.SLICE, M, 1)
+        nqb = w.nqb
+        rp, ci = [0], []
+        for e in range(2 * nqb):
+            n = 0 if e == 1 else int(g.integers(1, 150))
+            ci.append(np.sort(g.choice(L, n, replace=False)).astype(np.int32))
+            rp.append(rp[-1] + n)
+        w.row_ptr, w.col_idx = np.array(rp, np.int64), np.concatenate(ci)
+        w.head_layout = np.array([0, 1], np.uint8)
+        out.append(w)
+    # VIDEO, small SVG-like geometry, both runs, anchor 0 and 2
+    for run in ("A", "B"):
+        w = wl.svg(run, H=4, T=5, Hg=7, Wg=13, d=64)
+        w.head_pattern = np.array([wl.SPATIAL, wl.TEMPORAL, wl.SPATIAL, wl.DENSE], np.uint8)
+        w.anchor = 2 if run == "B" else 0
+        w.head_layout = np.array([0, 1, 1, 1], np.uint8) if run == "B" else np.zeros(4, np.uint8)
+        out.append(w)
+    return out
+
+
+@pytest.mark.parametrize("w", small_cases(), ids=lambda w: w.name)
+@pytest.mark.parametrize("regime", [-1, 0, 1])
+def test_plan_covers_each_kept_pair_once(w, regime):
+    if w.kind == wl.SLICE:
+        regime = -1  # slices run only in the gather regime matching M
+    p = plan_workload(w, device=-1, force_regime=regime)
+    for b in range(w.B):
+        for h in range(w.H):
+            got = coverage_counts(p, w, b, h)
+            want = expected(w, b, h)
+            bad = np.argwhere(got != want)
+            assert bad.size == 0, f"{w.name} h{h}: {len(bad)} pairs wrong, first {bad[:5].tolist()}"
+
+
+def test_block_bits_and_u8_give_the_same_plan():
+    w = small_cases()[1]
+    a = plan_workload(w, device=-1)
+    b = plan_workload(w, device=-1, bits=True)
+    for h in range(w.H):
+        assert a.coverage(0, h) == b.coverage(0, h)
+
+
+def test_every_query_tile_has_a_task():
+    w = small_cases()[0]
+    w.block[:] = 0
+    p = plan_workload(w, device=-1)
+    info = p.info()
+    assert info["tiles_full"] + info["tiles_partial"] == 0
+    assert info["tasks"] == w.H * -(-w.L // info["tile_q"])
+
+
+@pytest.mark.parametrize("run,pattern,layout,want", [
+    # (FULL, PARTIAL, EMPTY) per head for the 13 x 30x52 SVG workload at 128x64 tiles.
+    # The last query tile has only 56 rows; rows past the sequence end are never
+    # stored, so its 47 all-kept tiles are FULL (counting them PARTIAL would give
+    # 6942 / 1001).
+    ("A", wl.SPATIAL, 0, (6989, 954, 42460)),
+    ("A", wl.TEMPORAL, 0, (0, 12835, 37568)),
+    ("B", wl.TEMPORAL, 1, (0, 2998, 47405)),
+])
+def test_svg_tile_counts(run, pattern, layout, want):
+    """Tile classification at full size matches the counts derived from the
+    geometry (13 x 30x52, 128x64 tiles)."""
+    w = wl.svg(run, H=1)
+    w.head_pattern = np.array([pattern], np.uint8)
+    w.head_layout = np.array([layout], np.uint8)
+    info = plan_workload(w, device=-1, force_regime=0).info()
+    assert (info["tiles_full"], info["tiles_partial"], info["tiles_empty"]) == want
+
+
+def test_svg_plan_exact_on_sampled_query_tiles():
+    """Full-size SVG plans (both runs): for sampled query tiles, the computed
+    pairs equal the oracle's kept pairs exactly."""
+    for run in ("A", "B"):
+        w = wl.svg(run, H=24)
+        p = plan_workload(w, device=-1)
+        tq = p.info()["tile_q"]
+        tok_tm = tok_of_logical(w.T, w.Hg * w.Wg)
+        for h in (0, 11, 12, 23):
+            recs = p.coverage(0, h)
+            lay = w.layout()[h]
+            tok = tok_tm if lay else np.arange(w.L)
+            em = element_mask(w, 0, h)
+            for q0 in (0, 1536, 10112, (w.L // tq) * tq):
+                qs = tok[q0:min(q0 + tq, w.L)]
+                cnt = np.zeros((qs.size, w.L), np.uint16)
+                for r in recs:
+                    if r["q0"] != q0:
+                        continue
+                    ks = tok[r["k0"]:r["k1"]]
+                    if r["kind"] == bsa.TILE_FULL:
+                        cnt[:, ks] += 1
+                    else:
+                        cnt[:, ks] += em[np.ix_(qs, ks)]
+                assert np.array_equal(cnt, em[qs].astype(np.uint16)), (run, h, q0)
