@@ -135,6 +135,9 @@ def main():
     ap.add_argument("--cpu-rows-per-head", type=int, default=512)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--runs", default="A,B", help="comma list of runs to time (the headline needs B)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes 5 times (HBM counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -149,6 +152,15 @@ def main():
     import workloads as wl
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        n = args.copy_calibration // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 5}), flush=True)
+        return
     wA, wB = wl.svg("A"), wl.svg("B")
     log("[bench] generating inputs")
     Q, K, V = wl.make_qkv(wB)
@@ -163,7 +175,10 @@ def main():
     flops = 4 * wB.d * P
 
     res = {}
+    runs = [r.strip() for r in args.runs.split(",") if r.strip()]
     for name, w in (("A", wA), ("B", wB)):
+        if name not in runs:
+            continue
         log(f"[bench] run {name}: warmup {args.warmup}, steps {args.steps}")
         r, o = time_run(w, Q, K, V, args.steps, args.warmup)
         if not args.no_parity:
@@ -203,7 +218,8 @@ def main():
         "effective_tflops_step": round(B["effective_tflops_step"], 2),
         "effective_tflops_fwd": round(B["effective_tflops_fwd"], 2),
         "pct_bf16_peak_fwd": round(B["pct_bf16_peak_fwd"], 2),
-        "run_A": {k: (round(v, 4) if isinstance(v, float) else v) for k, v in res["A"].items() if k != "plan_info"},
+        "run_A": ({k: (round(v, 4) if isinstance(v, float) else v) for k, v in res["A"].items() if k != "plan_info"}
+                  if "A" in res else None),
         "run_B_plan": B["plan_info"],
         "parity": B.get("parity"),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MI355X_BF16_PEAK_TFLOPS,

@@ -777,6 +777,18 @@ extern "C" void bsa_plan_destroy(bsa_plan_t p)
     delete p;
 }
 
+// Division by a runtime constant d in [1, 2^30] for numerators 0 <= n < 2^31:
+// n / d == (umulhi(n, m) + n) >> s with s = ceil(log2 d) and
+// m = floor(2^32 (2^s - d) / d) + 1 (round-up multiplier; the sum cannot
+// overflow 32 bits because umulhi(n, m) < n).
+static void magic_div(uint32_t d, uint32_t *m, int32_t *s)
+{
+    int l = 0;
+    while ((1ull << l) < d) ++l;
+    *m = (uint32_t)((((1ull << l) - d) << 32) / d + 1);
+    *s = l;
+}
+
 extern "C" int32_t bsa_forward(bsa_plan_t p, const void *Q, const void *K, const void *V, void *O, void *stream)
 {
     if (!p) return fail(BSA_ERR_INVALID_ARGUMENT, "plan is NULL");
@@ -795,6 +807,9 @@ extern "C" int32_t bsa_forward(bsa_plan_t p, const void *Q, const void *K, const
     a.H = p->H;
     a.L = (int32_t)p->L;
     a.T = p->T; a.HW = p->Hg * p->Wg; a.W = p->Wg;
+    magic_div((uint32_t)std::max(a.T, 1), &a.magic_T, &a.shift_T);
+    magic_div((uint32_t)std::max(a.HW, 1), &a.magic_HW, &a.shift_HW);
+    magic_div((uint32_t)std::max(a.W, 1), &a.magic_W, &a.shift_W);
     a.anchor = p->anchor; a.radius = p->radius;
     a.mode = p->mode;
     a.bq_shift = p->bq_shift; a.bk_shift = p->bk_shift; a.nsk = p->nsk;

@@ -4,13 +4,14 @@
 // head) against the ordered key tiles the plan lists for it (Tessera, arXiv
 // 2609.25869, abstract: physical tiles grouped into GPU tasks for data reuse
 // and load/compute overlap). Every key tile of 64 keys is staged in LDS once
-// and shared by all waves; the next tile's load is in flight while the current
-// tile is computed (double-buffered LDS). Empty tiles never reach the kernel;
-// FULL tiles run with no mask code; PARTIAL tiles evaluate the exact predicate
-// (Sparse VideoGen / Splash Attention summary, "Splash Attention": empty tiles
+// and shared by all waves; the next tile's global loads are in flight while
+// the current tile is computed, and land in the other half of a
+// double-buffered LDS tile. Empty tiles never reach the kernel; FULL tiles
+// run with no mask code; PARTIAL tiles evaluate the exact predicate (Sparse
+// VideoGen / Splash Attention summary, "Splash Attention": empty tiles
 // bypassed, exact coordinate masking only on boundary tiles). Gathered tiles
 // load the listed key rows into packed LDS tiles (FG-Attn, arXiv 2509.16518,
-// abstract: asynchronous-gather load of a sparse key/value set).
+// abstract: gather a sparse set of key/value vectors into packed tiles).
 //
 // Matrix layout on the MFMA units (v_mfma_f32_32x32x16_bf16, wave64):
 //  - S^T = K Q^T: A = 32 keys x 16 dims from LDS, B = Q^T from registers.
@@ -21,10 +22,13 @@
 //    the transposing LDS read, B = P^T straight from the score registers.
 //    O^T again has one query per lane column, so the online-softmax rescale
 //    is per lane.
-// Online softmax in fp32 with base-2 exponentials: m' = max(m, rowmax(s)*c),
-// p = 2^(s*c - m'), l' = 2^(m - m') l + sum p, O' = 2^(m - m') O + P V with
-// c = log2(e)/sqrt(d); P is rounded to bf16 once and the same rounded values
-// feed both the PV product and the row sum. Rows with no kept key output 0.
+// Online softmax in fp32 with base-2 exponentials and c = log2(e)/sqrt(d):
+// p = 2^(s*c - m), l = sum p, O = sum p V, O / l at the end. The reference m
+// only moves when a tile's maximum exceeds it by more than kSlack (then O and
+// l are rescaled by 2^(m_old - m_new)); p therefore stays below 2^kSlack and
+// the result, O / l, does not depend on where m sits. P is rounded to bf16
+// once and the same rounded values feed both the PV product and the row sum.
+// Rows with no kept key output 0.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -42,31 +46,36 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T *)(p))
 
+constexpr float kSlack = 8.0f;  // log2 headroom before the softmax reference moves
+
+// Key-coordinate word of a slot past the sequence end: no frame equals it, and
+// (kNoKey - window origin) has both 16-bit halves far above any 2*radius
+// (radius <= 256, coordinates < 512), so no video predicate keeps it.
+constexpr int kNoKey = 0x7FFF7FFF;
+
 template <int NW, int D>
 struct Cfg {
     static constexpr int BQ = 32 * NW;
     static constexpr int BK = kTileK;
     static constexpr int ROWB = D * 2;                 // bytes per bf16 row
-    static constexpr int TILEB = BK * ROWB;            // bytes per K or V tile
+    static constexpr int KROW = ROWB + 16;             // padded K row in LDS
+    static constexpr int KTILEB = BK * KROW;           // bytes per K tile
+    static constexpr int TILEB = BK * ROWB;            // bytes per V tile
     static constexpr int CHUNKS = ROWB / 16;           // 16-byte chunks per row
     static constexpr int RPI = 1024 / ROWB;            // rows per wave-wide 1 KiB copy
     static constexpr int INSTS = BK / RPI / NW;        // copies per wave per tensor per tile
     static_assert(INSTS >= 1, "tile too small for the workgroup");
 };
 
-// XOR swizzles of the 16-byte chunks within a row (conflict-free LDS access):
-// K rows are read 8 or 16 rows at a time at one chunk; V is read through the
-// transposing read 4 consecutive keys at a time.
+// Conflict-free LDS layouts. K rows are padded by 16 bytes: a read of one
+// 16-byte chunk from 8 or 16 consecutive rows then hits distinct banks. V rows
+// keep their natural 256/128-byte stride with the 16-byte chunks of row k
+// XOR-swizzled by swz_v(k & 3): the transposing read of 4 consecutive keys x
+// 32 contiguous bytes then hits distinct banks.
 template <int D>
-__device__ __forceinline__ int swz_k(int row) { return D == 128 ? (row & 15) : (row & 7); }
-template <int D>
-__device__ __forceinline__ int swz_v(int row)
+__device__ __forceinline__ int swz_v(int key_mod4)
 {
-    if (D == 128) {
-        const int r = row & 3;
-        return r == 0 ? 0 : (r == 1 ? 6 : (r == 2 ? 12 : 10));
-    }
-    return 2 * (row & 3);
+    return D == 128 ? (int)((0xAC60u >> (4 * key_mod4)) & 15u) : 2 * key_mod4;  // {0,6,12,10} / {0,2,4,6}
 }
 
 __device__ __forceinline__ float swap_halves_max(float x)
@@ -80,17 +89,33 @@ __device__ __forceinline__ float swap_halves_sum(float x)
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// three-input maximum on one VALU op (scores are never NaN, so no quieting of
+// the inputs is needed)
+__device__ __forceinline__ float max3f(float a, float b, float c)
+{
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 __device__ __forceinline__ bf16x8 load_bf16x8(const __bf16 *p)
 {
     i32x4 v = *(const i32x4 *)p;
     return __builtin_bit_cast(bf16x8, v);
 }
 
+// n / d for 0 <= n < 2^31 with the host-computed multiplier (round-up method)
+__device__ __forceinline__ int fdiv(int n, uint32_t m, int s)
+{
+    return (int)((__umulhi((unsigned)n, m) + (unsigned)n) >> s);
+}
+
 template <int NW, int D>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void bsa_fwd_bf16(KernelArgs a)
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4 ? 2 : 1, 2))) void bsa_fwd_bf16(KernelArgs a)
 {
     using C = Cfg<NW, D>;
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[2][2][C::TILEB];  // [buffer][K, V][tile]
+    __shared__ __attribute__((aligned(1024))) unsigned char ksm[2][C::KTILEB];  // [buffer] padded K tile
+    __shared__ __attribute__((aligned(1024))) unsigned char vsm[2][C::TILEB];   // [buffer] swizzled V tile
     __shared__ __attribute__((aligned(16))) int kcoord[2][C::BK];
 
     const int tid = threadIdx.x;
@@ -103,14 +128,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const bool tm = (hflag & kHeadTemporalMajor) != 0;
     const int pat = (int)((hflag >> kHeadPatShift) & 3u);
     const int L = a.L;
-    const int T = a.T, HW = a.HW, W = a.W;
     const size_t head_off = (size_t)bh * (size_t)L * D;
     const __bf16 *Qh = (const __bf16 *)a.Q + head_off;
     const __bf16 *Kh = (const __bf16 *)a.K + head_off;
     const __bf16 *Vh = (const __bf16 *)a.V + head_off;
     __bf16 *Oh = (__bf16 *)a.O + head_off;
 
-    auto token = [&](int j) -> int { return tm ? (j % T) * HW + j / T : j; };
+    // logical position of the head -> frame-major token
+    auto token = [&](int j) -> int {
+        if (!tm) return j;
+        const int p = fdiv(j, a.magic_T, a.shift_T);
+        return (j - p * a.T) * a.HW + p;
+    };
 
     // ---- this lane's query row (logical position q, frame-major token qtok)
     const int q = task.q0 + 32 * w + l32;
@@ -119,26 +148,31 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
     const int ntile = task.te - task.tb;
     const bool gather = a.mode == kModeGather;
+    const bool video = a.mode == kModeVideo;
 
     f32x16 oacc[D / 32];
 #pragma unroll
     for (int n = 0; n < D / 32; ++n)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[n][r] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
+    float m_ref = -INFINITY, l_run = 0.f;
 
     if (ntile > 0) {
         bf16x8 qreg[D / 16];
 #pragma unroll
         for (int s = 0; s < D / 16; ++s) qreg[s] = load_bf16x8(Qh + (size_t)qtok * D + 16 * s + 8 * hf);
 
-        // query coordinates for the video predicates
-        int qt = 0, qy = 0, qx = 0;
-        if (a.mode == kModeVideo) {
-            qt = qtok / HW;
-            qy = (qtok % HW) / W;
-            qx = qtok % W;
+        // query coordinates for the video predicates: frame (spatial) or the
+        // packed window origin ((y - r) << 16) + (x - r) (temporal)
+        int qt = 0;
+        unsigned qwin = 0;
+        if (video) {
+            qt = fdiv(qtok, a.magic_HW, a.shift_HW);
+            const int p = qtok - qt * a.HW;
+            const int y = fdiv(p, a.magic_W, a.shift_W), x = p - y * a.W;
+            qwin = ((unsigned)(y - a.radius) << 16) + (unsigned)(x - a.radius);
         }
+        const unsigned win2 = 2u * (unsigned)a.radius;
 
         // rows this lane copies for each tile: slot = (w*INSTS + i)*RPI + lane/CHUNKS
         const int pos = lane % C::CHUNKS;
@@ -156,7 +190,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
         // global -> registers (in flight while the current tile is computed)
         i32x4 stage_k[C::INSTS], stage_v[C::INSTS];
-        int stage_c = -1;
+        int stage_c = kNoKey;
         auto fetch_tile = [&](int rec_i, const int *idx) {
             const TileRec r = a.tiles[rec_i];
 #pragma unroll
@@ -164,17 +198,20 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
                 const int slot = (w * C::INSTS + i) * C::RPI + lane / C::CHUNKS;
                 const int kpos = gather ? idx[i] : min(r.k0 + slot, L - 1);
                 const int ktok = token(kpos);
-                stage_k[i] = *(const i32x4 *)(Kh + (size_t)ktok * D + 8 * (pos ^ swz_k<D>(slot)));
-                stage_v[i] = *(const i32x4 *)(Vh + (size_t)ktok * D + 8 * (pos ^ swz_v<D>(slot)));
+                stage_k[i] = *(const i32x4 *)(Kh + (size_t)ktok * D + 8 * pos);
+                stage_v[i] = *(const i32x4 *)(Vh + (size_t)ktok * D + 8 * (pos ^ swz_v<D>(slot & 3)));
             }
-            if (a.mode == kModeVideo && w == 0) {
-                // packed (t, y, x) of each key slot; slots past the sequence end
-                // get a value no query coordinate can match
+            if (video && w == 0) {
+                // per key slot: frame (spatial) or packed (y << 16) | x
+                // (temporal); kNoKey past the sequence end
                 const int kp = r.k0 + lane;
-                int v = -1;
+                int v = kNoKey;
                 if (kp < L) {
                     const int kt = token(kp);
-                    v = ((kt / HW) << 20) | (((kt % HW) / W) << 10) | (kt % W);
+                    const int t = fdiv(kt, a.magic_HW, a.shift_HW);
+                    const int p = kt - t * a.HW;
+                    const int y = fdiv(p, a.magic_W, a.shift_W), x = p - y * a.W;
+                    v = pat == 1 ? t : (pat == 2 ? ((y << 16) | x) : 0);
                 }
                 stage_c = v;
             }
@@ -183,10 +220,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         auto store_tile = [&](int buf) {
 #pragma unroll
             for (int i = 0; i < C::INSTS; ++i) {
-                *LDS_PTR(i32x4, &smem[buf][0][(w * C::INSTS + i) * 1024 + 16 * lane]) = stage_k[i];
-                *LDS_PTR(i32x4, &smem[buf][1][(w * C::INSTS + i) * 1024 + 16 * lane]) = stage_v[i];
+                const int slot = (w * C::INSTS + i) * C::RPI + lane / C::CHUNKS;
+                *LDS_PTR(i32x4, &ksm[buf][slot * C::KROW + 16 * pos]) = stage_k[i];
+                *LDS_PTR(i32x4, &vsm[buf][(w * C::INSTS + i) * 1024 + 16 * lane]) = stage_v[i];
             }
-            if (a.mode == kModeVideo && w == 0) kcoord[buf][lane] = stage_c;
+            if (video && w == 0) kcoord[buf][lane] = stage_c;
         };
 
         // prologue: tile 0 into buffer 0
@@ -196,8 +234,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         store_tile(0);
         __syncthreads();
 
-        const int krow0 = l32, krow1 = 32 + l32;
-        const int fk0 = swz_k<D>(krow0), fk1 = swz_k<D>(krow1);
+        // per-lane LDS read offsets (loop-invariant; tile-relative parts are immediates)
+        const int koff = l32 * C::KROW + 16 * hf;  // K rows l32 (+32), chunk 2s + hf
+        const int grp = lane >> 4, jl = lane & 15;
+        const int dd_base = 16 * (grp & 1) + 4 * (jl & 3);  // first dim this lane addresses
+        const int key_sub = jl >> 2;                         // key within a group of 4
+        const int sv = swz_v<D>(key_sub);
+        int voff[D / 32];  // V^T operand of dim block n: keys 4*hf + key_sub (+16c, +8)
+#pragma unroll
+        for (int n = 0; n < D / 32; ++n)
+            voff[n] = (4 * hf + key_sub) * C::ROWB + 16 * (((32 * n + dd_base) >> 3) ^ sv) + 2 * (dd_base & 7);
+        const f32x16 zero16 = {};
 
         for (int j = 0; j < ntile; ++j) {
             const int cur = j & 1;
@@ -209,17 +256,20 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             }
 
             // ---- S^T = K Q^T
-            f32x16 sacc[2];
+            const unsigned char *kt = ksm[cur] + koff;
+            f32x16 s0, s1;
+            {
+                bf16x8 k0v = *LDS_PTR(bf16x8, kt);
+                bf16x8 k1v = *LDS_PTR(bf16x8, kt + 32 * C::KROW);
+                s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0v, qreg[0], zero16, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1v, qreg[0], zero16, 0, 0, 0);
+            }
 #pragma unroll
-            for (int r = 0; r < 16; ++r) { sacc[0][r] = 0.f; sacc[1][r] = 0.f; }
-            const unsigned char *kt = smem[cur][0];
-#pragma unroll
-            for (int s = 0; s < D / 16; ++s) {
-                const int c = 2 * s + hf;
-                bf16x8 k0v = *LDS_PTR(bf16x8, kt + krow0 * C::ROWB + 16 * (c ^ fk0));
-                bf16x8 k1v = *LDS_PTR(bf16x8, kt + krow1 * C::ROWB + 16 * (c ^ fk1));
-                sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0v, qreg[s], sacc[0], 0, 0, 0);
-                sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1v, qreg[s], sacc[1], 0, 0, 0);
+            for (int s = 1; s < D / 16; ++s) {
+                bf16x8 k0v = *LDS_PTR(bf16x8, kt + 32 * s);
+                bf16x8 k1v = *LDS_PTR(bf16x8, kt + 32 * C::KROW + 32 * s);
+                s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0v, qreg[s], s0, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1v, qreg[s], s1, 0, 0, 0);
             }
             // keep LDS reads next to the MFMAs that consume them (bounds register use)
 #pragma unroll
@@ -230,29 +280,43 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
             // ---- exact mask on PARTIAL tiles only
             if (rec.aux & kPartial) {
-                if (a.mode == kModeVideo) {
+                if (video) {
                     const int *kc = kcoord[cur];
-#pragma unroll
-                    for (int kb = 0; kb < 2; ++kb)
+                    if (pat == 1) {  // spatial: key in the query's frame or in the anchor frame
 #pragma unroll
                         for (int g = 0; g < 4; ++g) {
-                            const i32x4 c4 = *LDS_PTR(i32x4, kc + 32 * kb + 8 * g + 4 * hf);
+                            const i32x4 c0 = *LDS_PTR(i32x4, kc + 8 * g + 4 * hf);
+                            const i32x4 c1 = *LDS_PTR(i32x4, kc + 32 + 8 * g + 4 * hf);
 #pragma unroll
                             for (int e = 0; e < 4; ++e) {
-                                const int v = c4[e];
-                                bool keep;
-                                if (pat == 1) {
-                                    const int kt2 = (int)((unsigned)v >> 20);
-                                    keep = kt2 == qt || kt2 == a.anchor;
-                                } else if (pat == 2) {
-                                    const int ky = (v >> 10) & 1023, kx = v & 1023;
-                                    keep = abs(ky - qy) <= a.radius && abs(kx - qx) <= a.radius;
-                                } else {
-                                    keep = v != -1;
-                                }
-                                if (!keep) sacc[kb][4 * g + e] = -INFINITY;
+                                s0[4 * g + e] = (c0[e] == qt || c0[e] == a.anchor) ? s0[4 * g + e] : -INFINITY;
+                                s1[4 * g + e] = (c1[e] == qt || c1[e] == a.anchor) ? s1[4 * g + e] : -INFINITY;
                             }
                         }
+                    } else if (pat == 2) {  // temporal: |dy| <= r and |dx| <= r, any frame
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            const i32x4 c0 = *LDS_PTR(i32x4, kc + 8 * g + 4 * hf);
+                            const i32x4 c1 = *LDS_PTR(i32x4, kc + 32 + 8 * g + 4 * hf);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const unsigned d0 = (unsigned)c0[e] - qwin, d1 = (unsigned)c1[e] - qwin;
+                                s0[4 * g + e] = max(d0 & 0xffffu, d0 >> 16) <= win2 ? s0[4 * g + e] : -INFINITY;
+                                s1[4 * g + e] = max(d1 & 0xffffu, d1 >> 16) <= win2 ? s1[4 * g + e] : -INFINITY;
+                            }
+                        }
+                    } else {  // dense: only slots past the sequence end
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            const i32x4 c0 = *LDS_PTR(i32x4, kc + 8 * g + 4 * hf);
+                            const i32x4 c1 = *LDS_PTR(i32x4, kc + 32 + 8 * g + 4 * hf);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                s0[4 * g + e] = c0[e] != kNoKey ? s0[4 * g + e] : -INFINITY;
+                                s1[4 * g + e] = c1[e] != kNoKey ? s1[4 * g + e] : -INFINITY;
+                            }
+                        }
+                    }
                 } else {
                     // keep bits of key slots 0..31 (lo) and 32..63 (hi) for this lane's query
                     uint32_t lo, hi;
@@ -276,59 +340,55 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int bit = 8 * (r / 4) + (r % 4);
-                        if (!((lo >> bit) & 1u)) sacc[0][r] = -INFINITY;
-                        if (!((hi >> bit) & 1u)) sacc[1][r] = -INFINITY;
+                        s0[r] = ((lo >> bit) & 1u) ? s0[r] : -INFINITY;
+                        s1[r] = ((hi >> bit) & 1u) ? s1[r] : -INFINITY;
                     }
                 }
             }
 
-            // ---- online softmax
-            float mx = -INFINITY;
+            // ---- online softmax (reference max moves only by more than kSlack)
+            float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(sacc[0][r], sacc[1][r]));
-            mx = swap_halves_max(mx);
-            const float m_new = fmaxf(m_run, mx * a.scale_log2);
-            const float m_use = m_new == -INFINITY ? 0.f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-            m_run = m_new;
-
-            bf16x8 pk[4];
-            float psum = 0.f;
-            const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-#pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    const float s0 = sacc[c / 2][8 * (c % 2) + e], s1 = sacc[c / 2][8 * (c % 2) + e + 1];
-                    const float p0 = __builtin_amdgcn_exp2f(fmaf(s0, a.scale_log2, -m_use));
-                    const float p1 = __builtin_amdgcn_exp2f(fmaf(s1, a.scale_log2, -m_use));
-                    const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
-                    psum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, psum, false);
-                    pk[c][e] = pp[0];
-                    pk[c][e + 1] = pp[1];
-                }
-            }
-            l_run = l_run * alpha + psum;
-            if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+            for (int r = 1; r < 16; ++r) mx = max3f(mx, s0[r], s1[r]);
+            mx = swap_halves_max(mx) * a.scale_log2;
+            const bool need = mx > m_ref + kSlack;
+            if (__builtin_amdgcn_ballot_w64(need)) {
+                // lanes that keep their reference (also those still at -inf) scale by exactly 1
+                const float alpha = need ? __builtin_amdgcn_exp2f(m_ref - mx) : 1.0f;
+                m_ref = need ? mx : m_ref;
+                l_run *= alpha;
 #pragma unroll
                 for (int n = 0; n < D / 32; ++n)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) oacc[n][r] *= alpha;
             }
+            const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+
+            bf16x8 pk[4];
+            const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    const float x0 = (c < 2 ? s0 : s1)[8 * (c % 2) + e];
+                    const float x1 = (c < 2 ? s0 : s1)[8 * (c % 2) + e + 1];
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(x0, a.scale_log2, -m_use));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(x1, a.scale_log2, -m_use));
+                    const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
+                    l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_run, false);
+                    pk[c][e] = pp[0];
+                    pk[c][e + 1] = pp[1];
+                }
+            }
 
             // ---- O^T += V^T P^T
-            const unsigned char *vt = smem[cur][1];
-            const int grp = lane >> 4, jl = lane & 15;
-            const int dd_base = 16 * (grp & 1) + 4 * (jl & 3);  // dim offset this lane addresses
-            const int key_sub = jl >> 2;                         // key within the group of 4
+            const unsigned char *vt = vsm[cur];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
 #pragma unroll
                 for (int n = 0; n < D / 32; ++n) {
-                    const int dd = 32 * n + dd_base;
-                    const int ka = 16 * c + 4 * hf + key_sub, kb2 = ka + 8;
-                    const unsigned char *pa = vt + ka * C::ROWB + 16 * ((dd >> 3) ^ swz_v<D>(ka)) + 2 * (dd & 7);
-                    const unsigned char *pb = vt + kb2 * C::ROWB + 16 * ((dd >> 3) ^ swz_v<D>(kb2)) + 2 * (dd & 7);
+                    const unsigned char *pa = vt + voff[n] + 16 * c * C::ROWB;  // keys 16c + 4hf + key_sub
+                    const unsigned char *pb = pa + 8 * C::ROWB;                  // ... + 8
                     const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, pa));
                     const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, pb));
                     const bf16x4 a4 = __builtin_bit_cast(bf16x4, va), b4 = __builtin_bit_cast(bf16x4, vb);

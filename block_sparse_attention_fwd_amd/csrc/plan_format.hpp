@@ -50,6 +50,8 @@ struct KernelArgs {
     int32_t H;
     int32_t L;
     int32_t T, HW, W;          // video geometry (0 if unused)
+    uint32_t magic_T, magic_HW, magic_W;  // n / d == (umulhi(n, magic) + n) >> shift for 0 <= n < 2^31
+    int32_t shift_T, shift_HW, shift_W;
     int32_t anchor, radius;
     int32_t mode;              // MaskMode
     int32_t bq_shift, bk_shift, nsk;  // block sub-block geometry (log2 sizes, sub-blocks per key tile)
