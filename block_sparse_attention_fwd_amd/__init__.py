@@ -50,10 +50,13 @@ class PlanInfo(ctypes.Structure):
     _fields_ = [("regime", ctypes.c_int32), ("tile_q", ctypes.c_int32), ("tile_k", ctypes.c_int32),
                 ("gather", ctypes.c_int32), ("tasks", ctypes.c_int64), ("tiles_full", ctypes.c_int64),
                 ("tiles_partial", ctypes.c_int64), ("tiles_empty", ctypes.c_int64), ("gather_rows", ctypes.c_int64),
-                ("executed_pairs", ctypes.c_double), ("device_bytes", ctypes.c_int64), ("plan_ns", ctypes.c_int64)]
+                ("executed_pairs", ctypes.c_double), ("device_bytes", ctypes.c_int64), ("plan_ns", ctypes.c_int64),
+                ("phase_ns", ctypes.c_int64 * 5)]
 
     def as_dict(self):
-        return {k: getattr(self, k) for k, _ in self._fields_}
+        d = {k: getattr(self, k) for k, _ in self._fields_}
+        d["phase_ns"] = dict(zip(("ingest", "regime", "mapping", "tasks", "upload"), list(self.phase_ns)))
+        return d
 
 
 class RegimeDesc(ctypes.Structure):

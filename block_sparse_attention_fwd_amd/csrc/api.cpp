@@ -20,12 +20,16 @@
 #include <algorithm>
 #include <atomic>
 #include <chrono>
+#include <condition_variable>
+#include <functional>
+#include <mutex>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <fstream>
+#include <map>
 #include <memory>
 #include <new>
 #include <sstream>
@@ -34,6 +38,7 @@
 #include <vector>
 
 #include "../../include/bsa.h"
+#include "mempool.hpp"
 #include "plan_format.hpp"
 
 namespace bsa {
@@ -156,6 +161,12 @@ static bool parse_lut(const std::string &text, std::vector<LutRule> &rules, std:
 // the plan object
 // ---------------------------------------------------------------------------
 
+// A plan is one contiguous image -- tasks | tile records | gather indices |
+// head flags, each section 256-byte aligned -- identical on the host (pinned
+// memory from a recycling pool, or plain memory for host-only plans) and on
+// the device (a block from a per-device recycling pool). It is uploaded once,
+// asynchronously on a library stream; bsa_forward orders its launch after the
+// upload with an event.
 struct bsa_plan_s {
     int32_t B = 0, H = 0, d = 0, dtype = 0;
     int64_t L = 0;
@@ -165,21 +176,25 @@ struct bsa_plan_s {
     int32_t bq_shift = 0, bk_shift = 0, nsk = 1, sub_q = 0, sub_k = 0;
     int32_t mode = 0;
     std::vector<uint8_t> head_layout, head_pattern;
-    std::vector<Task> tasks;
-    std::vector<TileRec> tiles;
-    std::vector<int32_t> gidx;
-    std::vector<uint32_t> head_flags;
+    // image
+    uint8_t *img = nullptr;
+    size_t img_cap = 0, img_bytes = 0;
+    bool img_pinned = false;
+    std::vector<uint8_t> img_vec;
+    size_t off_tasks = 0, off_tiles = 0, off_gidx = 0, off_flags = 0;
+    int64_t ntasks = 0, ntiles = 0, ngidx = 0;
+    const Task *tasks() const { return (const Task *)(img + off_tasks); }
+    const TileRec *tiles() const { return (const TileRec *)(img + off_tiles); }
+    const int32_t *gidx() const { return (const int32_t *)(img + off_gidx); }
     // statistics
     int64_t tiles_full = 0, tiles_partial = 0, tiles_empty = 0, gather_rows = 0;
     int64_t plan_ns = 0;
+    int64_t phase_ns[5] = {0, 0, 0, 0, 0};  // ingest, regime, mapping, tasks, upload
     // device copy
     int32_t device = -1;
     void *dev = nullptr;
-    size_t dev_bytes = 0;
-    const Task *d_tasks = nullptr;
-    const TileRec *d_tiles = nullptr;
-    const int32_t *d_gidx = nullptr;
-    const uint32_t *d_head_flags = nullptr;
+    size_t dev_cap = 0;
+    hipEvent_t uploaded = nullptr;
 };
 
 static int ilog2(int v)
@@ -228,7 +243,18 @@ inline FrameSet frames_of(const Geo &g, bool tm, int64_t lo, int64_t hi)
     return f;
 }
 
-inline void range_rects(const Geo &g, int64_t p0, int64_t p1, std::vector<Rect> &out)
+// At most 6 rectangles: a raster range is <= 3, a range wrapping over the
+// frame end is two raster ranges.
+struct Rects {
+    Rect r[6];
+    int n = 0;
+    void clear() { n = 0; }
+    void push_back(const Rect &x) { r[n++] = x; }
+    const Rect *begin() const { return r; }
+    const Rect *end() const { return r + n; }
+};
+
+inline void range_rects(const Geo &g, int64_t p0, int64_t p1, Rects &out)
 {
     int64_t y0 = p0 / g.W, x0 = p0 % g.W, y1 = p1 / g.W, x1 = p1 % g.W;
     if (y0 == y1) { out.push_back({y0, y0, x0, x1}); return; }
@@ -238,7 +264,7 @@ inline void range_rects(const Geo &g, int64_t p0, int64_t p1, std::vector<Rect> 
 }
 
 // Pixels covered by logical positions [lo, hi] of a head.
-inline void pixel_rects(const Geo &g, bool tm, int64_t lo, int64_t hi, std::vector<Rect> &out)
+inline void pixel_rects(const Geo &g, bool tm, int64_t lo, int64_t hi, Rects &out)
 {
     out.clear();
     if (tm) { range_rects(g, lo / g.T, hi / g.T, out); return; }
@@ -255,7 +281,7 @@ enum { kEmpty = 0, kFull = 1, kPart = 2 };
 
 struct VideoTileSets {
     FrameSet f;
-    std::vector<Rect> r;
+    Rects r;
 };
 
 inline int classify_video(int pattern, int64_t anchor, int64_t radius, const VideoTileSets &q, const VideoTileSets &k,
@@ -302,26 +328,98 @@ struct HeadOut {
     std::vector<TileRec> tiles;  // k0/offsets relative to this head's gidx block
     std::vector<int32_t> gidx;
     int64_t full = 0, part = 0, empty = 0, grows = 0;
-    int32_t status = BSA_OK;
-    std::string err;
+    void clear()
+    {
+        tasks.clear();
+        tiles.clear();
+        gidx.clear();
+        full = part = empty = grows = 0;
+    }
 };
+
+// Persistent worker threads for the planner (creating threads on every
+// bsa_plan call costs more than the mapping of a small mask). One parallel
+// region runs at a time; a nested or concurrent region runs on the caller.
+class WorkerPool {
+  public:
+    static WorkerPool &get()
+    {
+        static WorkerPool *pool = new WorkerPool();  // lives until process exit
+        return *pool;
+    }
+
+    void run(int64_t n, const std::function<void(int64_t)> &f)
+    {
+        if (n <= 0) return;
+        std::unique_lock<std::mutex> region(region_mu_, std::try_to_lock);
+        if (n == 1 || in_worker_ || !region.owns_lock() || workers_.empty()) {
+            for (int64_t i = 0; i < n; ++i) f(i);
+            return;
+        }
+        {
+            std::lock_guard<std::mutex> g(mu_);
+            job_ = &f;
+            n_ = n;
+            next_.store(0);
+            pending_ = (int)workers_.size();
+            ++gen_;
+        }
+        cv_.notify_all();
+        drain();
+        std::unique_lock<std::mutex> g(mu_);
+        done_cv_.wait(g, [&] { return pending_ == 0; });
+        job_ = nullptr;
+    }
+
+  private:
+    WorkerPool()
+    {
+        unsigned hc = std::thread::hardware_concurrency();
+        const int nt = (int)std::max(1u, std::min(hc, 32u)) - 1;
+        for (int t = 0; t < nt; ++t) workers_.emplace_back([this] { loop(); });
+        for (auto &w : workers_) w.detach();
+    }
+
+    void drain()
+    {
+        for (int64_t i; (i = next_.fetch_add(1)) < n_;) (*job_)(i);
+    }
+
+    void loop()
+    {
+        in_worker_ = true;
+        uint64_t seen = 0;
+        for (;;) {
+            {
+                std::unique_lock<std::mutex> g(mu_);
+                cv_.wait(g, [&] { return gen_ != seen; });
+                seen = gen_;
+            }
+            drain();
+            {
+                std::lock_guard<std::mutex> g(mu_);
+                if (--pending_ == 0) done_cv_.notify_one();
+            }
+        }
+    }
+
+    std::mutex region_mu_, mu_;
+    std::condition_variable cv_, done_cv_;
+    std::vector<std::thread> workers_;
+    const std::function<void(int64_t)> *job_ = nullptr;
+    int64_t n_ = 0;
+    std::atomic<int64_t> next_{0};
+    int pending_ = 0;
+    uint64_t gen_ = 0;
+    static thread_local bool in_worker_;
+};
+thread_local bool WorkerPool::in_worker_ = false;
 
 template <class F>
 void parallel_for(int64_t n, F &&f)
 {
-    unsigned hc = std::thread::hardware_concurrency();
-    int nt = (int)std::min<int64_t>(n, std::max(1u, std::min(hc, 32u)));
-    if (nt <= 1) {
-        for (int64_t i = 0; i < n; ++i) f(i);
-        return;
-    }
-    std::atomic<int64_t> next{0};
-    std::vector<std::thread> th;
-    for (int t = 0; t < nt; ++t)
-        th.emplace_back([&] {
-            for (int64_t i; (i = next.fetch_add(1)) < n;) f(i);
-        });
-    for (auto &x : th) x.join();
+    const std::function<void(int64_t)> fn = f;
+    WorkerPool::get().run(n, fn);
 }
 
 }  // namespace
@@ -387,7 +485,10 @@ static void map_block_head(const bsa_plan_s &p, const bsa_mask_desc_t &m, int b,
     }
 }
 
-// VIDEO masks: classify every (query tile, key tile) of the head's layout.
+// VIDEO masks: for each query tile, classify the key tiles of a candidate
+// superset derived from the pattern (frames of the query tile and the anchor
+// frame; key pixels within the window of the query pixels); every tile outside
+// it is provably empty. Candidates are classified exactly.
 static void map_video_head(const bsa_plan_s &p, int b, int h, int BQ, HeadOut &out)
 {
     const int64_t L = p.L;
@@ -396,6 +497,7 @@ static void map_video_head(const bsa_plan_s &p, int b, int h, int BQ, HeadOut &o
     const int pat = p.head_pattern[h];
     const int64_t nqt = (L + BQ - 1) / BQ, nkt = (L + kTileK - 1) / kTileK;
     const int64_t bh = (int64_t)b * p.H + h;
+    const int64_t r = p.radius, W = p.Wg, Hg = p.Hg, HW = g.HW;
     std::vector<VideoTileSets> ks(nkt);
     for (int64_t tk = 0; tk < nkt; ++tk) {
         int64_t k0 = tk * kTileK, k1 = std::min<int64_t>(k0 + kTileK, L);
@@ -403,22 +505,58 @@ static void map_video_head(const bsa_plan_s &p, int b, int h, int BQ, HeadOut &o
         if (pat == BSA_PAT_TEMPORAL) pixel_rects(g, tm, k0, k1 - 1, ks[tk].r);
     }
     VideoTileSets qs;
+    std::vector<std::pair<int64_t, int64_t>> cand;  // key-tile index ranges [t0, t1]
+    auto add_keys = [&](int64_t lo, int64_t hi) {   // key positions [lo, hi]
+        lo = std::max<int64_t>(lo, 0);
+        hi = std::min<int64_t>(hi, L - 1);
+        if (lo <= hi) cand.push_back({lo / kTileK, hi / kTileK});
+    };
     out.tasks.reserve(nqt);
+    int64_t computed = 0;
     for (int64_t tq = 0; tq < nqt; ++tq) {
         const int64_t q0 = tq * BQ, q1 = std::min<int64_t>(q0 + BQ, L);
         if (pat == BSA_PAT_SPATIAL) qs.f = frames_of(g, tm, q0, q1 - 1);
         if (pat == BSA_PAT_TEMPORAL) pixel_rects(g, tm, q0, q1 - 1, qs.r);
-        Task t{(int32_t)bh, (int32_t)q0, (int32_t)out.tiles.size(), 0};
-        for (int64_t tk = 0; tk < nkt; ++tk) {
-            const int64_t k0 = tk * kTileK;
-            int c = classify_video(pat, p.anchor, p.radius, qs, ks[tk], k0 + kTileK > L);
-            if (c == kEmpty) { ++out.empty; continue; }
-            out.tiles.push_back({(int32_t)k0, c == kFull ? 0u : kPartial});
-            if (c == kFull) ++out.full; else ++out.part;
+        cand.clear();
+        if (pat == BSA_PAT_SPATIAL && !tm) {
+            const int64_t fa = q0 / HW, fb = (q1 - 1) / HW;
+            add_keys(fa * HW, (fb + 1) * HW - 1);
+            add_keys((int64_t)p.anchor * HW, ((int64_t)p.anchor + 1) * HW - 1);
+        } else if (pat == BSA_PAT_TEMPORAL && tm) {
+            // key pixels within the window of a query rectangle, one pixel range
+            // per window row; a pixel owns T consecutive positions
+            for (const Rect &rc : qs.r) {
+                const int64_t xa = std::max<int64_t>(0, rc.x0 - r), xb = std::min<int64_t>(W - 1, rc.x1 + r);
+                for (int64_t y = std::max<int64_t>(0, rc.y0 - r); y <= std::min<int64_t>(Hg - 1, rc.y1 + r); ++y)
+                    add_keys((y * W + xa) * p.T, (y * W + xb + 1) * p.T - 1);
+            }
+        } else if (pat == BSA_PAT_TEMPORAL) {
+            // frame-major: the band of window rows, once per frame
+            int64_t ymin = Hg, ymax = -1;
+            for (const Rect &rc : qs.r) { ymin = std::min(ymin, rc.y0); ymax = std::max(ymax, rc.y1); }
+            const int64_t ya = std::max<int64_t>(0, ymin - r), yb = std::min<int64_t>(Hg - 1, ymax + r);
+            for (int64_t t = 0; t < p.T; ++t) add_keys(t * HW + ya * W, t * HW + (yb + 1) * W - 1);
+        } else {
+            add_keys(0, L - 1);
         }
+        std::sort(cand.begin(), cand.end());
+        Task t{(int32_t)bh, (int32_t)q0, (int32_t)out.tiles.size(), 0};
+        int64_t last = -1;
+        for (const auto &c : cand) {
+            for (int64_t tk = std::max(c.first, last + 1); tk <= c.second; ++tk) {
+                const int64_t k0 = tk * kTileK;
+                int cl = classify_video(pat, p.anchor, p.radius, qs, ks[tk], k0 + kTileK > L);
+                if (cl == kEmpty) continue;
+                out.tiles.push_back({(int32_t)k0, cl == kFull ? 0u : kPartial});
+                if (cl == kFull) ++out.full; else ++out.part;
+            }
+            last = std::max(last, c.second);
+        }
+        computed += (int64_t)out.tiles.size() - t.tb;
         t.te = (int32_t)out.tiles.size();
         out.tasks.push_back(t);
     }
+    out.empty = nqt * nkt - computed;
 }
 
 // SLICE masks: each M-query block's sorted key list packed into gather tiles
@@ -607,81 +745,216 @@ static int32_t choose_regime(const bsa_mask_desc_t &m, int32_t B, int32_t H, int
 }
 
 // ---------------------------------------------------------------------------
+// plan memory: pools and the per-device upload stream
+// ---------------------------------------------------------------------------
+
+namespace {
+
+constexpr size_t kPoolCap = (size_t)1 << 30;  // cached bytes per pool
+
+BlockPool &pinned_pool()
+{
+    static BlockPool *pool = new BlockPool(
+        [](size_t n) -> void * {
+            void *p = nullptr;
+            return hipHostMalloc(&p, n, hipHostMallocDefault) == hipSuccess ? p : nullptr;
+        },
+        [](void *p) { (void)hipHostFree(p); }, kPoolCap);
+    return *pool;
+}
+
+struct DeviceRt {
+    hipStream_t upload = nullptr;  // non-blocking: uploads never wait for other streams' work
+    std::unique_ptr<BlockPool> pool;
+};
+
+// Per-device runtime, created on first use (the caller has the device current).
+DeviceRt *device_rt(int dev, std::string &err)
+{
+    static std::mutex mu;
+    static std::map<int, DeviceRt *> rts;
+    std::lock_guard<std::mutex> g(mu);
+    auto it = rts.find(dev);
+    if (it != rts.end()) return it->second;
+    DeviceRt *rt = new DeviceRt;
+    hipError_t e = hipStreamCreateWithFlags(&rt->upload, hipStreamNonBlocking);
+    if (e != hipSuccess) {
+        err = std::string("hipStreamCreateWithFlags: ") + hipGetErrorString(e);
+        delete rt;
+        return nullptr;
+    }
+    rt->pool.reset(new BlockPool(
+        [dev](size_t n) -> void * {
+            int cur = 0;
+            (void)hipGetDevice(&cur);
+            (void)hipSetDevice(dev);
+            void *p = nullptr;
+            hipError_t e2 = hipMalloc(&p, n);
+            (void)hipSetDevice(cur);
+            return e2 == hipSuccess ? p : nullptr;
+        },
+        [dev](void *p) {
+            int cur = 0;
+            (void)hipGetDevice(&cur);
+            (void)hipSetDevice(dev);
+            (void)hipFree(p);
+            (void)hipSetDevice(cur);
+        },
+        kPoolCap));
+    rts[dev] = rt;
+    return rt;
+}
+
+size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
 // task organisation
 // ---------------------------------------------------------------------------
 
 // One task per (batch, head, query tile) -- also for query tiles without any
 // key tile, so that every output row is written. Tasks are ordered longest
-// first (LPT) so the tail of the grid holds the cheapest work.
-static void organise_tasks(bsa_plan_s &p, std::vector<HeadOut> &heads)
+// first (LPT, a stable counting sort on the tile count) so the tail of the
+// grid holds the cheapest work. The heads' outputs are copied in parallel
+// into the plan image.
+static int32_t organise_tasks(bsa_plan_s &p, const std::vector<HeadOut *> &heads)
 {
-    size_t nt = 0, nr = 0, ng = 0;
-    for (auto &h : heads) { nt += h.tasks.size(); nr += h.tiles.size(); ng += h.gidx.size(); }
-    p.tasks.reserve(nt);
-    p.tiles.reserve(nr);
-    p.gidx.reserve(ng);
-    for (auto &h : heads) {
-        const int32_t toff = (int32_t)p.tiles.size(), goff = (int32_t)p.gidx.size();
-        for (Task t : h.tasks) { t.tb += toff; t.te += toff; p.tasks.push_back(t); }
-        for (TileRec r : h.tiles) {
-            if (p.mode == kModeGather) r.k0 += goff;
-            p.tiles.push_back(r);
-        }
-        p.gidx.insert(p.gidx.end(), h.gidx.begin(), h.gidx.end());
+    const size_t nh = heads.size();
+    std::vector<int64_t> t_off(nh + 1, 0), r_off(nh + 1, 0), g_off(nh + 1, 0);
+    int32_t max_cost = 0;
+    for (size_t i = 0; i < nh; ++i) {
+        const HeadOut &h = *heads[i];
+        t_off[i + 1] = t_off[i] + (int64_t)h.tasks.size();
+        r_off[i + 1] = r_off[i] + (int64_t)h.tiles.size();
+        g_off[i + 1] = g_off[i] + (int64_t)h.gidx.size();
         p.tiles_full += h.full;
         p.tiles_partial += h.part;
         p.tiles_empty += h.empty;
         p.gather_rows += h.grows;
-        std::vector<Task>().swap(h.tasks);
-        std::vector<TileRec>().swap(h.tiles);
-        std::vector<int32_t>().swap(h.gidx);
+        for (const Task &t : h.tasks) max_cost = std::max(max_cost, t.te - t.tb);
     }
-    std::stable_sort(p.tasks.begin(), p.tasks.end(), [](const Task &a, const Task &b) { return (a.te - a.tb) > (b.te - b.tb); });
+    p.ntasks = t_off[nh];
+    p.ntiles = r_off[nh];
+    p.ngidx = g_off[nh];
+    p.off_tasks = 0;
+    p.off_tiles = align_up(std::max<int64_t>(1, p.ntasks) * sizeof(Task));
+    p.off_gidx = p.off_tiles + align_up(std::max<int64_t>(1, p.ntiles) * sizeof(TileRec));
+    p.off_flags = p.off_gidx + align_up(std::max<int64_t>(1, p.ngidx) * sizeof(int32_t));
+    p.img_bytes = p.off_flags + align_up((size_t)p.H * sizeof(uint32_t));
+    if (p.device >= 0) {
+        p.img = (uint8_t *)pinned_pool().acquire(p.img_bytes, &p.img_cap);
+        if (!p.img) return fail(BSA_ERR_OUT_OF_MEMORY, "pinned host allocation of %zu bytes failed", p.img_bytes);
+        p.img_pinned = true;
+    } else {
+        p.img_vec.resize(p.img_bytes);
+        p.img = p.img_vec.data();
+        p.img_cap = p.img_bytes;
+    }
+    // tiles and gather indices, per head in parallel; tasks unsorted into a scratch list
+    std::vector<Task> unsorted((size_t)p.ntasks);
+    TileRec *tiles = (TileRec *)(p.img + p.off_tiles);
+    int32_t *gidx = (int32_t *)(p.img + p.off_gidx);
+    const bool gather = p.mode == kModeGather;
+    parallel_for((int64_t)nh, [&](int64_t i) {
+        const HeadOut &h = *heads[i];
+        const int32_t toff = (int32_t)r_off[i], goff = (int32_t)g_off[i];
+        Task *td = unsorted.data() + t_off[i];
+        for (size_t k = 0; k < h.tasks.size(); ++k) {
+            Task t = h.tasks[k];
+            t.tb += toff;
+            t.te += toff;
+            td[k] = t;
+        }
+        TileRec *rd = tiles + r_off[i];
+        if (gather) {
+            for (size_t k = 0; k < h.tiles.size(); ++k) rd[k] = {h.tiles[k].k0 + goff, h.tiles[k].aux};
+        } else if (!h.tiles.empty()) {
+            std::memcpy(rd, h.tiles.data(), h.tiles.size() * sizeof(TileRec));
+        }
+        if (!h.gidx.empty()) std::memcpy(gidx + g_off[i], h.gidx.data(), h.gidx.size() * sizeof(int32_t));
+    });
+    // stable LPT order: counting sort on the tile count, descending
+    Task *tasks = (Task *)(p.img + p.off_tasks);
+    std::vector<int64_t> bucket((size_t)max_cost + 2, 0);
+    for (const Task &t : unsorted) ++bucket[(size_t)(max_cost - (t.te - t.tb)) + 1];
+    for (size_t c = 1; c < bucket.size(); ++c) bucket[c] += bucket[c - 1];
+    for (const Task &t : unsorted) tasks[bucket[(size_t)(max_cost - (t.te - t.tb))]++] = t;
+    uint32_t *flags = (uint32_t *)(p.img + p.off_flags);
+    for (int h = 0; h < p.H; ++h)
+        flags[h] = (p.head_layout[h] ? kHeadTemporalMajor : 0u) | ((uint32_t)p.head_pattern[h] << kHeadPatShift);
+    return BSA_OK;
 }
 
 // ---------------------------------------------------------------------------
-// device upload
+// device upload (asynchronous, on the device's upload stream)
 // ---------------------------------------------------------------------------
-
-static size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 static int32_t upload(bsa_plan_s &p)
 {
     if (p.device < 0) return BSA_OK;
+    int cur = 0;
+    (void)hipGetDevice(&cur);
     hipError_t e = hipSetDevice(p.device);
     if (e != hipSuccess) return fail(BSA_ERR_HIP, "hipSetDevice(%d): %s", p.device, hipGetErrorString(e));
-    const size_t s_tasks = align_up(std::max<size_t>(1, p.tasks.size()) * sizeof(Task));
-    const size_t s_tiles = align_up(std::max<size_t>(1, p.tiles.size()) * sizeof(TileRec));
-    const size_t s_gidx = align_up(std::max<size_t>(1, p.gidx.size()) * sizeof(int32_t));
-    const size_t s_flags = align_up(p.head_flags.size() * sizeof(uint32_t));
-    p.dev_bytes = s_tasks + s_tiles + s_gidx + s_flags;
-    e = hipMalloc(&p.dev, p.dev_bytes);
-    if (e != hipSuccess) {
-        p.dev = nullptr;
-        return fail(e == hipErrorOutOfMemory ? BSA_ERR_OUT_OF_MEMORY : BSA_ERR_HIP, "hipMalloc(%zu): %s", p.dev_bytes,
-                    hipGetErrorString(e));
+    std::string err;
+    DeviceRt *rt = device_rt(p.device, err);
+    int32_t st = BSA_OK;
+    if (!rt) {
+        st = fail(BSA_ERR_HIP, "%s", err.c_str());
+    } else if (!(p.dev = rt->pool->acquire(p.img_bytes, &p.dev_cap))) {
+        st = fail(BSA_ERR_OUT_OF_MEMORY, "device allocation of %zu bytes failed", p.img_bytes);
+    } else if ((e = hipEventCreateWithFlags(&p.uploaded, hipEventDisableTiming)) != hipSuccess) {
+        p.uploaded = nullptr;
+        st = fail(BSA_ERR_HIP, "hipEventCreateWithFlags: %s", hipGetErrorString(e));
+    } else if ((e = hipMemcpyAsync(p.dev, p.img, p.img_bytes, hipMemcpyHostToDevice, rt->upload)) != hipSuccess ||
+               (e = hipEventRecord(p.uploaded, rt->upload)) != hipSuccess) {
+        st = fail(BSA_ERR_HIP, "plan upload: %s", hipGetErrorString(e));
     }
-    std::vector<uint8_t> host(p.dev_bytes, 0);
-    size_t off = 0;
-    auto put = [&](const void *src, size_t n, size_t sz) {
-        if (n) std::memcpy(host.data() + off, src, n);
-        size_t at = off;
-        off += sz;
-        return at;
-    };
-    size_t o_tasks = put(p.tasks.data(), p.tasks.size() * sizeof(Task), s_tasks);
-    size_t o_tiles = put(p.tiles.data(), p.tiles.size() * sizeof(TileRec), s_tiles);
-    size_t o_gidx = put(p.gidx.data(), p.gidx.size() * sizeof(int32_t), s_gidx);
-    size_t o_flags = put(p.head_flags.data(), p.head_flags.size() * sizeof(uint32_t), s_flags);
-    e = hipMemcpy(p.dev, host.data(), p.dev_bytes, hipMemcpyHostToDevice);
-    if (e != hipSuccess) return fail(BSA_ERR_HIP, "plan upload: %s", hipGetErrorString(e));
-    char *base = (char *)p.dev;
-    p.d_tasks = (const Task *)(base + o_tasks);
-    p.d_tiles = (const TileRec *)(base + o_tiles);
-    p.d_gidx = (const int32_t *)(base + o_gidx);
-    p.d_head_flags = (const uint32_t *)(base + o_flags);
-    return BSA_OK;
+    (void)hipSetDevice(cur);
+    return st;
 }
+
+// Give the plan's memory back to the pools (after its upload has completed).
+static void release_plan_memory(bsa_plan_s *p)
+{
+    if (p->uploaded) {
+        (void)hipEventSynchronize(p->uploaded);
+        (void)hipEventDestroy(p->uploaded);
+        p->uploaded = nullptr;
+    }
+    if (p->dev) {
+        std::string err;
+        if (DeviceRt *rt = device_rt(p->device, err)) rt->pool->release(p->dev, p->dev_cap);
+        p->dev = nullptr;
+    }
+    if (p->img && p->img_pinned) pinned_pool().release(p->img, p->img_cap);
+    p->img = nullptr;
+}
+
+// Reused per-head mapping buffers (their capacity survives across plans).
+namespace {
+struct Builder {
+    std::vector<HeadOut> heads;
+};
+std::mutex g_builder_mu;
+std::vector<Builder *> g_builders;
+
+Builder *take_builder()
+{
+    std::lock_guard<std::mutex> g(g_builder_mu);
+    if (g_builders.empty()) return new Builder;
+    Builder *b = g_builders.back();
+    g_builders.pop_back();
+    return b;
+}
+
+void give_builder(Builder *b)
+{
+    std::lock_guard<std::mutex> g(g_builder_mu);
+    g_builders.push_back(b);
+}
+}  // namespace
 
 // ---------------------------------------------------------------------------
 // C entry points
@@ -702,17 +975,23 @@ extern "C" int32_t bsa_plan(const bsa_mask_desc_t *logical_mask, int32_t B, int3
     if (!out_plan) return fail(BSA_ERR_INVALID_ARGUMENT, "out_plan is NULL");
     *out_plan = nullptr;
     const auto t_start = std::chrono::steady_clock::now();
+    auto now_ns = [&] {
+        return (int64_t)std::chrono::duration_cast<std::chrono::nanoseconds>(std::chrono::steady_clock::now() - t_start).count();
+    };
+    int64_t t_ingest = 0, t_regime = 0, t_map = 0, t_tasks = 0;
     try {
         bsa_plan_opts_t o;
         bsa_plan_opts_default(&o);
         if (opts) o = *opts;
         int32_t st = validate(logical_mask, B, H, L, d, block_q, block_k, o);
         if (st != BSA_OK) return st;
+        t_ingest = now_ns();
         if (std::getenv("BSA_TEST_FAIL_ALLOC")) return fail(BSA_ERR_OUT_OF_MEMORY, "simulated allocation failure");
         const bsa_mask_desc_t &m = *logical_mask;
         int regime = 0;
         st = choose_regime(m, B, H, L, block_q, block_k, o, &regime);
         if (st != BSA_OK) return st;
+        t_regime = now_ns();
 
         std::unique_ptr<bsa_plan_s> p(new bsa_plan_s);
         p->B = B; p->H = H; p->L = L; p->d = d; p->dtype = o.dtype;
@@ -734,27 +1013,39 @@ extern "C" int32_t bsa_plan(const bsa_mask_desc_t *logical_mask, int32_t B, int3
             p->bk_shift = ilog2(p->sub_k);
             p->nsk = kTileK / p->sub_k;
         }
-        p->head_flags.resize(H);
-        for (int h = 0; h < H; ++h)
-            p->head_flags[h] = (p->head_layout[h] ? kHeadTemporalMajor : 0u) | ((uint32_t)p->head_pattern[h] << kHeadPatShift);
-
-        std::vector<HeadOut> heads((size_t)B * H);
+        Builder *builder = take_builder();
+        std::unique_ptr<Builder, void (*)(Builder *)> builder_guard(builder, give_builder);
+        std::vector<HeadOut> &heads = builder->heads;
+        if (heads.size() < (size_t)B * H) heads.resize((size_t)B * H);
         parallel_for((int64_t)B * H, [&](int64_t bh) {
+            heads[bh].clear();
             const int b = (int)(bh / H), h = (int)(bh % H);
             if (p->mode == kModeBlock) map_block_head(*p, m, b, h, R.tile_q, heads[bh]);
             else if (p->mode == kModeVideo) map_video_head(*p, b, h, R.tile_q, heads[bh]);
             else map_slice_head(*p, m, b, h, heads[bh]);
         });
         size_t total_tiles = 0;
-        for (auto &h : heads) total_tiles += h.tiles.size();
+        for (int64_t i = 0; i < (int64_t)B * H; ++i) total_tiles += heads[i].tiles.size();
         if (total_tiles >= (size_t)INT32_MAX) return fail(BSA_ERR_UNSUPPORTED, "plan has more than 2^31 tiles");
-        organise_tasks(*p, heads);
-        st = upload(*p);
+        t_map = now_ns();
+        std::vector<HeadOut *> hp((size_t)B * H);
+        for (int64_t i = 0; i < (int64_t)B * H; ++i) hp[i] = &heads[i];
+        st = organise_tasks(*p, hp);
+        t_tasks = now_ns();
+        if (st == BSA_OK) st = upload(*p);
         if (st != BSA_OK) {
-            if (p->dev) (void)hipFree(p->dev);
+            release_plan_memory(p.get());
             return st;
         }
-        p->plan_ns = std::chrono::duration_cast<std::chrono::nanoseconds>(std::chrono::steady_clock::now() - t_start).count();
+        p->plan_ns = now_ns();
+        const int64_t marks[6] = {0, t_ingest, t_regime, t_map, t_tasks, p->plan_ns};
+        for (int i = 0; i < 5; ++i) p->phase_ns[i] = marks[i + 1] - marks[i];
+        if (const char *lg = std::getenv("BSA_LOG"); lg && std::atoi(lg) >= 1)
+            std::fprintf(stderr, "[bsa] plan %.3f ms: ingest %.3f, regime %.3f (r%d), mapping %.3f, tasks %.3f, upload %.3f; "
+                                 "tiles full %lld partial %lld empty %lld\n",
+                         p->plan_ns * 1e-6, p->phase_ns[0] * 1e-6, p->phase_ns[1] * 1e-6, p->regime, p->phase_ns[2] * 1e-6,
+                         p->phase_ns[3] * 1e-6, p->phase_ns[4] * 1e-6, (long long)p->tiles_full,
+                         (long long)p->tiles_partial, (long long)p->tiles_empty);
         *out_plan = p.release();
         return BSA_OK;
     } catch (const std::bad_alloc &) {
@@ -767,13 +1058,7 @@ extern "C" int32_t bsa_plan(const bsa_mask_desc_t *logical_mask, int32_t B, int3
 extern "C" void bsa_plan_destroy(bsa_plan_t p)
 {
     if (!p) return;
-    if (p->dev) {
-        int cur = 0;
-        (void)hipGetDevice(&cur);
-        (void)hipSetDevice(p->device);
-        (void)hipFree(p->dev);
-        (void)hipSetDevice(cur);
-    }
+    release_plan_memory(p);
     delete p;
 }
 
@@ -796,14 +1081,15 @@ extern "C" int32_t bsa_forward(bsa_plan_t p, const void *Q, const void *K, const
     if (!Q || !K || !V || !O) return fail(BSA_ERR_INVALID_ARGUMENT, "Q, K, V and O must be non-NULL device pointers");
     if (((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V | (uintptr_t)O) & 15)
         return fail(BSA_ERR_INVALID_ARGUMENT, "Q, K, V and O must be 16-byte aligned");
-    if (p->tasks.empty()) return BSA_OK;
+    if (p->ntasks == 0) return BSA_OK;
     KernelArgs a{};
     a.Q = Q; a.K = K; a.V = V; a.O = O;
-    a.tasks = p->d_tasks;
-    a.tiles = p->d_tiles;
-    a.gidx = p->d_gidx;
-    a.head_flags = p->d_head_flags;
-    a.ntasks = (int32_t)p->tasks.size();
+    const uint8_t *dev = (const uint8_t *)p->dev;
+    a.tasks = (const Task *)(dev + p->off_tasks);
+    a.tiles = (const TileRec *)(dev + p->off_tiles);
+    a.gidx = (const int32_t *)(dev + p->off_gidx);
+    a.head_flags = (const uint32_t *)(dev + p->off_flags);
+    a.ntasks = (int32_t)p->ntasks;
     a.H = p->H;
     a.L = (int32_t)p->L;
     a.T = p->T; a.HW = p->Hg * p->Wg; a.W = p->Wg;
@@ -817,7 +1103,9 @@ extern "C" int32_t bsa_forward(bsa_plan_t p, const void *Q, const void *K, const
     int cur = 0;
     (void)hipGetDevice(&cur);
     if (cur != p->device) (void)hipSetDevice(p->device);
-    hipError_t e = launch_forward(a, kRegimes[p->regime].waves, p->d, p->dtype, (hipStream_t)stream);
+    // the launch is ordered after the plan's upload (a no-op once it is done)
+    hipError_t e = hipStreamWaitEvent((hipStream_t)stream, p->uploaded, 0);
+    if (e == hipSuccess) e = launch_forward(a, kRegimes[p->regime].waves, p->d, p->dtype, (hipStream_t)stream);
     if (cur != p->device) (void)hipSetDevice(cur);
     if (e != hipSuccess) return fail(BSA_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
     return BSA_OK;
@@ -831,14 +1119,15 @@ extern "C" int32_t bsa_plan_info(bsa_plan_t p, bsa_plan_info_t *out)
     out->tile_q = R.tile_q;
     out->tile_k = kTileK;
     out->gather = R.family;
-    out->tasks = (int64_t)p->tasks.size();
+    out->tasks = p->ntasks;
     out->tiles_full = p->tiles_full;
     out->tiles_partial = p->tiles_partial;
     out->tiles_empty = p->tiles_empty;
     out->gather_rows = p->gather_rows;
     out->executed_pairs = (double)(p->tiles_full + p->tiles_partial) * R.tile_q * kTileK;
-    out->device_bytes = (int64_t)p->dev_bytes;
+    out->device_bytes = (int64_t)p->dev_cap;
     out->plan_ns = p->plan_ns;
+    for (int i = 0; i < 5; ++i) out->phase_ns[i] = p->phase_ns[i];
     return BSA_OK;
 }
 
@@ -848,17 +1137,20 @@ extern "C" int32_t bsa_plan_coverage(bsa_plan_t p, int32_t b, int32_t h, bsa_cov
     if (b < 0 || b >= p->B || h < 0 || h >= p->H) return fail(BSA_ERR_INVALID_ARGUMENT, "head (%d, %d) out of range", b, h);
     const Regime &R = kRegimes[p->regime];
     const int32_t bh = b * p->H + h;
-    for (const Task &t : p->tasks) {
+    const Task *tasks = p->tasks();
+    const TileRec *tiles = p->tiles();
+    for (int64_t ti = 0; ti < p->ntasks; ++ti) {
+        const Task &t = tasks[ti];
         if (t.bh != bh) continue;
         for (int32_t i = t.tb; i < t.te; ++i) {
-            const TileRec &r = p->tiles[i];
+            const TileRec &r = tiles[i];
             bsa_tile_record_t rec{};
             rec.q0 = t.q0;
             rec.q1 = std::min<int64_t>(t.q0 + R.tile_q, p->L);
             rec.kind = (r.aux & kPartial) ? BSA_TILE_PARTIAL : BSA_TILE_FULL;
             if (p->mode == kModeGather) {
                 rec.predicate = BSA_PRED_LIST;
-                rec.keys = p->gidx.data() + r.k0;
+                rec.keys = p->gidx() + r.k0;
                 rec.nkeys = r.aux & kAuxMask;
             } else {
                 rec.predicate = p->mode == kModeBlock ? BSA_PRED_SUBBLOCK : BSA_PRED_VIDEO;

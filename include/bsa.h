@@ -132,6 +132,8 @@ typedef struct {
     double executed_pairs;         /* tile_q * tile_k per computed tile            */
     int64_t device_bytes;          /* device memory owned by the plan              */
     int64_t plan_ns;               /* wall time of bsa_plan                         */
+    int64_t phase_ns[5];           /* of which: ingest/validation, regime lookup,
+                                      physical mapping, task organisation, upload */
 } bsa_plan_info_t;
 
 typedef struct {
