@@ -48,7 +48,8 @@ class PlanOpts(ctypes.Structure):
 
 class PlanInfo(ctypes.Structure):
     _fields_ = [("regime", ctypes.c_int32), ("tile_q", ctypes.c_int32), ("tile_k", ctypes.c_int32),
-                ("gather", ctypes.c_int32), ("tasks", ctypes.c_int64), ("tiles_full", ctypes.c_int64),
+                ("gather", ctypes.c_int32), ("tasks", ctypes.c_int64), ("workgroups", ctypes.c_int64),
+                ("tiles_full", ctypes.c_int64),
                 ("tiles_partial", ctypes.c_int64), ("tiles_empty", ctypes.c_int64), ("gather_rows", ctypes.c_int64),
                 ("executed_pairs", ctypes.c_double), ("device_bytes", ctypes.c_int64), ("plan_ns", ctypes.c_int64),
                 ("phase_ns", ctypes.c_int64 * 5)]

@@ -175,6 +175,7 @@ struct bsa_plan_s {
     int32_t T = 0, Hg = 0, Wg = 0, anchor = 0, radius = 0;
     int32_t bq_shift = 0, bk_shift = 0, nsk = 1, sub_q = 0, sub_k = 0;
     int32_t mode = 0;
+    int32_t task_order = 1;  // 0 = XCD segments, 1 = longest first
     std::vector<uint8_t> head_layout, head_pattern;
     // image
     uint8_t *img = nullptr;
@@ -182,7 +183,8 @@ struct bsa_plan_s {
     bool img_pinned = false;
     std::vector<uint8_t> img_vec;
     size_t off_tasks = 0, off_tiles = 0, off_gidx = 0, off_flags = 0;
-    int64_t ntasks = 0, ntiles = 0, ngidx = 0;
+    int64_t ntasks = 0, ntiles = 0, ngidx = 0;  // ntasks: launched workgroups (incl. padding)
+    int64_t nreal_tasks = 0;                    // one per (batch, head, query tile)
     const Task *tasks() const { return (const Task *)(img + off_tasks); }
     const TileRec *tiles() const { return (const TileRec *)(img + off_tiles); }
     const int32_t *gidx() const { return (const int32_t *)(img + off_gidx); }
@@ -814,10 +816,23 @@ size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 // ---------------------------------------------------------------------------
 
 // One task per (batch, head, query tile) -- also for query tiles without any
-// key tile, so that every output row is written. Tasks are ordered longest
-// first (LPT, a stable counting sort on the tile count) so the tail of the
-// grid holds the cheapest work. The heads' outputs are copied in parallel
-// into the plan image.
+// key tile, so that every output row is written. The heads' outputs are
+// copied in parallel into the plan image, then ordered for the device:
+//  - XCD order (default): workgroup i of a launch runs on XCD i % X (X = 8 on
+//    MI355X), each XCD with its own L2. Tasks in (head, query tile) order --
+//    neighbouring query tiles share most of their key tiles -- are cut into X
+//    contiguous segments of equal tile count (plus one per task), and slot
+//    i*X + x of the launch takes task i of segment x, so each XCD streams one
+//    contiguous piece of the key space through its L2. Segments shorter than
+//    the longest are padded with no-op tasks (bh = -1).
+//  - LPT order: longest task first (a stable counting sort on the tile
+//    count), so the tail of the grid holds the cheapest work.
+static int xcd_count()
+{
+    if (const char *e = std::getenv("BSA_XCDS")) return std::max(1, std::atoi(e));
+    return 8;
+}
+
 static int32_t organise_tasks(bsa_plan_s &p, const std::vector<HeadOut *> &heads)
 {
     const size_t nh = heads.size();
@@ -834,9 +849,33 @@ static int32_t organise_tasks(bsa_plan_s &p, const std::vector<HeadOut *> &heads
         p.gather_rows += h.grows;
         for (const Task &t : h.tasks) max_cost = std::max(max_cost, t.te - t.tb);
     }
-    p.ntasks = t_off[nh];
+    const int64_t nreal = t_off[nh];
     p.ntiles = r_off[nh];
     p.ngidx = g_off[nh];
+    // XCD segments over the locality-ordered tasks (computed from the per-head
+    // lists before they are copied)
+    const int X = p.task_order == 0 ? xcd_count() : 1;
+    std::vector<int64_t> seg_start(X + 1, nreal);
+    seg_start[0] = 0;
+    int64_t seg_len = nreal;
+    if (X > 1 && nreal > 0) {
+        int64_t total = 0;
+        for (size_t i = 0; i < nh; ++i)
+            for (const Task &t : heads[i]->tasks) total += (t.te - t.tb) + 1;
+        int64_t acc = 0, idx = 0;
+        int x = 1;
+        for (size_t i = 0; i < nh && x < X; ++i)
+            for (const Task &t : heads[i]->tasks) {
+                acc += (t.te - t.tb) + 1;
+                ++idx;
+                while (x < X && acc * X >= total * x) seg_start[x++] = idx;
+            }
+        while (x < X) seg_start[x++] = nreal;
+        seg_len = 0;
+        for (int k = 0; k < X; ++k) seg_len = std::max(seg_len, seg_start[k + 1] - seg_start[k]);
+    }
+    p.ntasks = X > 1 ? seg_len * X : nreal;
+    p.nreal_tasks = nreal;
     p.off_tasks = 0;
     p.off_tiles = align_up(std::max<int64_t>(1, p.ntasks) * sizeof(Task));
     p.off_gidx = p.off_tiles + align_up(std::max<int64_t>(1, p.ntiles) * sizeof(TileRec));
@@ -852,7 +891,7 @@ static int32_t organise_tasks(bsa_plan_s &p, const std::vector<HeadOut *> &heads
         p.img_cap = p.img_bytes;
     }
     // tiles and gather indices, per head in parallel; tasks unsorted into a scratch list
-    std::vector<Task> unsorted((size_t)p.ntasks);
+    std::vector<Task> unsorted((size_t)nreal);
     TileRec *tiles = (TileRec *)(p.img + p.off_tiles);
     int32_t *gidx = (int32_t *)(p.img + p.off_gidx);
     const bool gather = p.mode == kModeGather;
@@ -874,12 +913,21 @@ static int32_t organise_tasks(bsa_plan_s &p, const std::vector<HeadOut *> &heads
         }
         if (!h.gidx.empty()) std::memcpy(gidx + g_off[i], h.gidx.data(), h.gidx.size() * sizeof(int32_t));
     });
-    // stable LPT order: counting sort on the tile count, descending
     Task *tasks = (Task *)(p.img + p.off_tasks);
-    std::vector<int64_t> bucket((size_t)max_cost + 2, 0);
-    for (const Task &t : unsorted) ++bucket[(size_t)(max_cost - (t.te - t.tb)) + 1];
-    for (size_t c = 1; c < bucket.size(); ++c) bucket[c] += bucket[c - 1];
-    for (const Task &t : unsorted) tasks[bucket[(size_t)(max_cost - (t.te - t.tb))]++] = t;
+    if (X > 1) {
+        const Task noop{-1, 0, 0, 0};
+        for (int x = 0; x < X; ++x)
+            for (int64_t i = 0; i < seg_len; ++i) {
+                const int64_t src = seg_start[x] + i;
+                tasks[i * X + x] = src < seg_start[x + 1] ? unsorted[src] : noop;
+            }
+    } else {
+        // stable LPT order: counting sort on the tile count, descending
+        std::vector<int64_t> bucket((size_t)max_cost + 2, 0);
+        for (const Task &t : unsorted) ++bucket[(size_t)(max_cost - (t.te - t.tb)) + 1];
+        for (size_t c = 1; c < bucket.size(); ++c) bucket[c] += bucket[c - 1];
+        for (const Task &t : unsorted) tasks[bucket[(size_t)(max_cost - (t.te - t.tb))]++] = t;
+    }
     uint32_t *flags = (uint32_t *)(p.img + p.off_flags);
     for (int h = 0; h < p.H; ++h)
         flags[h] = (p.head_layout[h] ? kHeadTemporalMajor : 0u) | ((uint32_t)p.head_pattern[h] << kHeadPatShift);
@@ -1000,6 +1048,7 @@ extern "C" int32_t bsa_plan(const bsa_mask_desc_t *logical_mask, int32_t B, int3
         p->T = o.T; p->Hg = o.Hg; p->Wg = o.Wg;
         p->anchor = m.anchor_frame; p->radius = m.radius;
         p->device = o.device;
+        if (const char *e = std::getenv("BSA_TASK_ORDER")) p->task_order = std::strcmp(e, "xcd") == 0 ? 0 : 1;
         p->head_layout.assign(H, 0);
         if (o.head_layout) p->head_layout.assign(o.head_layout, o.head_layout + H);
         p->head_pattern.assign(H, 0);
@@ -1119,7 +1168,8 @@ extern "C" int32_t bsa_plan_info(bsa_plan_t p, bsa_plan_info_t *out)
     out->tile_q = R.tile_q;
     out->tile_k = kTileK;
     out->gather = R.family;
-    out->tasks = p->ntasks;
+    out->tasks = p->nreal_tasks;
+    out->workgroups = p->ntasks;
     out->tiles_full = p->tiles_full;
     out->tiles_partial = p->tiles_partial;
     out->tiles_empty = p->tiles_empty;
@@ -1141,7 +1191,7 @@ extern "C" int32_t bsa_plan_coverage(bsa_plan_t p, int32_t b, int32_t h, bsa_cov
     const TileRec *tiles = p->tiles();
     for (int64_t ti = 0; ti < p->ntasks; ++ti) {
         const Task &t = tasks[ti];
-        if (t.bh != bh) continue;
+        if (t.bh != bh) continue;  // (no-op padding tasks have bh = -1)
         for (int32_t i = t.tb; i < t.te; ++i) {
             const TileRec &r = tiles[i];
             bsa_tile_record_t rec{};

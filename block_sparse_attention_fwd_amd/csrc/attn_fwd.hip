@@ -122,6 +122,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4
     const int lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
     const Task task = a.tasks[blockIdx.x];
+    if (task.bh < 0) return;  // padding task of an XCD segment
     const int bh = task.bh;
     const int h = bh % a.H;
     const uint32_t hflag = a.head_flags[h];

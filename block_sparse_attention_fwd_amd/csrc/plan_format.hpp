@@ -29,7 +29,7 @@ constexpr uint32_t kHeadTemporalMajor = 1u;   // bit 0: logical j = p*T + t
 constexpr uint32_t kHeadPatShift = 1;         // bits 1..2: video pattern
 
 struct Task {        // 16 bytes
-    int32_t bh;      // b * H + h
+    int32_t bh;      // b * H + h; -1 = no-op padding task
     int32_t q0;      // first logical query position of the tile
     int32_t tb, te;  // key-tile records [tb, te)
 };

@@ -124,7 +124,8 @@ typedef struct {
     int32_t regime;                /* regime id (see bsa_regime_info)              */
     int32_t tile_q, tile_k;        /* physical tile shape                          */
     int32_t gather;                /* 1 if key tiles are gathered row lists        */
-    int64_t tasks;                 /* workgroup tasks (one per query tile)         */
+    int64_t tasks;                 /* tasks: one per (batch, head, query tile)     */
+    int64_t workgroups;            /* launched workgroups (tasks + XCD padding)    */
     int64_t tiles_full;            /* key tiles computed without a mask            */
     int64_t tiles_partial;         /* key tiles with exact masking                 */
     int64_t tiles_empty;           /* (query tile, key tile) pairs skipped         */
