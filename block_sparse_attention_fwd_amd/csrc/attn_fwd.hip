@@ -58,25 +58,41 @@ struct Cfg {
     static constexpr int BQ = 32 * NW;
     static constexpr int BK = kTileK;
     static constexpr int ROWB = D * 2;                 // bytes per bf16 row
-    static constexpr int KROW = ROWB + 16;             // padded K row in LDS
-    static constexpr int KTILEB = BK * KROW;           // bytes per K tile
-    static constexpr int TILEB = BK * ROWB;            // bytes per V tile
+    static constexpr int TILEB = BK * ROWB;            // bytes per K or V tile
     static constexpr int CHUNKS = ROWB / 16;           // 16-byte chunks per row
     static constexpr int RPI = 1024 / ROWB;            // rows per wave-wide 1 KiB copy
     static constexpr int INSTS = BK / RPI / NW;        // copies per wave per tensor per tile
     static_assert(INSTS >= 1, "tile too small for the workgroup");
 };
 
-// Conflict-free LDS layouts. K rows are padded by 16 bytes: a read of one
-// 16-byte chunk from 8 or 16 consecutive rows then hits distinct banks. V rows
-// keep their natural 256/128-byte stride with the 16-byte chunks of row k
-// XOR-swizzled by swz_v(k & 3): the transposing read of 4 consecutive keys x
-// 32 contiguous bytes then hits distinct banks.
+// Conflict-free LDS layouts; rows keep their natural 256/128-byte stride and
+// the 16-byte chunks of a row are XOR-swizzled. K row r stores chunk c at
+// position c ^ swz_k(r): one chunk read from 8 or 16 consecutive rows hits
+// distinct banks. V row k stores chunk c at c ^ swz_v(k & 3): the transposing
+// read of 4 consecutive keys x 32 contiguous bytes hits distinct banks.
+template <int D>
+__device__ __forceinline__ int swz_k(int row) { return row & (D / 8 - 1); }
 template <int D>
 __device__ __forceinline__ int swz_v(int key_mod4)
 {
     return D == 128 ? (int)((0xAC60u >> (4 * key_mod4)) & 15u) : 2 * key_mod4;  // {0,6,12,10} / {0,2,4,6}
 }
+
+// Direct global -> LDS copy (global_load_lds_dwordx4): lane l writes the 16
+// bytes at its global address to LDS bytes [lds + 16 l, +16). It is issued
+// through inline assembly so that the compiler does not make every later LDS
+// read wait for it (it cannot tell that the reads use the other buffer);
+// completion is awaited explicitly (s_waitcnt vmcnt) before the barrier that
+// hands the buffer to the other waves. M0 carries the LDS address; no
+// compiler-generated code of this kernel uses M0.
+__device__ __forceinline__ void copy16_to_lds(const void *g, uint32_t lds)
+{
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+#pragma clang diagnostic pop
+}
+__device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 __device__ __forceinline__ float swap_halves_max(float x)
 {
@@ -114,8 +130,8 @@ template <int NW, int D>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4 ? 2 : 1, 2))) void bsa_fwd_bf16(KernelArgs a)
 {
     using C = Cfg<NW, D>;
-    __shared__ __attribute__((aligned(1024))) unsigned char ksm[2][C::KTILEB];  // [buffer] padded K tile
-    __shared__ __attribute__((aligned(1024))) unsigned char vsm[2][C::TILEB];   // [buffer] swizzled V tile
+    __shared__ __attribute__((aligned(1024))) unsigned char ksm[2][C::TILEB];  // [buffer] swizzled K tile
+    __shared__ __attribute__((aligned(1024))) unsigned char vsm[2][C::TILEB];  // [buffer] swizzled V tile
     __shared__ __attribute__((aligned(16))) int kcoord[2][C::BK];
 
     const int tid = threadIdx.x;
@@ -180,7 +196,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4
         int idx_nxt[C::INSTS];  // gathered logical key positions of the next tile to fetch
 
         auto load_indices = [&](int rec_i, int *dst) {
-            const TileRec r = a.tiles[rec_i];
+            const TileRec r = a.tiles[__builtin_amdgcn_readfirstlane(rec_i)];  // scalar load
             const int cnt = (int)(r.aux & kAuxMask);
 #pragma unroll
             for (int i = 0; i < C::INSTS; ++i) {
@@ -189,18 +205,20 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4
             }
         };
 
-        // global -> registers (in flight while the current tile is computed)
-        i32x4 stage_k[C::INSTS], stage_v[C::INSTS];
+        // global -> LDS copies of a tile (in flight while the previous tile is
+        // computed); the video key coordinates go through a register
         int stage_c = kNoKey;
-        auto fetch_tile = [&](int rec_i, const int *idx) {
-            const TileRec r = a.tiles[rec_i];
+        auto fetch_tile = [&](int rec_i, const int *idx, int buf) {
+            const TileRec r = a.tiles[__builtin_amdgcn_readfirstlane(rec_i)];
+            const uint32_t kl = (uint32_t)(uintptr_t)&ksm[buf][0], vl = (uint32_t)(uintptr_t)&vsm[buf][0];
 #pragma unroll
             for (int i = 0; i < C::INSTS; ++i) {
                 const int slot = (w * C::INSTS + i) * C::RPI + lane / C::CHUNKS;
                 const int kpos = gather ? idx[i] : min(r.k0 + slot, L - 1);
                 const int ktok = token(kpos);
-                stage_k[i] = *(const i32x4 *)(Kh + (size_t)ktok * D + 8 * pos);
-                stage_v[i] = *(const i32x4 *)(Vh + (size_t)ktok * D + 8 * (pos ^ swz_v<D>(slot & 3)));
+                const uint32_t off = (uint32_t)((w * C::INSTS + i) * 1024);
+                copy16_to_lds(Kh + (size_t)ktok * D + 8 * (pos ^ swz_k<D>(slot)), __builtin_amdgcn_readfirstlane(kl + off));
+                copy16_to_lds(Vh + (size_t)ktok * D + 8 * (pos ^ swz_v<D>(slot & 3)), __builtin_amdgcn_readfirstlane(vl + off));
             }
             if (video && w == 0) {
                 // per key slot: frame (spatial) or packed (y << 16) | x
@@ -217,26 +235,23 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4
                 stage_c = v;
             }
         };
-        // registers -> LDS buffer `buf`
-        auto store_tile = [&](int buf) {
-#pragma unroll
-            for (int i = 0; i < C::INSTS; ++i) {
-                const int slot = (w * C::INSTS + i) * C::RPI + lane / C::CHUNKS;
-                *LDS_PTR(i32x4, &ksm[buf][slot * C::KROW + 16 * pos]) = stage_k[i];
-                *LDS_PTR(i32x4, &vsm[buf][(w * C::INSTS + i) * 1024 + 16 * lane]) = stage_v[i];
-            }
+        // publish a fetched tile: its copies have landed, its key coordinates stored
+        auto finish_tile = [&](int buf) {
             if (video && w == 0) kcoord[buf][lane] = stage_c;
+            wait_copies();
         };
 
         // prologue: tile 0 into buffer 0
         if (gather) load_indices(task.tb, idx_nxt);
-        fetch_tile(task.tb, idx_nxt);
+        fetch_tile(task.tb, idx_nxt, 0);
         if (gather && ntile > 1) load_indices(task.tb + 1, idx_nxt);
-        store_tile(0);
+        finish_tile(0);
         __syncthreads();
 
         // per-lane LDS read offsets (loop-invariant; tile-relative parts are immediates)
-        const int koff = l32 * C::KROW + 16 * hf;  // K rows l32 (+32), chunk 2s + hf
+        int koff[D / 16];  // K rows l32 (+32: same swizzle), chunk 2s + hf
+#pragma unroll
+        for (int s = 0; s < D / 16; ++s) koff[s] = l32 * C::ROWB + 16 * ((2 * s + hf) ^ swz_k<D>(l32));
         const int grp = lane >> 4, jl = lane & 15;
         const int dd_base = 16 * (grp & 1) + 4 * (jl & 3);  // first dim this lane addresses
         const int key_sub = jl >> 2;                         // key within a group of 4
@@ -252,32 +267,34 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4
             const TileRec rec = a.tiles[task.tb + j];
             const bool more = j + 1 < ntile;
             if (more) {
-                fetch_tile(task.tb + j + 1, idx_nxt);
+                fetch_tile(task.tb + j + 1, idx_nxt, cur ^ 1);
                 if (gather && j + 2 < ntile) load_indices(task.tb + j + 2, idx_nxt);
             }
 
             // ---- S^T = K Q^T
-            const unsigned char *kt = ksm[cur] + koff;
+            const unsigned char *kt = ksm[cur];
             f32x16 s0, s1;
             {
-                bf16x8 k0v = *LDS_PTR(bf16x8, kt);
-                bf16x8 k1v = *LDS_PTR(bf16x8, kt + 32 * C::KROW);
+                bf16x8 k0v = *LDS_PTR(bf16x8, kt + koff[0]);
+                bf16x8 k1v = *LDS_PTR(bf16x8, kt + koff[0] + 32 * C::ROWB);
                 s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0v, qreg[0], zero16, 0, 0, 0);
                 s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1v, qreg[0], zero16, 0, 0, 0);
             }
 #pragma unroll
             for (int s = 1; s < D / 16; ++s) {
-                bf16x8 k0v = *LDS_PTR(bf16x8, kt + 32 * s);
-                bf16x8 k1v = *LDS_PTR(bf16x8, kt + 32 * C::KROW + 32 * s);
+                bf16x8 k0v = *LDS_PTR(bf16x8, kt + koff[s]);
+                bf16x8 k1v = *LDS_PTR(bf16x8, kt + koff[s] + 32 * C::ROWB);
                 s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0v, qreg[s], s0, 0, 0, 0);
                 s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1v, qreg[s], s1, 0, 0, 0);
             }
-            // keep LDS reads next to the MFMAs that consume them (bounds register use)
+            // LDS reads run two MFMA pairs ahead of the MFMAs that consume them
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-            for (int s = 0; s < D / 16; ++s) {
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            for (int s = 0; s < D / 16 - 2; ++s) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 
             // ---- exact mask on PARTIAL tiles only
             if (rec.aux & kPartial) {
@@ -397,13 +414,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4
                     oacc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pk[c], oacc[n], 0, 0, 0);
                 }
             }
+            // transposing reads run two MFMAs ahead
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
 #pragma unroll
-            for (int i = 0; i < 4 * (D / 32); ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+            for (int i = 0; i < 4 * (D / 32) - 2; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
             }
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
 
-            if (more) store_tile(cur ^ 1);
+            if (more) finish_tile(cur ^ 1);
             __syncthreads();
         }
     }
