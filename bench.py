@@ -53,31 +53,50 @@ def time_run(w, Q, K, V, steps, warmup):
     o = torch.empty_like(q)
     stream = torch.cuda.current_stream()
 
-    # whole-path steps: plan + forward (plans kept alive until the timed region ends)
-    for _ in range(warmup):
-        p = plan_workload(w)
-        bsa.forward(p, q, k, v, o, stream)
-    torch.cuda.synchronize()
-    plans, ev = [], []
-    plan_s = 0.0
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
+    # whole-path steps: plan + forward for a fresh mask each step. A plan is
+    # retired (its memory returns to the library's pools) once an event shows
+    # that its forward has finished; a ring of RING plans keeps the host
+    # planning ahead of the GPU.
+    RING = 3
+    ring = []
+
+    def step(ev_list=None):
+        if len(ring) >= RING:
+            old_p, old_done = ring.pop(0)
+            old_done.synchronize()
+            old_p.close()
         tp = time.perf_counter()
         p = plan_workload(w)
-        plan_s += time.perf_counter() - tp
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
+        dt = time.perf_counter() - tp
+        if ev_list is not None:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
         bsa.forward(p, q, k, v, o, stream)
-        e1.record(stream)
-        plans.append(p)
-        ev.append((e0, e1))
+        done = torch.cuda.Event()
+        done.record(stream)
+        if ev_list is not None:
+            e1.record(stream)
+            ev_list.append((e0, e1))
+        ring.append((p, done))
+        return dt, p
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = []
+    plan_s = 0.0
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        dt, p = step(ev)
+        plan_s += dt
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     step_ms = (t1 - t0) * 1e3 / steps
     kern_ms_inline = sum(a.elapsed_time(b) for a, b in ev) / steps
-    info = plans[-1].info()
-    del plans
+    info = p.info()
+    for pp, _ in ring:
+        pp.close()
+    ring.clear()
 
     # forward-only launches back to back on a reused plan (kernel throughput)
     p = plan_workload(w)

@@ -62,7 +62,7 @@ class PlanInfo(ctypes.Structure):
 
 class RegimeDesc(ctypes.Structure):
     _fields_ = [("family", ctypes.c_int32), ("tile_q", ctypes.c_int32), ("tile_k", ctypes.c_int32),
-                ("waves", ctypes.c_int32)]
+                ("waves", ctypes.c_int32), ("rows_per_wave", ctypes.c_int32)]
 
 
 class TileRecord(ctypes.Structure):
@@ -226,5 +226,6 @@ def regimes():
     for r in range(L_.bsa_regime_count()):
         d = RegimeDesc()
         _check(L_.bsa_regime_info(r, ctypes.byref(d)))
-        out.append({"family": d.family, "tile_q": d.tile_q, "tile_k": d.tile_k, "waves": d.waves})
+        out.append({"family": d.family, "tile_q": d.tile_q, "tile_k": d.tile_k, "waves": d.waves,
+                    "rows_per_wave": d.rows_per_wave})
     return out

@@ -42,7 +42,7 @@
 #include "plan_format.hpp"
 
 namespace bsa {
-hipError_t launch_forward(const KernelArgs &a, int waves, int d, int dtype, hipStream_t stream);
+hipError_t launch_forward(const KernelArgs &a, int waves, int rb, int d, int dtype, hipStream_t stream);
 }
 
 using namespace bsa;
@@ -88,15 +88,17 @@ extern "C" int32_t bsa_abi_version(void) { return BSA_ABI_VERSION; }
 
 struct Regime {
     int family;  // 0 = contiguous / permuted key tiles, 1 = gathered key lists
-    int tile_q;
-    int waves;
+    int tile_q;  // = 32 * waves * rb
+    int waves;   // wavefronts per workgroup
+    int rb;      // 32-row query blocks per wave
 };
 
 static const Regime kRegimes[] = {
-    {0, 128, 4},  // 0: 128 x 64 tiles
-    {0, 64, 2},   // 1: 64 x 64 tiles
-    {1, 64, 2},   // 2: 64-query gather tiles
-    {1, 128, 4},  // 3: 128-query gather tiles
+    {0, 128, 4, 1},  // 0: 128 x 64 tiles, 4 waves of 32 rows
+    {0, 64, 2, 1},   // 1: 64 x 64 tiles, 2 waves of 32 rows
+    {1, 64, 2, 1},   // 2: 64-query gather tiles
+    {1, 128, 4, 1},  // 3: 128-query gather tiles
+    {0, 256, 8, 1},  // 4: 256 x 64 tiles, 8 waves of 32 rows
 };
 static const int kNumRegimes = (int)(sizeof kRegimes / sizeof kRegimes[0]);
 
@@ -109,6 +111,7 @@ extern "C" int32_t bsa_regime_info(int32_t r, bsa_regime_desc_t *out)
     out->tile_q = kRegimes[r].tile_q;
     out->tile_k = kTileK;
     out->waves = kRegimes[r].waves;
+    out->rows_per_wave = 32 * kRegimes[r].rb;
     return BSA_OK;
 }
 
@@ -1154,7 +1157,8 @@ extern "C" int32_t bsa_forward(bsa_plan_t p, const void *Q, const void *K, const
     if (cur != p->device) (void)hipSetDevice(p->device);
     // the launch is ordered after the plan's upload (a no-op once it is done)
     hipError_t e = hipStreamWaitEvent((hipStream_t)stream, p->uploaded, 0);
-    if (e == hipSuccess) e = launch_forward(a, kRegimes[p->regime].waves, p->d, p->dtype, (hipStream_t)stream);
+    if (e == hipSuccess)
+        e = launch_forward(a, kRegimes[p->regime].waves, kRegimes[p->regime].rb, p->d, p->dtype, (hipStream_t)stream);
     if (cur != p->device) (void)hipSetDevice(cur);
     if (e != hipSuccess) return fail(BSA_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
     return BSA_OK;

@@ -43,6 +43,12 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+template <int V>
+struct IntC {
+    static constexpr int value = V;
+};
 
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T *)(p))
 
@@ -53,9 +59,9 @@ constexpr float kSlack = 8.0f;  // log2 headroom before the softmax reference mo
 // (radius <= 256, coordinates < 512), so no video predicate keeps it.
 constexpr int kNoKey = 0x7FFF7FFF;
 
-template <int NW, int D>
+template <int NW, int RB, int D>
 struct Cfg {
-    static constexpr int BQ = 32 * NW;
+    static constexpr int BQ = 32 * NW * RB;            // query rows per task
     static constexpr int BK = kTileK;
     static constexpr int ROWB = D * 2;                 // bytes per bf16 row
     static constexpr int TILEB = BK * ROWB;            // bytes per K or V tile
@@ -92,6 +98,19 @@ __device__ __forceinline__ void copy16_to_lds(const void *g, uint32_t lds)
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
 #pragma clang diagnostic pop
 }
+// The same copy with a wave-uniform base address in SGPRs and a 32-bit
+// per-lane byte offset (no per-lane 64-bit address arithmetic).
+__device__ __forceinline__ void copy16_to_lds_s(const void *base, uint32_t off, uint32_t lds)
+{
+    // the base is wave-uniform; make that explicit so it lives in an SGPR pair
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    const uint64_t sb = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(sb), "s"(lds) : "memory", "m0");
+#pragma clang diagnostic pop
+}
 __device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 __device__ __forceinline__ float swap_halves_max(float x)
@@ -126,10 +145,13 @@ __device__ __forceinline__ int fdiv(int n, uint32_t m, int s)
     return (int)((__umulhi((unsigned)n, m) + (unsigned)n) >> s);
 }
 
-template <int NW, int D>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4 ? 2 : 1, 2))) void bsa_fwd_bf16(KernelArgs a)
+// Kernel: NW waves per workgroup, each wave owns RB consecutive blocks of 32
+// query rows. Every K operand read from LDS feeds RB score MFMAs and every V
+// operand read feeds RB output MFMAs, so LDS bytes per MFMA fall as 1/RB.
+template <int NW, int RB, int D>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1 && NW >= 4 ? 2 : 1, RB == 1 ? 2 : 1))) void bsa_fwd_bf16(KernelArgs a)
 {
-    using C = Cfg<NW, D>;
+    using C = Cfg<NW, RB, D>;
     __shared__ __attribute__((aligned(1024))) unsigned char ksm[2][C::TILEB];  // [buffer] swizzled K tile
     __shared__ __attribute__((aligned(1024))) unsigned char vsm[2][C::TILEB];  // [buffer] swizzled V tile
     __shared__ __attribute__((aligned(16))) int kcoord[2][C::BK];
@@ -158,36 +180,52 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4
         return (j - p * a.T) * a.HW + p;
     };
 
-    // ---- this lane's query row (logical position q, frame-major token qtok)
-    const int q = task.q0 + 32 * w + l32;
-    const bool qvalid = q < L;
-    const int qtok = token(qvalid ? q : L - 1);
+    // ---- this lane's query rows: one per 32-row block rb (logical q, frame-major token qtok)
+    int q[RB], qtok[RB];
+    bool qvalid[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        q[rb] = task.q0 + 32 * (w * RB + rb) + l32;
+        qvalid[rb] = q[rb] < L;
+        qtok[rb] = token(qvalid[rb] ? q[rb] : L - 1);
+    }
 
     const int ntile = task.te - task.tb;
     const bool gather = a.mode == kModeGather;
     const bool video = a.mode == kModeVideo;
 
-    f32x16 oacc[D / 32];
+    f32x16 oacc[RB][D / 32];
 #pragma unroll
-    for (int n = 0; n < D / 32; ++n)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[n][r] = 0.f;
-    float m_ref = -INFINITY, l_run = 0.f;
+        for (int n = 0; n < D / 32; ++n)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[rb][n][r] = 0.f;
+    float m_ref[RB], l_run[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) { m_ref[rb] = -INFINITY; l_run[rb] = 0.f; }
 
     if (ntile > 0) {
-        bf16x8 qreg[D / 16];
+        bf16x8 qreg[RB][D / 16];
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) qreg[s] = load_bf16x8(Qh + (size_t)qtok * D + 16 * s + 8 * hf);
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int s = 0; s < D / 16; ++s) qreg[rb][s] = load_bf16x8(Qh + (size_t)qtok[rb] * D + 16 * s + 8 * hf);
 
         // query coordinates for the video predicates: frame (spatial) or the
         // packed window origin ((y - r) << 16) + (x - r) (temporal)
-        int qt = 0;
-        unsigned qwin = 0;
-        if (video) {
-            qt = fdiv(qtok, a.magic_HW, a.shift_HW);
-            const int p = qtok - qt * a.HW;
-            const int y = fdiv(p, a.magic_W, a.shift_W), x = p - y * a.W;
-            qwin = ((unsigned)(y - a.radius) << 16) + (unsigned)(x - a.radius);
+        int qt[RB];
+        unsigned qwin[RB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            qt[rb] = 0;
+            qwin[rb] = 0;
+            if (video) {
+                qt[rb] = fdiv(qtok[rb], a.magic_HW, a.shift_HW);
+                const int p = qtok[rb] - qt[rb] * a.HW;
+                const int y = fdiv(p, a.magic_W, a.shift_W), x = p - y * a.W;
+                qwin[rb] = ((unsigned)(y - a.radius) << 16) + (unsigned)(x - a.radius);
+            }
         }
         const unsigned win2 = 2u * (unsigned)a.radius;
 
@@ -208,9 +246,27 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4
         // global -> LDS copies of a tile (in flight while the previous tile is
         // computed); the video key coordinates go through a register
         int stage_c = kNoKey;
+        // per-lane byte offsets of the copied chunks within a contiguous tile
+        uint32_t kgoff[C::INSTS], vgoff[C::INSTS];
+#pragma unroll
+        for (int i = 0; i < C::INSTS; ++i) {
+            const int slot = (w * C::INSTS + i) * C::RPI + lane / C::CHUNKS;
+            kgoff[i] = (uint32_t)(slot * C::ROWB + 16 * (pos ^ swz_k<D>(slot)));
+            vgoff[i] = (uint32_t)(slot * C::ROWB + 16 * (pos ^ swz_v<D>(slot & 3)));
+        }
         auto fetch_tile = [&](int rec_i, const int *idx, int buf) {
             const TileRec r = a.tiles[__builtin_amdgcn_readfirstlane(rec_i)];
             const uint32_t kl = (uint32_t)(uintptr_t)&ksm[buf][0], vl = (uint32_t)(uintptr_t)&vsm[buf][0];
+            if (!tm && !gather && r.k0 + C::BK <= L) {
+                // 64 consecutive rows: scalar base + loop-invariant lane offsets
+                const __bf16 *kb = Kh + (size_t)r.k0 * D, *vb = Vh + (size_t)r.k0 * D;
+#pragma unroll
+                for (int i = 0; i < C::INSTS; ++i) {
+                    const uint32_t off = (uint32_t)((w * C::INSTS + i) * 1024);
+                    copy16_to_lds_s(kb, kgoff[i], __builtin_amdgcn_readfirstlane(kl + off));
+                    copy16_to_lds_s(vb, vgoff[i], __builtin_amdgcn_readfirstlane(vl + off));
+                }
+            } else {
 #pragma unroll
             for (int i = 0; i < C::INSTS; ++i) {
                 const int slot = (w * C::INSTS + i) * C::RPI + lane / C::CHUNKS;
@@ -219,6 +275,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4
                 const uint32_t off = (uint32_t)((w * C::INSTS + i) * 1024);
                 copy16_to_lds(Kh + (size_t)ktok * D + 8 * (pos ^ swz_k<D>(slot)), __builtin_amdgcn_readfirstlane(kl + off));
                 copy16_to_lds(Vh + (size_t)ktok * D + 8 * (pos ^ swz_v<D>(slot & 3)), __builtin_amdgcn_readfirstlane(vl + off));
+            }
             }
             if (video && w == 0) {
                 // per key slot: frame (spatial) or packed (y << 16) | x
@@ -262,39 +319,39 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4
             voff[n] = (4 * hf + key_sub) * C::ROWB + 16 * (((32 * n + dd_base) >> 3) ^ sv) + 2 * (dd_base & 7);
         const f32x16 zero16 = {};
 
-        for (int j = 0; j < ntile; ++j) {
-            const int cur = j & 1;
-            const TileRec rec = a.tiles[task.tb + j];
+        // one key tile; the LDS buffer index is a compile-time constant (the loop
+        // below is unrolled by two), so every LDS operand address is a
+        // loop-invariant register plus an immediate offset
+        auto tile_step = [&](const int j, auto cur_c) {
+            constexpr int cur = decltype(cur_c)::value;
+            const TileRec rec = a.tiles[__builtin_amdgcn_readfirstlane(task.tb + j)];
             const bool more = j + 1 < ntile;
             if (more) {
                 fetch_tile(task.tb + j + 1, idx_nxt, cur ^ 1);
                 if (gather && j + 2 < ntile) load_indices(task.tb + j + 2, idx_nxt);
             }
 
-            // ---- S^T = K Q^T
+            // ---- S^T = K Q^T: s0 = keys 0..31, s1 = keys 32..63 of each row block
             const unsigned char *kt = ksm[cur];
-            f32x16 s0, s1;
-            {
-                bf16x8 k0v = *LDS_PTR(bf16x8, kt + koff[0]);
-                bf16x8 k1v = *LDS_PTR(bf16x8, kt + koff[0] + 32 * C::ROWB);
-                s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0v, qreg[0], zero16, 0, 0, 0);
-                s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1v, qreg[0], zero16, 0, 0, 0);
-            }
+            f32x16 s0[RB], s1[RB];
 #pragma unroll
-            for (int s = 1; s < D / 16; ++s) {
-                bf16x8 k0v = *LDS_PTR(bf16x8, kt + koff[s]);
-                bf16x8 k1v = *LDS_PTR(bf16x8, kt + koff[s] + 32 * C::ROWB);
-                s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0v, qreg[s], s0, 0, 0, 0);
-                s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1v, qreg[s], s1, 0, 0, 0);
+            for (int s = 0; s < D / 16; ++s) {
+                const bf16x8 k0v = *LDS_PTR(bf16x8, kt + koff[s]);
+                const bf16x8 k1v = *LDS_PTR(bf16x8, kt + koff[s] + 32 * C::ROWB);
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    s0[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0v, qreg[rb][s], s == 0 ? zero16 : s0[rb], 0, 0, 0);
+                    s1[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1v, qreg[rb][s], s == 0 ? zero16 : s1[rb], 0, 0, 0);
+                }
             }
-            // LDS reads run two MFMA pairs ahead of the MFMAs that consume them
+            // LDS reads run two read pairs ahead of the MFMAs that consume them
             __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
             for (int s = 0; s < D / 16 - 2; ++s) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 2 * RB, 0);
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4 * RB, 0);
 
             // ---- exact mask on PARTIAL tiles only
             if (rec.aux & kPartial) {
@@ -306,10 +363,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4
                             const i32x4 c0 = *LDS_PTR(i32x4, kc + 8 * g + 4 * hf);
                             const i32x4 c1 = *LDS_PTR(i32x4, kc + 32 + 8 * g + 4 * hf);
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                s0[4 * g + e] = (c0[e] == qt || c0[e] == a.anchor) ? s0[4 * g + e] : -INFINITY;
-                                s1[4 * g + e] = (c1[e] == qt || c1[e] == a.anchor) ? s1[4 * g + e] : -INFINITY;
-                            }
+                            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) {
+                                    s0[rb][4 * g + e] = (c0[e] == qt[rb] || c0[e] == a.anchor) ? s0[rb][4 * g + e] : -INFINITY;
+                                    s1[rb][4 * g + e] = (c1[e] == qt[rb] || c1[e] == a.anchor) ? s1[rb][4 * g + e] : -INFINITY;
+                                }
                         }
                     } else if (pat == 2) {  // temporal: |dy| <= r and |dx| <= r, any frame
 #pragma unroll
@@ -317,11 +376,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4
                             const i32x4 c0 = *LDS_PTR(i32x4, kc + 8 * g + 4 * hf);
                             const i32x4 c1 = *LDS_PTR(i32x4, kc + 32 + 8 * g + 4 * hf);
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                const unsigned d0 = (unsigned)c0[e] - qwin, d1 = (unsigned)c1[e] - qwin;
-                                s0[4 * g + e] = max(d0 & 0xffffu, d0 >> 16) <= win2 ? s0[4 * g + e] : -INFINITY;
-                                s1[4 * g + e] = max(d1 & 0xffffu, d1 >> 16) <= win2 ? s1[4 * g + e] : -INFINITY;
-                            }
+                            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) {
+                                    const unsigned d0 = (unsigned)c0[e] - qwin[rb], d1 = (unsigned)c1[e] - qwin[rb];
+                                    s0[rb][4 * g + e] = max(d0 & 0xffffu, d0 >> 16) <= win2 ? s0[rb][4 * g + e] : -INFINITY;
+                                    s1[rb][4 * g + e] = max(d1 & 0xffffu, d1 >> 16) <= win2 ? s1[rb][4 * g + e] : -INFINITY;
+                                }
                         }
                     } else {  // dense: only slots past the sequence end
 #pragma unroll
@@ -329,77 +390,80 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4
                             const i32x4 c0 = *LDS_PTR(i32x4, kc + 8 * g + 4 * hf);
                             const i32x4 c1 = *LDS_PTR(i32x4, kc + 32 + 8 * g + 4 * hf);
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                s0[4 * g + e] = c0[e] != kNoKey ? s0[4 * g + e] : -INFINITY;
-                                s1[4 * g + e] = c1[e] != kNoKey ? s1[4 * g + e] : -INFINITY;
-                            }
+                            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) {
+                                    s0[rb][4 * g + e] = c0[e] != kNoKey ? s0[rb][4 * g + e] : -INFINITY;
+                                    s1[rb][4 * g + e] = c1[e] != kNoKey ? s1[rb][4 * g + e] : -INFINITY;
+                                }
                         }
                     }
                 } else {
-                    // keep bits of key slots 0..31 (lo) and 32..63 (hi) for this lane's query
-                    uint32_t lo, hi;
-                    int kmax;  // slots >= kmax are not kept (sequence end / list end)
-                    if (a.mode == kModeBlock) {
-                        const int sq = (q - task.q0) >> a.bq_shift;
-                        const uint32_t rowbits = rec.aux >> (sq * a.nsk);
-                        lo = (rowbits & 1u) ? ~0u : 0u;
-                        hi = ((rowbits >> (a.nsk - 1)) & 1u) ? ~0u : 0u;
-                        kmax = L - rec.k0;
-                    } else {
-                        lo = hi = ~0u;
-                        kmax = (int)(rec.aux & kAuxMask);
-                    }
+                    // keep bits of key slots 0..31 (lo) and 32..63 (hi) for each row block
+                    const int kmax = a.mode == kModeBlock ? L - rec.k0 : (int)(rec.aux & kAuxMask);
+                    uint32_t vlo = ~0u, vhi = ~0u;  // slots >= kmax: past the sequence / list end
                     if (kmax < 64) {
-                        lo &= kmax >= 32 ? ~0u : ((1u << max(kmax, 0)) - 1u);
-                        hi &= kmax <= 32 ? 0u : ((1u << (kmax - 32)) - 1u);
+                        vlo = kmax >= 32 ? ~0u : ((1u << max(kmax, 0)) - 1u);
+                        vhi = kmax <= 32 ? 0u : ((1u << (kmax - 32)) - 1u);
                     }
-                    lo >>= 4 * hf;
-                    hi >>= 4 * hf;
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int bit = 8 * (r / 4) + (r % 4);
-                        s0[r] = ((lo >> bit) & 1u) ? s0[r] : -INFINITY;
-                        s1[r] = ((hi >> bit) & 1u) ? s1[r] : -INFINITY;
+                    for (int rb = 0; rb < RB; ++rb) {
+                        uint32_t lo = vlo, hi = vhi;
+                        if (a.mode == kModeBlock) {
+                            const int sq = (q[rb] - task.q0) >> a.bq_shift;
+                            const uint32_t rowbits = rec.aux >> (sq * a.nsk);
+                            lo &= (rowbits & 1u) ? ~0u : 0u;
+                            hi &= ((rowbits >> (a.nsk - 1)) & 1u) ? ~0u : 0u;
+                        }
+                        lo >>= 4 * hf;
+                        hi >>= 4 * hf;
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int bit = 8 * (r / 4) + (r % 4);
+                            s0[rb][r] = ((lo >> bit) & 1u) ? s0[rb][r] : -INFINITY;
+                            s1[rb][r] = ((hi >> bit) & 1u) ? s1[rb][r] : -INFINITY;
+                        }
                     }
                 }
             }
 
-            // ---- online softmax (reference max moves only by more than kSlack)
-            float mx = fmaxf(s0[0], s1[0]);
+            // ---- online softmax per row block (reference max moves only by more than kSlack)
+            u32x4 pk[RB][4];  // bf16 pairs, one cvt_pk each
 #pragma unroll
-            for (int r = 1; r < 16; ++r) mx = max3f(mx, s0[r], s1[r]);
-            mx = swap_halves_max(mx) * a.scale_log2;
-            const bool need = mx > m_ref + kSlack;
-            if (__builtin_amdgcn_ballot_w64(need)) {
-                // lanes that keep their reference (also those still at -inf) scale by exactly 1
-                const float alpha = need ? __builtin_amdgcn_exp2f(m_ref - mx) : 1.0f;
-                m_ref = need ? mx : m_ref;
-                l_run *= alpha;
+            for (int rb = 0; rb < RB; ++rb) {
+                float mx = fmaxf(s0[rb][0], s1[rb][0]);
 #pragma unroll
-                for (int n = 0; n < D / 32; ++n)
+                for (int r = 1; r < 16; ++r) mx = max3f(mx, s0[rb][r], s1[rb][r]);
+                mx = swap_halves_max(mx) * a.scale_log2;
+                const bool need = mx > m_ref[rb] + kSlack;
+                if (__builtin_amdgcn_ballot_w64(need)) {
+                    // lanes that keep their reference (also those still at -inf) scale by exactly 1
+                    const float alpha = need ? __builtin_amdgcn_exp2f(m_ref[rb] - mx) : 1.0f;
+                    m_ref[rb] = need ? mx : m_ref[rb];
+                    l_run[rb] *= alpha;
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[n][r] *= alpha;
-            }
-            const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
-
-            bf16x8 pk[4];
-            const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+                    for (int n = 0; n < D / 32; ++n)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
+                        for (int r = 0; r < 16; ++r) oacc[rb][n][r] *= alpha;
+                }
+                const float m_use = m_ref[rb] == -INFINITY ? 0.f : m_ref[rb];
+                const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    const float x0 = (c < 2 ? s0 : s1)[8 * (c % 2) + e];
-                    const float x1 = (c < 2 ? s0 : s1)[8 * (c % 2) + e + 1];
-                    const float p0 = __builtin_amdgcn_exp2f(fmaf(x0, a.scale_log2, -m_use));
-                    const float p1 = __builtin_amdgcn_exp2f(fmaf(x1, a.scale_log2, -m_use));
-                    const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
-                    l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_run, false);
-                    pk[c][e] = pp[0];
-                    pk[c][e + 1] = pp[1];
+                for (int c = 0; c < 4; ++c) {
+#pragma unroll
+                    for (int e = 0; e < 8; e += 2) {
+                        const float x0 = (c < 2 ? s0[rb] : s1[rb])[8 * (c % 2) + e];
+                        const float x1 = (c < 2 ? s0[rb] : s1[rb])[8 * (c % 2) + e + 1];
+                        const float p0 = __builtin_amdgcn_exp2f(fmaf(x0, a.scale_log2, -m_use));
+                        const float p1 = __builtin_amdgcn_exp2f(fmaf(x1, a.scale_log2, -m_use));
+                        const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
+                        l_run[rb] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_run[rb], false);
+                        pk[rb][c][e / 2] = __builtin_bit_cast(unsigned, pp);
+                    }
                 }
             }
 
-            // ---- O^T += V^T P^T
+            // ---- O^T += V^T P^T (one V operand read feeds RB MFMAs)
             const unsigned char *vt = vsm[cur];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
@@ -411,54 +475,69 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW == 4
                     const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, pb));
                     const bf16x4 a4 = __builtin_bit_cast(bf16x4, va), b4 = __builtin_bit_cast(bf16x4, vb);
                     const bf16x8 vop = {a4[0], a4[1], a4[2], a4[3], b4[0], b4[1], b4[2], b4[3]};
-                    oacc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, pk[c], oacc[n], 0, 0, 0);
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb)
+                        oacc[rb][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, __builtin_bit_cast(bf16x8, pk[rb][c]), oacc[rb][n], 0, 0, 0);
                 }
             }
-            // transposing reads run two MFMAs ahead
+            // transposing reads run two operand reads ahead
             __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
 #pragma unroll
             for (int i = 0; i < 4 * (D / 32) - 2; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+                __builtin_amdgcn_sched_group_barrier(0x008, RB, 1);
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2 * RB, 1);
 
             if (more) finish_tile(cur ^ 1);
             __syncthreads();
+        };
+        int j = 0;
+        for (; j + 1 < ntile; j += 2) {
+            tile_step(j, IntC<0>{});
+            tile_step(j + 1, IntC<1>{});
         }
+        if (j < ntile) tile_step(j, IntC<0>{});
     }
 
     // ---- epilogue: O = O / l (0 for rows without a kept key), bf16 RNE
-    const float l_tot = swap_halves_sum(l_run);
-    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-    if (qvalid) {
-        __bf16 *orow = Oh + (size_t)qtok * D;
 #pragma unroll
-        for (int n = 0; n < D / 32; ++n)
+    for (int rb = 0; rb < RB; ++rb) {
+        const float l_tot = swap_halves_sum(l_run[rb]);
+        const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+        if (qvalid[rb]) {
+            __bf16 *orow = Oh + (size_t)qtok[rb] * D;
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int dd = 32 * n + 8 * rr + 4 * hf;
-                const bf16x4 o4 = {(__bf16)(oacc[n][4 * rr] * inv), (__bf16)(oacc[n][4 * rr + 1] * inv),
-                                   (__bf16)(oacc[n][4 * rr + 2] * inv), (__bf16)(oacc[n][4 * rr + 3] * inv)};
-                *(bf16x4 *)(orow + dd) = o4;
-            }
+            for (int n = 0; n < D / 32; ++n)
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int dd = 32 * n + 8 * rr + 4 * hf;
+                    const bf16x4 o4 = {(__bf16)(oacc[rb][n][4 * rr] * inv), (__bf16)(oacc[rb][n][4 * rr + 1] * inv),
+                                       (__bf16)(oacc[rb][n][4 * rr + 2] * inv), (__bf16)(oacc[rb][n][4 * rr + 3] * inv)};
+                    *(bf16x4 *)(orow + dd) = o4;
+                }
+        }
     }
 }
 
-template <int NW, int D>
+template <int NW, int RB, int D>
 static hipError_t launch(const KernelArgs &a, hipStream_t stream)
 {
-    hipLaunchKernelGGL((bsa_fwd_bf16<NW, D>), dim3(a.ntasks), dim3(NW * 64), 0, stream, a);
+    hipLaunchKernelGGL((bsa_fwd_bf16<NW, RB, D>), dim3(a.ntasks), dim3(NW * 64), 0, stream, a);
     return hipGetLastError();
 }
 
-hipError_t launch_forward(const KernelArgs &a, int waves, int d, int dtype, hipStream_t stream)
+hipError_t launch_forward(const KernelArgs &a, int waves, int rb, int d, int dtype, hipStream_t stream)
 {
     if (dtype != 0) return hipErrorInvalidValue;
-    if (waves == 4 && d == 128) return launch<4, 128>(a, stream);
-    if (waves == 4 && d == 64) return launch<4, 64>(a, stream);
-    if (waves == 2 && d == 128) return launch<2, 128>(a, stream);
-    if (waves == 2 && d == 64) return launch<2, 64>(a, stream);
+    if (rb == 1) {
+        if (waves == 8 && d == 128) return launch<8, 1, 128>(a, stream);
+        if (waves == 8 && d == 64) return launch<8, 1, 64>(a, stream);
+        if (waves == 4 && d == 128) return launch<4, 1, 128>(a, stream);
+        if (waves == 4 && d == 64) return launch<4, 1, 64>(a, stream);
+        if (waves == 2 && d == 128) return launch<2, 1, 128>(a, stream);
+        if (waves == 2 && d == 64) return launch<2, 1, 64>(a, stream);
+    }
     return hipErrorInvalidValue;
 }
 

@@ -141,6 +141,7 @@ typedef struct {
     int32_t family;                /* 0 = contiguous/permuted tiles, 1 = gather    */
     int32_t tile_q, tile_k;
     int32_t waves;                 /* wavefronts per workgroup                     */
+    int32_t rows_per_wave;         /* query rows each wavefront owns (32 or 64)    */
 } bsa_regime_desc_t;
 
 /* One physical tile of a plan, as computed by the device (test hook for
