@@ -233,6 +233,7 @@ def main():
                    "heads": "12 spatial (same frame + frame 0), 12 temporal (|dy|,|dx| <= 2, all frames)",
                    "kept_pairs": P, "step": "bsa_plan + bsa_forward"},
         "fwd_ms": round(B["fwd_ms"], 4),
+        "fwd_ms_in_steps": round(B["fwd_ms_inline"], 4),
         "plan_ms": round(B["plan_ms"], 4),
         "effective_tflops_step": round(B["effective_tflops_step"], 2),
         "effective_tflops_fwd": round(B["effective_tflops_fwd"], 2),

@@ -821,14 +821,14 @@ size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 // One task per (batch, head, query tile) -- also for query tiles without any
 // key tile, so that every output row is written. The heads' outputs are
 // copied in parallel into the plan image, then ordered for the device:
-//  - XCD order (default): workgroup i of a launch runs on XCD i % X (X = 8 on
+//  - XCD order (BSA_TASK_ORDER=xcd): workgroup i of a launch runs on XCD i % X (X = 8 on
 //    MI355X), each XCD with its own L2. Tasks in (head, query tile) order --
 //    neighbouring query tiles share most of their key tiles -- are cut into X
 //    contiguous segments of equal tile count (plus one per task), and slot
 //    i*X + x of the launch takes task i of segment x, so each XCD streams one
 //    contiguous piece of the key space through its L2. Segments shorter than
 //    the longest are padded with no-op tasks (bh = -1).
-//  - LPT order: longest task first (a stable counting sort on the tile
+//  - LPT order (default): longest task first (a stable counting sort on the tile
 //    count), so the tail of the grid holds the cheapest work.
 static int xcd_count()
 {
