@@ -43,6 +43,7 @@
 
 namespace bsa {
 hipError_t launch_forward(const KernelArgs &a, int waves, int rb, int d, int dtype, hipStream_t stream);
+hipError_t launch_forward_f32(const KernelArgs &a, int waves, int d, hipStream_t stream);
 }
 
 using namespace bsa;
@@ -601,7 +602,6 @@ static int32_t validate(const bsa_mask_desc_t *m, int32_t B, int32_t H, int64_t 
         ;  // sizes are addressed with 64-bit arithmetic in the kernel; nothing to check here
     if (d != 64 && d != 128) return fail(BSA_ERR_UNSUPPORTED, "head dim d = %d (supported: 64, 128)", d);
     if (o.dtype != BSA_DTYPE_BF16 && o.dtype != BSA_DTYPE_F32) return fail(BSA_ERR_INVALID_ARGUMENT, "dtype %d", o.dtype);
-    if (o.dtype == BSA_DTYPE_F32) return fail(BSA_ERR_UNSUPPORTED, "fp32 plans are not built in this version");
     const bool has_geo = o.T || o.Hg || o.Wg;
     if (has_geo) {
         if (o.T < 1 || o.Hg < 1 || o.Wg < 1 || (int64_t)o.T * o.Hg * o.Wg != L)
@@ -1157,8 +1157,11 @@ extern "C" int32_t bsa_forward(bsa_plan_t p, const void *Q, const void *K, const
     if (cur != p->device) (void)hipSetDevice(p->device);
     // the launch is ordered after the plan's upload (a no-op once it is done)
     hipError_t e = hipStreamWaitEvent((hipStream_t)stream, p->uploaded, 0);
-    if (e == hipSuccess)
-        e = launch_forward(a, kRegimes[p->regime].waves, kRegimes[p->regime].rb, p->d, p->dtype, (hipStream_t)stream);
+    if (e == hipSuccess) {
+        const Regime &R = kRegimes[p->regime];
+        e = p->dtype == BSA_DTYPE_F32 ? launch_forward_f32(a, R.waves, p->d, (hipStream_t)stream)
+                                      : launch_forward(a, R.waves, R.rb, p->d, p->dtype, (hipStream_t)stream);
+    }
     if (cur != p->device) (void)hipSetDevice(cur);
     if (e != hipSuccess) return fail(BSA_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
     return BSA_OK;

@@ -33,31 +33,20 @@
 
 #include <cstdint>
 
-#include "plan_format.hpp"
+#include "kernel_common.hpp"
 
 namespace bsa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 template <int V>
 struct IntC {
     static constexpr int value = V;
 };
-
-#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T *)(p))
-
-constexpr float kSlack = 8.0f;  // log2 headroom before the softmax reference moves
-
-// Key-coordinate word of a slot past the sequence end: no frame equals it, and
-// (kNoKey - window origin) has both 16-bit halves far above any 2*radius
-// (radius <= 256, coordinates < 512), so no video predicate keeps it.
-constexpr int kNoKey = 0x7FFF7FFF;
 
 template <int NW, int RB, int D>
 struct Cfg {
@@ -113,36 +102,10 @@ __device__ __forceinline__ void copy16_to_lds_s(const void *base, uint32_t off, 
 }
 __device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-__device__ __forceinline__ float swap_halves_max(float x)
-{
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float swap_halves_sum(float x)
-{
-    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// three-input maximum on one VALU op (scores are never NaN, so no quieting of
-// the inputs is needed)
-__device__ __forceinline__ float max3f(float a, float b, float c)
-{
-    float r;
-    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-    return r;
-}
-
 __device__ __forceinline__ bf16x8 load_bf16x8(const __bf16 *p)
 {
     i32x4 v = *(const i32x4 *)p;
     return __builtin_bit_cast(bf16x8, v);
-}
-
-// n / d for 0 <= n < 2^31 with the host-computed multiplier (round-up method)
-__device__ __forceinline__ int fdiv(int n, uint32_t m, int s)
-{
-    return (int)((__umulhi((unsigned)n, m) + (unsigned)n) >> s);
 }
 
 // Kernel: NW waves per workgroup, each wave owns RB consecutive blocks of 32
@@ -152,9 +115,9 @@ template <int NW, int RB, int D>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1 && NW >= 4 ? 2 : 1, RB == 1 ? 2 : 1))) void bsa_fwd_bf16(KernelArgs a)
 {
     using C = Cfg<NW, RB, D>;
+    __shared__ __attribute__((aligned(16))) int kcoord[2][C::BK];  // [buffer] video key coordinates
     __shared__ __attribute__((aligned(1024))) unsigned char ksm[2][C::TILEB];  // [buffer] swizzled K tile
     __shared__ __attribute__((aligned(1024))) unsigned char vsm[2][C::TILEB];  // [buffer] swizzled V tile
-    __shared__ __attribute__((aligned(16))) int kcoord[2][C::BK];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
@@ -173,12 +136,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1
     const __bf16 *Vh = (const __bf16 *)a.V + head_off;
     __bf16 *Oh = (__bf16 *)a.O + head_off;
 
-    // logical position of the head -> frame-major token
-    auto token = [&](int j) -> int {
-        if (!tm) return j;
-        const int p = fdiv(j, a.magic_T, a.shift_T);
-        return (j - p * a.T) * a.HW + p;
-    };
+    auto token = [&](int j) -> int { return head_token(j, tm, a); };
 
     // ---- this lane's query rows: one per 32-row block rb (logical q, frame-major token qtok)
     int q[RB], qtok[RB];
@@ -220,14 +178,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1
         for (int rb = 0; rb < RB; ++rb) {
             qt[rb] = 0;
             qwin[rb] = 0;
-            if (video) {
-                qt[rb] = fdiv(qtok[rb], a.magic_HW, a.shift_HW);
-                const int p = qtok[rb] - qt[rb] * a.HW;
-                const int y = fdiv(p, a.magic_W, a.shift_W), x = p - y * a.W;
-                qwin[rb] = ((unsigned)(y - a.radius) << 16) + (unsigned)(x - a.radius);
-            }
+            if (video) video_query_coords(qtok[rb], a, qt[rb], qwin[rb]);
         }
-        const unsigned win2 = 2u * (unsigned)a.radius;
 
         // rows this lane copies for each tile: slot = (w*INSTS + i)*RPI + lane/CHUNKS
         const int pos = lane % C::CHUNKS;
@@ -280,16 +232,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1
             if (video && w == 0) {
                 // per key slot: frame (spatial) or packed (y << 16) | x
                 // (temporal); kNoKey past the sequence end
-                const int kp = r.k0 + lane;
-                int v = kNoKey;
-                if (kp < L) {
-                    const int kt = token(kp);
-                    const int t = fdiv(kt, a.magic_HW, a.shift_HW);
-                    const int p = kt - t * a.HW;
-                    const int y = fdiv(p, a.magic_W, a.shift_W), x = p - y * a.W;
-                    v = pat == 1 ? t : (pat == 2 ? ((y << 16) | x) : 0);
-                }
-                stage_c = v;
+                stage_c = video_key_word(r.k0 + lane, tm, pat, a);
             }
         };
         // publish a fetched tile: its copies have landed, its key coordinates stored
@@ -354,78 +297,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1
             __builtin_amdgcn_sched_group_barrier(0x008, 4 * RB, 0);
 
             // ---- exact mask on PARTIAL tiles only
-            if (rec.aux & kPartial) {
-                if (video) {
-                    const int *kc = kcoord[cur];
-                    if (pat == 1) {  // spatial: key in the query's frame or in the anchor frame
-#pragma unroll
-                        for (int g = 0; g < 4; ++g) {
-                            const i32x4 c0 = *LDS_PTR(i32x4, kc + 8 * g + 4 * hf);
-                            const i32x4 c1 = *LDS_PTR(i32x4, kc + 32 + 8 * g + 4 * hf);
-#pragma unroll
-                            for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-                                for (int e = 0; e < 4; ++e) {
-                                    s0[rb][4 * g + e] = (c0[e] == qt[rb] || c0[e] == a.anchor) ? s0[rb][4 * g + e] : -INFINITY;
-                                    s1[rb][4 * g + e] = (c1[e] == qt[rb] || c1[e] == a.anchor) ? s1[rb][4 * g + e] : -INFINITY;
-                                }
-                        }
-                    } else if (pat == 2) {  // temporal: |dy| <= r and |dx| <= r, any frame
-#pragma unroll
-                        for (int g = 0; g < 4; ++g) {
-                            const i32x4 c0 = *LDS_PTR(i32x4, kc + 8 * g + 4 * hf);
-                            const i32x4 c1 = *LDS_PTR(i32x4, kc + 32 + 8 * g + 4 * hf);
-#pragma unroll
-                            for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-                                for (int e = 0; e < 4; ++e) {
-                                    const unsigned d0 = (unsigned)c0[e] - qwin[rb], d1 = (unsigned)c1[e] - qwin[rb];
-                                    s0[rb][4 * g + e] = max(d0 & 0xffffu, d0 >> 16) <= win2 ? s0[rb][4 * g + e] : -INFINITY;
-                                    s1[rb][4 * g + e] = max(d1 & 0xffffu, d1 >> 16) <= win2 ? s1[rb][4 * g + e] : -INFINITY;
-                                }
-                        }
-                    } else {  // dense: only slots past the sequence end
-#pragma unroll
-                        for (int g = 0; g < 4; ++g) {
-                            const i32x4 c0 = *LDS_PTR(i32x4, kc + 8 * g + 4 * hf);
-                            const i32x4 c1 = *LDS_PTR(i32x4, kc + 32 + 8 * g + 4 * hf);
-#pragma unroll
-                            for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-                                for (int e = 0; e < 4; ++e) {
-                                    s0[rb][4 * g + e] = c0[e] != kNoKey ? s0[rb][4 * g + e] : -INFINITY;
-                                    s1[rb][4 * g + e] = c1[e] != kNoKey ? s1[rb][4 * g + e] : -INFINITY;
-                                }
-                        }
-                    }
-                } else {
-                    // keep bits of key slots 0..31 (lo) and 32..63 (hi) for each row block
-                    const int kmax = a.mode == kModeBlock ? L - rec.k0 : (int)(rec.aux & kAuxMask);
-                    uint32_t vlo = ~0u, vhi = ~0u;  // slots >= kmax: past the sequence / list end
-                    if (kmax < 64) {
-                        vlo = kmax >= 32 ? ~0u : ((1u << max(kmax, 0)) - 1u);
-                        vhi = kmax <= 32 ? 0u : ((1u << (kmax - 32)) - 1u);
-                    }
-#pragma unroll
-                    for (int rb = 0; rb < RB; ++rb) {
-                        uint32_t lo = vlo, hi = vhi;
-                        if (a.mode == kModeBlock) {
-                            const int sq = (q[rb] - task.q0) >> a.bq_shift;
-                            const uint32_t rowbits = rec.aux >> (sq * a.nsk);
-                            lo &= (rowbits & 1u) ? ~0u : 0u;
-                            hi &= ((rowbits >> (a.nsk - 1)) & 1u) ? ~0u : 0u;
-                        }
-                        lo >>= 4 * hf;
-                        hi >>= 4 * hf;
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int bit = 8 * (r / 4) + (r % 4);
-                            s0[rb][r] = ((lo >> bit) & 1u) ? s0[rb][r] : -INFINITY;
-                            s1[rb][r] = ((hi >> bit) & 1u) ? s1[rb][r] : -INFINITY;
-                        }
-                    }
-                }
-            }
+            if (rec.aux & kPartial) mask_partial_tile<RB>(s0, s1, a, rec.k0, rec.aux, video, pat, LDS_PTR(const int, &kcoord[cur][4 * hf]), qt, qwin, q, task.q0, hf);
 
             // ---- online softmax per row block (reference max moves only by more than kSlack)
             u32x4 pk[RB][4];  // bf16 pairs, one cvt_pk each

@@ -12,6 +12,7 @@ from bsa_helpers import plan_workload
 
 MAX_ABS = 1e-2   # bf16 inputs: max-abs error against the fp64 oracle
 MEAN_ABS = 1e-3  # bf16 inputs: mean-abs error against the fp64 oracle
+ROW_REL_F32 = 1e-5  # fp32 inputs: max over rows of |O - O_ref|_inf / |O_ref|_inf
 
 
 def log(*a):
@@ -23,11 +24,22 @@ def to_device_bf16(x_u16: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(x_u16.view(np.int16)).view(torch.bfloat16).to("cuda:0")
 
 
+def to_device(x: np.ndarray) -> torch.Tensor:
+    """bf16 bit patterns (uint16) or float32 host arrays -> cuda:0 tensor."""
+    if x.dtype == np.uint16:
+        return to_device_bf16(x)
+    assert x.dtype == np.float32
+    return torch.from_numpy(np.ascontiguousarray(x)).to("cuda:0")
+
+
 def run_gpu(w, Q, K, V, force_regime=-1, plan=None, fill=float("nan")):
-    """Plan + forward on cuda:0; returns (O as float64 numpy [B][H][L][d], plan)."""
-    p = plan if plan is not None else plan_workload(w, device=0, force_regime=force_regime)
-    q, k, v = to_device_bf16(Q), to_device_bf16(K), to_device_bf16(V)
-    o = torch.full(q.shape, fill, dtype=torch.bfloat16, device="cuda:0")
+    """Plan + forward on cuda:0 in the inputs' dtype (bf16 bits or float32);
+    returns (O as float64 numpy [B][H][L][d], plan)."""
+    f32 = Q.dtype == np.float32
+    dtype = bsa.DTYPE_F32 if f32 else bsa.DTYPE_BF16
+    p = plan if plan is not None else plan_workload(w, device=0, force_regime=force_regime, dtype=dtype)
+    q, k, v = to_device(Q), to_device(K), to_device(V)
+    o = torch.full(q.shape, fill, dtype=torch.float32 if f32 else torch.bfloat16, device="cuda:0")
     bsa.forward(p, q, k, v, o)
     torch.cuda.synchronize()
     return o.float().cpu().numpy().astype(np.float64), p
@@ -62,6 +74,37 @@ def compare(w, Q, K, V, O_gpu, rows=None, label=""):
     assert mx <= MAX_ABS, f"{label}: max-abs {mx}"
     assert mean <= MEAN_ABS, f"{label}: mean-abs {mean}"
     return mx, mean
+
+
+def compare_f32(w, Q, K, V, O_gpu, rows=None, label=""):
+    """fp32 build: per-row normwise relative error against the fp64 oracle
+    (max over rows of |O - O_ref|_inf / |O_ref|_inf <= 1e-5); rows without a
+    kept key exactly 0; elementwise relative error reported only."""
+    if rows is None:
+        rows = np.arange(w.B * w.H * w.L, dtype=np.int64)
+    ref, cnt = oracle.attend(w, Q, K, V, rows=rows, return_counts=True)
+    got = O_gpu.reshape(-1, w.d)[rows]
+    nan = int(np.isnan(got).sum())
+    zero_rows = cnt == 0
+    zero_ok = bool(np.all(got[zero_rows] == 0.0))
+    live = ~zero_rows
+    num = np.abs(got[live] - ref[live]).max(axis=1)
+    den = np.abs(ref[live]).max(axis=1)
+    row_rel = num / den
+    worst = float(row_rel.max()) if row_rel.size else 0.0
+    elem = np.abs(got[live] - ref[live]) / np.maximum(np.abs(ref[live]), 1e-30)
+    log(f"[parity f32] {label}: rows={rows.size} max_row_rel={worst:.3e} median_row_rel="
+        f"{float(np.median(row_rel)) if row_rel.size else 0:.3e} max_elem_rel={float(elem.max()) if elem.size else 0:.3e} "
+        f"nan={nan} empty_rows={int(zero_rows.sum())} empty_exact_zero={zero_ok}")
+    if worst > ROW_REL_F32:
+        idx = np.flatnonzero(live)
+        for i in np.argsort(-row_rel)[:8]:
+            bh, q = divmod(int(rows[idx[i]]), w.L)
+            log(f"    worst row: head={bh % w.H} q={q} kept={int(cnt[idx[i]])} row_rel={row_rel[i]:.3e}")
+    assert nan == 0, f"{label}: {nan} NaN outputs"
+    assert zero_ok, f"{label}: rows without kept keys are not exactly 0"
+    assert worst <= ROW_REL_F32, f"{label}: max row-relative error {worst}"
+    return worst
 
 
 def sample_rows(w, per_head=64, seed=0, tile=128):

@@ -38,7 +38,7 @@ def _small_block_cases():
     return out
 
 
-@pytest.mark.parametrize("regime", [-1, 0, 1])
+@pytest.mark.parametrize("regime", [-1, 0, 1, 4])
 def test_tiny_config(regime):
     w = wl.tiny()
     Q, K, V = wl.make_qkv(w)
@@ -48,7 +48,7 @@ def test_tiny_config(regime):
 
 
 @pytest.mark.parametrize("w", _small_block_cases(), ids=lambda w: w.name)
-@pytest.mark.parametrize("regime", [0, 1])
+@pytest.mark.parametrize("regime", [0, 1, 4])
 def test_small_block_masks(w, regime):
     Q, K, V = wl.make_qkv(w)
     log(f"[case] {w.name} regime={regime}")
@@ -123,3 +123,37 @@ def test_fgattn_full_size_sampled():
     O, p = run_gpu(w, Q, K, V)
     rows = sample_rows(w, per_head=16, tile=64)
     compare(w, Q, K, V, O, rows=rows, label=f"fgattn {p.info()}")
+
+
+@pytest.fixture(scope="module")
+def tessera_qkv():
+    log("[case] generating Tessera-style Q/K/V (24 x 75600 x 128)")
+    return wl.make_qkv(wl.tessera(0))
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("i", [0, 5, 10, 14, 19, 23, 27, 31, 35, 40, 47])
+def test_tessera_full_size_sampled(i, tessera_qkv):
+    """Tessera-style block masks at full size (24 heads, L = 75,600, d = 128):
+    every block shape, density and layout appears among the masks tested;
+    sampled rows of every head, including the ragged last query tile."""
+    w = wl.tessera(i)
+    Q, K, V = tessera_qkv
+    log(f"[case] tessera mask {i}: {w.bq}x{w.bk} density {float(w.block.mean()):.4f}")
+    O, p = run_gpu(w, Q, K, V)
+    rows = sample_rows(w, per_head=12, tile=256)
+    compare(w, Q, K, V, O, rows=rows, label=f"tessera{i} {p.info()['regime']}")
+
+
+@pytest.mark.timeout(900)
+def test_highres_full_size_sampled():
+    """High-res 128x128 rasterised block mask at full size (24 heads,
+    L = 302,400, d = 128; spatial heads frame-major, temporal heads
+    temporal-major); sampled rows of every head."""
+    w = wl.highres()
+    log("[case] generating high-res Q/K/V (24 x 302400 x 128)")
+    Q, K, V = wl.make_qkv(w)
+    log("[case] highres full")
+    O, p = run_gpu(w, Q, K, V)
+    rows = sample_rows(w, per_head=8, tile=128)
+    compare(w, Q, K, V, O, rows=rows, label=f"highres {p.info()}")
