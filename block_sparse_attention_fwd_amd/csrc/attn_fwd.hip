@@ -100,7 +100,12 @@ __device__ __forceinline__ void copy16_to_lds_s(const void *base, uint32_t off, 
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(sb), "s"(lds) : "memory", "m0");
 #pragma clang diagnostic pop
 }
-__device__ __forceinline__ void wait_copies() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// All vector-memory operations issued so far (the copies included) have
+// completed: s_waitcnt vmcnt(0), written with the compiler builtin so that the
+// compiler's own wait bookkeeping sees it and does not wait again, later, for
+// loads it issued before this point (with copies in flight, such a wait would
+// stall on the copies).
+__device__ __forceinline__ void wait_copies() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 __device__ __forceinline__ bf16x8 load_bf16x8(const __bf16 *p)
 {
@@ -185,8 +190,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1
         const int pos = lane % C::CHUNKS;
         int idx_nxt[C::INSTS];  // gathered logical key positions of the next tile to fetch
 
-        auto load_indices = [&](int rec_i, int *dst) {
-            const TileRec r = a.tiles[__builtin_amdgcn_readfirstlane(rec_i)];  // scalar load
+        RecordStream rs;
+        rs.init(a.tiles, task.tb, task.te, lane);
+
+        auto load_indices = [&](const TileRec r, int *dst) {
             const int cnt = (int)(r.aux & kAuxMask);
 #pragma unroll
             for (int i = 0; i < C::INSTS; ++i) {
@@ -206,8 +213,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1
             kgoff[i] = (uint32_t)(slot * C::ROWB + 16 * (pos ^ swz_k<D>(slot)));
             vgoff[i] = (uint32_t)(slot * C::ROWB + 16 * (pos ^ swz_v<D>(slot & 3)));
         }
-        auto fetch_tile = [&](int rec_i, const int *idx, int buf) {
-            const TileRec r = a.tiles[__builtin_amdgcn_readfirstlane(rec_i)];
+        auto fetch_tile = [&](const TileRec r, const int *idx, int buf) {
             const uint32_t kl = (uint32_t)(uintptr_t)&ksm[buf][0], vl = (uint32_t)(uintptr_t)&vsm[buf][0];
             if (!tm && !gather && r.k0 + C::BK <= L) {
                 // 64 consecutive rows: scalar base + loop-invariant lane offsets
@@ -219,15 +225,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1
                     copy16_to_lds_s(vb, vgoff[i], __builtin_amdgcn_readfirstlane(vl + off));
                 }
             } else {
+                // listed rows (gather) or rows of a temporal-major head: one
+                // address per lane, all computed before the copies are issued
+                int ktok[C::INSTS];
 #pragma unroll
-            for (int i = 0; i < C::INSTS; ++i) {
-                const int slot = (w * C::INSTS + i) * C::RPI + lane / C::CHUNKS;
-                const int kpos = gather ? idx[i] : min(r.k0 + slot, L - 1);
-                const int ktok = token(kpos);
-                const uint32_t off = (uint32_t)((w * C::INSTS + i) * 1024);
-                copy16_to_lds(Kh + (size_t)ktok * D + 8 * (pos ^ swz_k<D>(slot)), __builtin_amdgcn_readfirstlane(kl + off));
-                copy16_to_lds(Vh + (size_t)ktok * D + 8 * (pos ^ swz_v<D>(slot & 3)), __builtin_amdgcn_readfirstlane(vl + off));
-            }
+                for (int i = 0; i < C::INSTS; ++i) {
+                    const int slot = (w * C::INSTS + i) * C::RPI + lane / C::CHUNKS;
+                    ktok[i] = token(gather ? idx[i] : min(r.k0 + slot, L - 1));
+                }
+#pragma unroll
+                for (int i = 0; i < C::INSTS; ++i) {
+                    const int slot = (w * C::INSTS + i) * C::RPI + lane / C::CHUNKS;
+                    const uint32_t off = (uint32_t)((w * C::INSTS + i) * 1024);
+                    copy16_to_lds(Kh + (size_t)ktok[i] * D + 8 * (pos ^ swz_k<D>(slot)), __builtin_amdgcn_readfirstlane(kl + off));
+                    copy16_to_lds(Vh + (size_t)ktok[i] * D + 8 * (pos ^ swz_v<D>(slot & 3)), __builtin_amdgcn_readfirstlane(vl + off));
+                }
             }
             if (video && w == 0) {
                 // per key slot: frame (spatial) or packed (y << 16) | x
@@ -242,9 +254,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1
         };
 
         // prologue: tile 0 into buffer 0
-        if (gather) load_indices(task.tb, idx_nxt);
-        fetch_tile(task.tb, idx_nxt, 0);
-        if (gather && ntile > 1) load_indices(task.tb + 1, idx_nxt);
+        if (gather) load_indices(rs.get(0), idx_nxt);
+        fetch_tile(rs.get(0), idx_nxt, 0);
+        if (gather && ntile > 1) load_indices(rs.get(1), idx_nxt);
         finish_tile(0);
         __syncthreads();
 
@@ -267,11 +279,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1
         // loop-invariant register plus an immediate offset
         auto tile_step = [&](const int j, auto cur_c) {
             constexpr int cur = decltype(cur_c)::value;
-            const TileRec rec = a.tiles[__builtin_amdgcn_readfirstlane(task.tb + j)];
+            if ((j & 63) == 0 && j > 0) rs.advance();
+            const TileRec rec = rs.get(j);
             const bool more = j + 1 < ntile;
             if (more) {
-                fetch_tile(task.tb + j + 1, idx_nxt, cur ^ 1);
-                if (gather && j + 2 < ntile) load_indices(task.tb + j + 2, idx_nxt);
+                fetch_tile(rs.get(j + 1), idx_nxt, cur ^ 1);
+                if (gather && j + 2 < ntile) load_indices(rs.get(j + 2), idx_nxt);
             }
 
             // ---- S^T = K Q^T: s0 = keys 0..31, s1 = keys 32..63 of each row block

@@ -86,8 +86,11 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_f32(KernelArgs a)
             }
         const f32x16 zero16 = {};
 
+        RecordStream rs;
+        rs.init(a.tiles, task.tb, task.te, lane);
         for (int j = 0; j < ntile; ++j) {
-            const TileRec rec = a.tiles[__builtin_amdgcn_readfirstlane(task.tb + j)];
+            if ((j & 63) == 0 && j > 0) rs.advance();
+            const TileRec rec = rs.get(j);
             const int cnt = (int)(rec.aux & kAuxMask);
             __syncthreads();  // the previous tile's LDS readers are done
             // ---- K/V tile -> LDS (rows past the sequence / list end repeat a

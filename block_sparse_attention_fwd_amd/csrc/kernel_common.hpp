@@ -86,6 +86,56 @@ __device__ __forceinline__ float max3f(float a, float b, float c)
     return r;
 }
 
+// The key-tile records of one task, as a wave reads them: 64 records per
+// vector load (lane l holds record 64 c + l of chunk c), one chunk ahead of
+// use, and a record is taken out with two lane reads into scalar registers.
+// A per-tile load of each record would put a memory round trip in front of
+// every tile. get(j) serves records j in [64*chunk, 64*chunk + 128) of the
+// task; advance() is called at the top of the tile step that enters a new
+// chunk, where no tile copies are in flight, so the wait for the chunk loaded
+// 64 tiles earlier costs nothing. Lanes past the task's end repeat its last
+// record (no branch, so the loads land straight in their registers).
+struct RecordStream {
+    const TileRec *tiles;
+    int tb, te, lane, chunk;
+    uint32_t cur_k0, cur_aux, nxt_k0, nxt_aux;
+
+    __device__ __forceinline__ void load(int c, uint32_t &k0, uint32_t &aux) const
+    {
+        const TileRec r = tiles[min(tb + 64 * c + lane, te - 1)];
+        k0 = (uint32_t)r.k0;
+        aux = r.aux;
+    }
+    __device__ __forceinline__ void init(const TileRec *t, int b, int e, int ln)
+    {
+        tiles = t;
+        tb = b;
+        te = e;
+        lane = ln;
+        chunk = 0;
+        load(0, cur_k0, cur_aux);
+        load(1, nxt_k0, nxt_aux);
+    }
+    __device__ __forceinline__ void advance()
+    {
+        cur_k0 = nxt_k0;
+        cur_aux = nxt_aux;
+        ++chunk;
+        load(chunk + 1, nxt_k0, nxt_aux);
+    }
+    __device__ __forceinline__ TileRec get(int j) const
+    {
+        const bool in_cur = (j >> 6) == chunk;
+        const int l = j & 63;
+        const uint32_t k0c = __builtin_amdgcn_readlane(cur_k0, l), k0n = __builtin_amdgcn_readlane(nxt_k0, l);
+        const uint32_t axc = __builtin_amdgcn_readlane(cur_aux, l), axn = __builtin_amdgcn_readlane(nxt_aux, l);
+        TileRec r;
+        r.k0 = (int32_t)(in_cur ? k0c : k0n);
+        r.aux = in_cur ? axc : axn;
+        return r;
+    }
+};
+
 // Exact predicate of a PARTIAL 64-key tile (Sparse VideoGen / Splash
 // Attention summary, "Splash Attention": exact coordinate masking on boundary
 // tiles only). s0 / s1 are the scores of keys 0..31 / 32..63 of each 32-row
