@@ -17,6 +17,7 @@ with the kept pairs counted by the CPU oracle's own mask expansion.
 Prints one JSON line.
 """
 import argparse
+import contextlib
 import hashlib
 import json
 import os
@@ -123,7 +124,8 @@ def parity_sample(w, Q, K, V, o):
     from gpu_util import compare, sample_rows
     O = o.float().cpu().numpy().astype(np.float64)
     rows = sample_rows(w, per_head=8)
-    mx, mean = compare(w, Q, K, V, O, rows=rows, label="bench sample")
+    with contextlib.redirect_stdout(sys.stderr):  # stdout carries only the JSON line
+        mx, mean = compare(w, Q, K, V, O, rows=rows, label="bench sample")
     return {"rows": int(rows.size), "max_abs": mx, "mean_abs": mean}
 
 

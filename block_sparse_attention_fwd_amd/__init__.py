@@ -84,6 +84,14 @@ def lib(path: str = LIB_PATH):
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build() (no CPU fallback exists)")
+    # PyTorch ships its own HIP runtime under the same soname. Loading torch
+    # first makes the library bind to that runtime, so that device pointers
+    # and streams from torch are valid in the library (two HIP runtimes in one
+    # process do not share devices, memory or streams).
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     L = ctypes.CDLL(path)
     L.bsa_abi_version.restype = ctypes.c_int32
     L.bsa_plan_opts_default.argtypes = [ctypes.POINTER(PlanOpts)]

@@ -157,14 +157,23 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1
     const bool gather = a.mode == kModeGather;
     const bool video = a.mode == kModeVideo;
 
+    // Softmax reference: a row takes the maximum of its first kept scores as
+    // reference and keeps it; the per-tile row maximum is computed only while
+    // some row of the wave has no reference yet. Scores more than 64 (base 2)
+    // above the reference would make sums overflow: a row whose sum ends above
+    // 2^64, or not finite, makes the whole task run again in careful mode,
+    // where every tile computes its row maximum and the reference follows it
+    // (moving only when a tile's maximum exceeds it by more than kSlack).
+    bool careful = false;
     f32x16 oacc[RB][D / 32];
+    float m_ref[RB], l_run[RB];
+    for (;;) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int n = 0; n < D / 32; ++n)
 #pragma unroll
             for (int r = 0; r < 16; ++r) oacc[rb][n][r] = 0.f;
-    float m_ref[RB], l_run[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) { m_ref[rb] = -INFINITY; l_run[rb] = 0.f; }
 
@@ -312,24 +321,26 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1
             // ---- exact mask on PARTIAL tiles only
             if (rec.aux & kPartial) mask_partial_tile<RB>(s0, s1, a, rec.k0, rec.aux, video, pat, LDS_PTR(const int, &kcoord[cur][4 * hf]), qt, qwin, q, task.q0, hf);
 
-            // ---- online softmax per row block (reference max moves only by more than kSlack)
+            // ---- online softmax per row block
             u32x4 pk[RB][4];  // bf16 pairs, one cvt_pk each
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
-                float mx = fmaxf(s0[rb][0], s1[rb][0]);
+                if (careful || __builtin_amdgcn_ballot_w64(m_ref[rb] == -INFINITY)) {
+                    float mx = fmaxf(s0[rb][0], s1[rb][0]);
 #pragma unroll
-                for (int r = 1; r < 16; ++r) mx = max3f(mx, s0[rb][r], s1[rb][r]);
-                mx = swap_halves_max(mx) * a.scale_log2;
-                const bool need = mx > m_ref[rb] + kSlack;
-                if (__builtin_amdgcn_ballot_w64(need)) {
-                    // lanes that keep their reference (also those still at -inf) scale by exactly 1
-                    const float alpha = need ? __builtin_amdgcn_exp2f(m_ref[rb] - mx) : 1.0f;
-                    m_ref[rb] = need ? mx : m_ref[rb];
-                    l_run[rb] *= alpha;
+                    for (int r = 1; r < 16; ++r) mx = max3f(mx, s0[rb][r], s1[rb][r]);
+                    mx = swap_halves_max(mx) * a.scale_log2;
+                    const bool need = mx > m_ref[rb] + kSlack;
+                    if (__builtin_amdgcn_ballot_w64(need)) {
+                        // lanes that keep their reference (also those still at -inf) scale by exactly 1
+                        const float alpha = need ? __builtin_amdgcn_exp2f(m_ref[rb] - mx) : 1.0f;
+                        m_ref[rb] = need ? mx : m_ref[rb];
+                        l_run[rb] *= alpha;
 #pragma unroll
-                    for (int n = 0; n < D / 32; ++n)
+                        for (int n = 0; n < D / 32; ++n)
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) oacc[rb][n][r] *= alpha;
+                            for (int r = 0; r < 16; ++r) oacc[rb][n][r] *= alpha;
+                    }
                 }
                 const float m_use = m_ref[rb] == -INFINITY ? 0.f : m_ref[rb];
                 const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
@@ -383,6 +394,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1
             tile_step(j + 1, IntC<1>{});
         }
         if (j < ntile) tile_step(j, IntC<0>{});
+    }
+    bool bad = false;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) bad |= !(l_run[rb] <= 0x1p64f);
+    if (careful || !__syncthreads_or(bad)) break;
+    careful = true;
     }
 
     // ---- epilogue: O = O / l (0 for rows without a kept key), bf16 RNE

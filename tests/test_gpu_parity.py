@@ -157,3 +157,28 @@ def test_highres_full_size_sampled():
     O, p = run_gpu(w, Q, K, V)
     rows = sample_rows(w, per_head=8, tile=128)
     compare(w, Q, K, V, O, rows=rows, label=f"highres {p.info()}")
+
+
+@pytest.mark.parametrize("scale_first", [False, True])
+def test_wide_score_range(scale_first):
+    """Keys of one part of the sequence scaled by 100, so that scores of
+    later tiles lie far above (or far below) the reference a row takes from
+    its first tiles: exercises the overflow check and the careful re-run."""
+    w = wl.tiny()
+    w.block[:] = 1
+    Q, K, V = wl.make_qkv(w)
+    k = wl.bf16_bits_to_f32(K).copy()
+    half = w.L // 2
+    if scale_first:
+        k[:, :, :half, :] *= 100.0
+    else:
+        k[:, :, half:, :] *= 100.0
+    K = wl.f32_to_bf16_bits(k)
+    log(f"[case] wide score range scale_first={scale_first}")
+    O, _ = run_gpu(w, Q, K, V)
+    # Scores this wide make most rows' softmax nearly one-hot, where the one
+    # bf16 rounding of P (relative 2^-9 per weight) is no longer averaged
+    # over many keys: the bound is then |dO| <= 2^-9 * 2 max|V| per element.
+    vmax = float(np.abs(wl.bf16_bits_to_f32(V)).max())
+    compare(w, Q, K, V, O, label=f"wide range first={scale_first}", max_abs=2.0 ** -8 * vmax)
+
