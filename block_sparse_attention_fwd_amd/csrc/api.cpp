@@ -179,7 +179,7 @@ struct bsa_plan_s {
     int32_t T = 0, Hg = 0, Wg = 0, anchor = 0, radius = 0;
     int32_t bq_shift = 0, bk_shift = 0, nsk = 1, sub_q = 0, sub_k = 0;
     int32_t mode = 0;
-    int32_t task_order = 1;  // 0 = XCD segments, 1 = longest first
+    int32_t task_order = 1;  // 0 = XCD segments, 1 = longest first, 2 = longest first in XCD blocks
     std::vector<uint8_t> head_layout, head_pattern;
     // image
     uint8_t *img = nullptr;
@@ -830,6 +830,13 @@ size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 //    the longest are padded with no-op tasks (bh = -1).
 //  - LPT order (default): longest task first (a stable counting sort on the tile
 //    count), so the tail of the grid holds the cheapest work.
+static int cu_count(int device)
+{
+    int n = 256;
+    if (device >= 0 && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) n = 256;
+    return std::max(1, n);
+}
+
 static int xcd_count()
 {
     if (const char *e = std::getenv("BSA_XCDS")) return std::max(1, std::atoi(e));
@@ -877,7 +884,23 @@ static int32_t organise_tasks(bsa_plan_s &p, const std::vector<HeadOut *> &heads
         seg_len = 0;
         for (int k = 0; k < X; ++k) seg_len = std::max(seg_len, seg_start[k + 1] - seg_start[k]);
     }
-    p.ntasks = X > 1 ? seg_len * X : nreal;
+    // XCD blocks of the longest-first order: the order is cut into blocks of
+    // G tasks (one round of the XCD's workgroup slots), and block b runs on
+    // XCD b % X, so each XCD works through a contiguous piece of the order --
+    // tasks of similar length, adjacent in (head, query tile), sharing key
+    // tiles in that XCD's L2 -- and every XCD gets blocks of all lengths.
+    const int XB = p.task_order == 2 ? xcd_count() : 1;
+    const int64_t G = std::max<int64_t>(1, 2 * (int64_t)cu_count(p.device) / std::max(1, XB));
+    int64_t blk_len = 0;
+    if (XB > 1) {
+        const int64_t nb = (nreal + G - 1) / G;
+        for (int x = 0; x < XB; ++x) {
+            int64_t len = 0;
+            for (int64_t b = x; b < nb; b += XB) len += std::min(G, nreal - b * G);
+            blk_len = std::max(blk_len, len);
+        }
+    }
+    p.ntasks = X > 1 ? seg_len * X : (XB > 1 ? blk_len * XB : nreal);
     p.nreal_tasks = nreal;
     p.off_tasks = 0;
     p.off_tiles = align_up(std::max<int64_t>(1, p.ntasks) * sizeof(Task));
@@ -929,7 +952,20 @@ static int32_t organise_tasks(bsa_plan_s &p, const std::vector<HeadOut *> &heads
         std::vector<int64_t> bucket((size_t)max_cost + 2, 0);
         for (const Task &t : unsorted) ++bucket[(size_t)(max_cost - (t.te - t.tb)) + 1];
         for (size_t c = 1; c < bucket.size(); ++c) bucket[c] += bucket[c - 1];
-        for (const Task &t : unsorted) tasks[bucket[(size_t)(max_cost - (t.te - t.tb))]++] = t;
+        if (XB == 1) {
+            for (const Task &t : unsorted) tasks[bucket[(size_t)(max_cost - (t.te - t.tb))]++] = t;
+        } else {
+            std::vector<Task> lpt((size_t)nreal);
+            for (const Task &t : unsorted) lpt[bucket[(size_t)(max_cost - (t.te - t.tb))]++] = t;
+            const Task noop{-1, 0, 0, 0};
+            const int64_t nb = (nreal + G - 1) / G;
+            for (int x = 0; x < XB; ++x) {
+                int64_t k = 0;
+                for (int64_t b = x; b < nb; b += XB)
+                    for (int64_t i = b * G; i < std::min(nreal, (b + 1) * G); ++i) tasks[(k++) * XB + x] = lpt[i];
+                for (; k < blk_len; ++k) tasks[k * XB + x] = noop;
+            }
+        }
     }
     uint32_t *flags = (uint32_t *)(p.img + p.off_flags);
     for (int h = 0; h < p.H; ++h)
@@ -1051,7 +1087,8 @@ extern "C" int32_t bsa_plan(const bsa_mask_desc_t *logical_mask, int32_t B, int3
         p->T = o.T; p->Hg = o.Hg; p->Wg = o.Wg;
         p->anchor = m.anchor_frame; p->radius = m.radius;
         p->device = o.device;
-        if (const char *e = std::getenv("BSA_TASK_ORDER")) p->task_order = std::strcmp(e, "xcd") == 0 ? 0 : 1;
+        if (const char *e = std::getenv("BSA_TASK_ORDER"))
+            p->task_order = std::strcmp(e, "xcd") == 0 ? 0 : (std::strcmp(e, "xcdlpt") == 0 ? 2 : 1);
         p->head_layout.assign(H, 0);
         if (o.head_layout) p->head_layout.assign(o.head_layout, o.head_layout + H);
         p->head_pattern.assign(H, 0);
@@ -1159,7 +1196,7 @@ extern "C" int32_t bsa_forward(bsa_plan_t p, const void *Q, const void *K, const
     hipError_t e = hipStreamWaitEvent((hipStream_t)stream, p->uploaded, 0);
     if (e == hipSuccess) {
         const Regime &R = kRegimes[p->regime];
-        e = p->dtype == BSA_DTYPE_F32 ? launch_forward_f32(a, R.waves, p->d, (hipStream_t)stream)
+        e = p->dtype == BSA_DTYPE_F32 ? launch_forward_f32(a, R.tile_q / 32, p->d, (hipStream_t)stream)
                                       : launch_forward(a, R.waves, R.rb, p->d, p->dtype, (hipStream_t)stream);
     }
     if (cur != p->device) (void)hipSetDevice(cur);

@@ -127,11 +127,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1
     const int tid = threadIdx.x;
     const int lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
-    const Task task = a.tasks[blockIdx.x];
+    // task fields and head flags are workgroup-uniform: scalar registers
+    const Task tl = a.tasks[blockIdx.x];
+    const Task task{__builtin_amdgcn_readfirstlane(tl.bh), __builtin_amdgcn_readfirstlane(tl.q0),
+                    __builtin_amdgcn_readfirstlane(tl.tb), __builtin_amdgcn_readfirstlane(tl.te)};
     if (task.bh < 0) return;  // padding task of an XCD segment
     const int bh = task.bh;
     const int h = bh % a.H;
-    const uint32_t hflag = a.head_flags[h];
+    const uint32_t hflag = (uint32_t)__builtin_amdgcn_readfirstlane((int)a.head_flags[h]);
     const bool tm = (hflag & kHeadTemporalMajor) != 0;
     const int pat = (int)((hflag >> kHeadPatShift) & 3u);
     const int L = a.L;

@@ -129,9 +129,11 @@ struct RecordStream {
         const int l = j & 63;
         const uint32_t k0c = __builtin_amdgcn_readlane(cur_k0, l), k0n = __builtin_amdgcn_readlane(nxt_k0, l);
         const uint32_t axc = __builtin_amdgcn_readlane(cur_aux, l), axn = __builtin_amdgcn_readlane(nxt_aux, l);
+        // (the fields are wave-uniform; readfirstlane keeps them, and all the
+        // address arithmetic on them, in scalar registers)
         TileRec r;
-        r.k0 = (int32_t)(in_cur ? k0c : k0n);
-        r.aux = in_cur ? axc : axn;
+        r.k0 = __builtin_amdgcn_readfirstlane((int32_t)(in_cur ? k0c : k0n));
+        r.aux = (uint32_t)__builtin_amdgcn_readfirstlane((int32_t)(in_cur ? axc : axn));
         return r;
     }
 };

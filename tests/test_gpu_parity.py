@@ -64,7 +64,7 @@ def test_small_video(run, d):
     w.anchor = 2 if run == "B" else 0
     w.head_layout = np.array([0, 1, 1, 1], np.uint8) if run == "B" else np.zeros(4, np.uint8)
     Q, K, V = wl.make_qkv(w)
-    for regime in (0, 1):
+    for regime in (0, 1, 4):
         log(f"[case] small video run={run} d={d} regime={regime}")
         O, _ = run_gpu(w, Q, K, V, force_regime=regime)
         compare(w, Q, K, V, O, label=f"video{run} d{d} r{regime}")
@@ -104,14 +104,15 @@ def test_deterministic_repeat():
     assert np.array_equal(O1, O2)
 
 
+@pytest.mark.parametrize("regime", [-1, 4])
 @pytest.mark.parametrize("run", ["A", "B"])
-def test_svg_full_size_sampled(run):
+def test_svg_full_size_sampled(run, regime):
     """SVG head routing at full size (24 heads, 13 x 30x52, d=128), in the
     launch configuration the benchmark times; sampled rows of every head."""
     w = wl.svg(run)
     Q, K, V = wl.make_qkv(w)
-    log(f"[case] svg full run={run}")
-    O, p = run_gpu(w, Q, K, V)
+    log(f"[case] svg full run={run} regime={regime}")
+    O, p = run_gpu(w, Q, K, V, force_regime=regime)
     rows = sample_rows(w, per_head=48)
     compare(w, Q, K, V, O, rows=rows, label=f"svg{run} {p.info()}")
 
@@ -159,8 +160,9 @@ def test_highres_full_size_sampled():
     compare(w, Q, K, V, O, rows=rows, label=f"highres {p.info()}")
 
 
+@pytest.mark.parametrize("regime", [-1, 4])
 @pytest.mark.parametrize("scale_first", [False, True])
-def test_wide_score_range(scale_first):
+def test_wide_score_range(scale_first, regime):
     """Keys of one part of the sequence scaled by 100, so that scores of
     later tiles lie far above (or far below) the reference a row takes from
     its first tiles: exercises the overflow check and the careful re-run."""
@@ -174,8 +176,8 @@ def test_wide_score_range(scale_first):
     else:
         k[:, :, half:, :] *= 100.0
     K = wl.f32_to_bf16_bits(k)
-    log(f"[case] wide score range scale_first={scale_first}")
-    O, _ = run_gpu(w, Q, K, V)
+    log(f"[case] wide score range scale_first={scale_first} regime={regime}")
+    O, _ = run_gpu(w, Q, K, V, force_regime=regime)
     # Scores this wide make most rows' softmax nearly one-hot, where the one
     # bf16 rounding of P (relative 2^-9 per weight) is no longer averaged
     # over many keys: the bound is then |dO| <= 2^-9 * 2 max|V| per element.
