@@ -1,0 +1,147 @@
+#!/usr/bin/env python3
+"""Offline profiling that builds the regime lookup table for this GPU.
+
+Tessera (arXiv 2609.25869), abstract: the execution regime of a request is
+chosen through a lookup table built by offline profiling, which keeps
+preparation cheap at run time. This script is that offline step: for every
+bin of the table's features -- mask kind, logical block shape, kept-block
+density, sequence length -- it plans and runs synthetic requests of that bin
+with every regime that can run them, times the forward passes on the GPU and
+writes the fastest regime of each bin as one rule of the table.
+
+Inputs are seeded and synthetic (workloads module): BLOCK masks in banded,
+local-window and random layouts, video head routing (half spatial heads,
+half temporal heads in temporal-major order), Q/K/V ~ N(0,1) in bf16.
+
+Usage (on the target GPU, from the repository root):
+    python3 block_sparse_attention_fwd_amd/lut/build_lut.py [--out lut/gfx950.lut] [--quick]
+Prints one progress line per measurement and writes the table (rules plus the
+measurements as comments). Rebuild the library afterwards: the default table
+is compiled into it.
+"""
+import argparse
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(os.path.dirname(HERE))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+TILE_REGIMES = (0, 1, 4)        # contiguous-tile regimes (block and video masks)
+SLICE_RULES = ((64, 2), (128, 3))  # slice masks: the gather regime of the slice height
+# sequence-length bins: (representative token grid T x Hg x Wg, L range of the rule)
+LENGTH_BINS = (
+    ((4, 32, 32), (0, 8192)),
+    ((13, 30, 52), (8193, 40000)),
+    ((21, 45, 80), (40001, 9999999999)),
+)
+BLOCK_SHAPES = ((32, 32), (64, 64), (128, 128), (64, 256))
+DENSITY_BINS = ((0.05, (0.0, 0.1)), (0.15, (0.1, 0.275)), (0.4, (0.275, 1.0)))
+LAYOUTS = ("banded", "local", "random")
+
+
+def log(*a):
+    print(*a, flush=True)
+
+
+def time_regimes(bsa, torch, w, regimes, q, k, v, o, reps, rounds=3):
+    """Median forward time (ms) of each regime on workload w. The regimes are
+    timed in interleaved rounds, so that clock and thermal drift during the
+    sweep falls on all of them alike."""
+    from bsa_helpers import plan_workload
+    plans = {r: plan_workload(w, force_regime=r) for r in regimes}
+    try:
+        times = {r: [] for r in regimes}
+        for _ in range(rounds):
+            for r in regimes:
+                p = plans[r]
+                bsa.forward(p, q, k, v, o)
+                torch.cuda.synchronize()
+                ev = []
+                for _ in range(reps):
+                    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    a.record()
+                    bsa.forward(p, q, k, v, o)
+                    b.record()
+                    ev.append((a, b))
+                torch.cuda.synchronize()
+                times[r] += [a.elapsed_time(b) for a, b in ev]
+        return {r: sorted(t)[len(t) // 2] for r, t in times.items()}
+    finally:
+        for p in plans.values():
+            p.close()
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--out", default=os.path.join(HERE, "gfx950.lut"))
+    ap.add_argument("--heads", type=int, default=24, help="heads per synthetic request")
+    ap.add_argument("--reps", type=int, default=5)
+    ap.add_argument("--quick", action="store_true", help="one layout per bin, two length bins")
+    args = ap.parse_args()
+
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import torch
+
+    import block_sparse_attention_fwd_amd as bsa
+    import workloads as wl
+    from gpu_util import to_device_bf16
+
+    assert torch.cuda.is_available(), "the lookup table is built on the GPU it is for"
+    H, d = args.heads, 128
+    length_bins = LENGTH_BINS[:2] if args.quick else LENGTH_BINS
+    layouts = LAYOUTS[:1] if args.quick else LAYOUTS
+    rules, notes = [], []
+    t_start = time.time()
+    for (T, Hg, Wg), (llo, lhi) in length_bins:
+        L = T * Hg * Wg
+        base = wl.Workload("lut", 9, 1, H, L, d, T, Hg, Wg, wl.BLOCK, 64, 64)
+        Q, K, V = wl.make_qkv(base)
+        q, k, v = to_device_bf16(Q), to_device_bf16(K), to_device_bf16(V)
+        o = torch.empty_like(q)
+        # video head routing
+        wv = wl.svg("B", H=H, T=T, Hg=Hg, Wg=Wg, d=d, cfg=9)
+        tv = time_regimes(bsa, torch, wv, TILE_REGIMES, q, k, v, o, args.reps)
+        best = min(tv, key=tv.get)
+        log(f"[lut] video L={L}: " + ", ".join(f"r{r} {t:.4f} ms" for r, t in tv.items()) + f" -> {best}")
+        notes.append(f"video L={L}: " + " ".join(f"r{r}={t:.4f}ms" for r, t in tv.items()))
+        rules.append(f"video   *       *       -1         1          {llo:<4d} {lhi:<10d} {best}")
+        for (bq, bk) in BLOCK_SHAPES:
+            for rho, (dlo, dhi) in DENSITY_BINS:
+                tot = {r: 0.0 for r in TILE_REGIMES}
+                for li, lay in enumerate(layouts):
+                    w = wl.block_request(f"lut_{bq}x{bk}_{rho}_{lay}", 9, li, bq, bk, rho, lay, H, T, Hg, Wg, d)
+                    for r, t in time_regimes(bsa, torch, w, TILE_REGIMES, q, k, v, o, args.reps).items():
+                        tot[r] += t
+                best = min(tot, key=tot.get)
+                log(f"[lut] block {bq}x{bk} density {rho} L={L}: "
+                    + ", ".join(f"r{r} {t:.4f} ms" for r, t in tot.items()) + f" -> {best}")
+                notes.append(f"block {bq}x{bk} rho={rho} L={L} (sum over {len(layouts)} layouts): "
+                             + " ".join(f"r{r}={t:.4f}ms" for r, t in tot.items()))
+                rules.append(f"block   {bq:<7d} {bk:<7d} {dlo:<10g} {dhi:<10g} {llo:<4d} {lhi:<10d} {best}")
+        del q, k, v, o
+        torch.cuda.empty_cache()
+    for m, r in SLICE_RULES:
+        rules.append(f"slice   {m:<7d} 1       0          1          0    9999999999 {r}")
+    # anything not covered (other block shapes): the default tile regime
+    rules.append("block   *       *       0          1          0    9999999999 0")
+    rules.append("video   *       *       -1         1          0    9999999999 0")
+    head = [
+        "# Regime lookup table for gfx950 (MI355X), built by lut/build_lut.py (offline profiling).",
+        "# First matching rule wins. Regimes: 0 = 128x64 tiles (4 waves), 1 = 64x64 tiles (2 waves),",
+        "# 2 = 64-query gather, 3 = 128-query gather, 4 = 256x64 tiles (8 waves).",
+        f"# Synthetic requests: {H} heads, d = {d}, bf16; median of 3 interleaved rounds of {args.reps} forwards.",
+        "# kind  block_q block_k density_lo density_hi L_lo L_hi      regime",
+    ]
+    text = "\n".join(head + rules + ["#", "# measurements:"] + ["# " + n for n in notes]) + "\n"
+    with open(args.out, "w") as f:
+        f.write(text)
+    log(f"[lut] wrote {args.out} ({len(rules)} rules) in {time.time() - t_start:.1f} s")
+
+
+if __name__ == "__main__":
+    np.seterr(all="ignore")
+    main()

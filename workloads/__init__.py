@@ -366,17 +366,23 @@ def _local(T, Hg, Wg, bq, bk, rho):
     return best
 
 
-def tessera(i: int, H=24, T=21, Hg=45, Wg=80, d=128, cfg=4) -> Workload:
-    """Tessera-style dynamic block-sparse request, mask ``i`` of 48."""
-    (bq, bk), rho, lay = c4_params(i)
+def block_request(name, cfg, i, bq, bk, rho, lay, H=24, T=21, Hg=45, Wg=80, d=128) -> Workload:
+    """A BLOCK-mask request on a T x Hg x Wg token grid: layout ``lay``
+    (banded / local / random) at target block density ``rho``."""
     L = T * Hg * Wg
-    w = Workload(f"tessera{i}", cfg, 1, H, L, d, T, Hg, Wg, BLOCK, bq, bk)
+    w = Workload(name, cfg, 1, H, L, d, T, Hg, Wg, BLOCK, bq, bk)
     if lay == "random":
         w.block = bernoulli_block_mask(cfg * 100 + i, 1, H, w.nqb, w.nkb, rho)
     else:
         one = _banded(L, bq, bk, rho) if lay == "banded" else _local(T, Hg, Wg, bq, bk, rho)
         w.block = np.broadcast_to(one, (1, H) + one.shape).copy()
     return w
+
+
+def tessera(i: int, H=24, T=21, Hg=45, Wg=80, d=128, cfg=4) -> Workload:
+    """Tessera-style dynamic block-sparse request, mask ``i`` of 48."""
+    (bq, bk), rho, lay = c4_params(i)
+    return block_request(f"tessera{i}", cfg, i, bq, bk, rho, lay, H, T, Hg, Wg, d)
 
 
 def highres(H=24, T=21, Hg=90, Wg=160, d=128, blk=128, cfg=5) -> Workload:
