@@ -186,7 +186,9 @@ struct bsa_plan_s {
     size_t img_cap = 0, img_bytes = 0;
     bool img_pinned = false;
     std::vector<uint8_t> img_vec;
-    size_t off_tasks = 0, off_tiles = 0, off_gidx = 0, off_flags = 0;
+    size_t off_tasks = 0, off_tiles = 0, off_gidx = 0, off_flags = 0, off_coords = 0;
+    int64_t coord_stride = 0;                   // words per video key-coordinate table
+    std::vector<uint8_t> head_coord_table;      // per head: index of its table
     int64_t ntasks = 0, ntiles = 0, ngidx = 0;  // ntasks: launched workgroups (incl. padding)
     int64_t nreal_tasks = 0;                    // one per (batch, head, query tile)
     const Task *tasks() const { return (const Task *)(img + off_tasks); }
@@ -906,7 +908,20 @@ static int32_t organise_tasks(bsa_plan_s &p, const std::vector<HeadOut *> &heads
     p.off_tiles = align_up(std::max<int64_t>(1, p.ntasks) * sizeof(Task));
     p.off_gidx = p.off_tiles + align_up(std::max<int64_t>(1, p.ntiles) * sizeof(TileRec));
     p.off_flags = p.off_gidx + align_up(std::max<int64_t>(1, p.ngidx) * sizeof(int32_t));
-    p.img_bytes = p.off_flags + align_up((size_t)p.H * sizeof(uint32_t));
+    p.off_coords = p.off_flags + align_up((size_t)p.H * sizeof(uint32_t));
+    // video masks: one key-coordinate table per (pattern, layout) pair the heads use
+    int ntables = 0;
+    int table_of[3][2] = {{-1, -1}, {-1, -1}, {-1, -1}};
+    p.head_coord_table.assign(p.H, 0);
+    if (p.mode == kModeVideo) {
+        p.coord_stride = (p.L + kTileK - 1) / kTileK * kTileK;
+        for (int h = 0; h < p.H; ++h) {
+            int &t = table_of[p.head_pattern[h]][p.head_layout[h] ? 1 : 0];
+            if (t < 0) t = ntables++;
+            p.head_coord_table[h] = (uint8_t)t;
+        }
+    }
+    p.img_bytes = p.off_coords + align_up((size_t)std::max(1, ntables) * (size_t)std::max<int64_t>(1, p.coord_stride) * sizeof(int32_t));
     if (p.device >= 0) {
         p.img = (uint8_t *)pinned_pool().acquire(p.img_bytes, &p.img_cap);
         if (!p.img) return fail(BSA_ERR_OUT_OF_MEMORY, "pinned host allocation of %zu bytes failed", p.img_bytes);
@@ -969,7 +984,32 @@ static int32_t organise_tasks(bsa_plan_s &p, const std::vector<HeadOut *> &heads
     }
     uint32_t *flags = (uint32_t *)(p.img + p.off_flags);
     for (int h = 0; h < p.H; ++h)
-        flags[h] = (p.head_layout[h] ? kHeadTemporalMajor : 0u) | ((uint32_t)p.head_pattern[h] << kHeadPatShift);
+        flags[h] = (p.head_layout[h] ? kHeadTemporalMajor : 0u) | ((uint32_t)p.head_pattern[h] << kHeadPatShift) |
+                   ((uint32_t)p.head_coord_table[h] << kHeadCoordShift);
+    // Key-coordinate word of each logical position of a head, as the exact
+    // video predicates compare it (Sparse VideoGen / Splash Attention summary,
+    // "Splash Attention": coordinate masking on boundary tiles): the frame
+    // (spatial pattern) or (y << 16) | x (temporal pattern) of the position's
+    // token; positions past the sequence end hold a word no predicate keeps.
+    if (p.mode == kModeVideo) {
+        int32_t *coords = (int32_t *)(p.img + p.off_coords);
+        for (int pat = 0; pat < 3; ++pat)
+            for (int lay = 0; lay < 2; ++lay) {
+                if (table_of[pat][lay] < 0) continue;
+                int32_t *c = coords + table_of[pat][lay] * p.coord_stride;
+                // walk the positions in order with running coordinates (no divisions)
+                int32_t t = 0, y = 0, x = 0;
+                for (int64_t k = 0; k < p.L; ++k) {
+                    c[k] = pat == BSA_PAT_SPATIAL ? t : (pat == BSA_PAT_TEMPORAL ? ((y << 16) | x) : 0);
+                    if (lay) {  // j = pixel * T + frame: frame first, then the pixel
+                        if (++t == p.T) { t = 0; if (++x == p.Wg) { x = 0; ++y; } }
+                    } else {    // token = frame * HW + y * Wg + x
+                        if (++x == p.Wg) { x = 0; if (++y == p.Hg) { y = 0; ++t; } }
+                    }
+                }
+                for (int64_t k = p.L; k < p.coord_stride; ++k) c[k] = 0x7FFF7FFF;
+            }
+    }
     return BSA_OK;
 }
 
@@ -1178,6 +1218,8 @@ extern "C" int32_t bsa_forward(bsa_plan_t p, const void *Q, const void *K, const
     a.tiles = (const TileRec *)(dev + p->off_tiles);
     a.gidx = (const int32_t *)(dev + p->off_gidx);
     a.head_flags = (const uint32_t *)(dev + p->off_flags);
+    a.coords = (const int32_t *)(dev + p->off_coords);
+    a.coords_stride = (int32_t)p->coord_stride;
     a.ntasks = (int32_t)p->ntasks;
     a.H = p->H;
     a.L = (int32_t)p->L;

@@ -100,6 +100,18 @@ __device__ __forceinline__ void copy16_to_lds_s(const void *base, uint32_t off, 
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(sb), "s"(lds) : "memory", "m0");
 #pragma clang diagnostic pop
 }
+// One dword per lane (global_load_lds_dword): lane l writes LDS bytes
+// [lds + 4 l, +4); scalar base, 32-bit lane offsets, as copy16_to_lds_s.
+__device__ __forceinline__ void copy4_to_lds_s(const void *base, uint32_t off, uint32_t lds)
+{
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    const uint64_t sb = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(off), "s"(sb), "s"(lds) : "memory", "m0");
+#pragma clang diagnostic pop
+}
 // All vector-memory operations issued so far (the copies included) have
 // completed: s_waitcnt vmcnt(0), written with the compiler builtin so that the
 // compiler's own wait bookkeeping sees it and does not wait again, later, for
@@ -215,8 +227,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1
         };
 
         // global -> LDS copies of a tile (in flight while the previous tile is
-        // computed); the video key coordinates go through a register
-        int stage_c = kNoKey;
+        // computed), the video key coordinates included
+        const int32_t *ctab = a.coords + (int)((hflag >> kHeadCoordShift) & 3u) * a.coords_stride;
         // per-lane byte offsets of the copied chunks within a contiguous tile
         uint32_t kgoff[C::INSTS], vgoff[C::INSTS];
 #pragma unroll
@@ -254,16 +266,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1
                 }
             }
             if (video && w == 0) {
-                // per key slot: frame (spatial) or packed (y << 16) | x
-                // (temporal); kNoKey past the sequence end
-                stage_c = video_key_word(r.k0 + lane, tm, pat, a);
+                // the tile's 64 key-coordinate words, copied from the head's
+                // table in the plan (frame, or (y << 16) | x; kNoKey past the end)
+                copy4_to_lds_s(ctab + r.k0, 4u * (uint32_t)lane, __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&kcoord[buf][0]));
             }
         };
-        // publish a fetched tile: its copies have landed, its key coordinates stored
-        auto finish_tile = [&](int buf) {
-            if (video && w == 0) kcoord[buf][lane] = stage_c;
-            wait_copies();
-        };
+        // publish a fetched tile: its copies have landed
+        auto finish_tile = [&](int) { wait_copies(); };
 
         // prologue: tile 0 into buffer 0
         if (gather) load_indices(rs.get(0), idx_nxt);

@@ -27,6 +27,7 @@ enum MaskMode : int32_t {
 // Per-head flags (kernel reads head_flags[h]).
 constexpr uint32_t kHeadTemporalMajor = 1u;   // bit 0: logical j = p*T + t
 constexpr uint32_t kHeadPatShift = 1;         // bits 1..2: video pattern
+constexpr uint32_t kHeadCoordShift = 3;       // bits 3..4: video key-coordinate table of the head
 
 struct Task {        // 16 bytes
     int32_t bh;      // b * H + h; -1 = no-op padding task
@@ -46,7 +47,9 @@ struct KernelArgs {
     const TileRec *tiles;
     const int32_t *gidx;
     const uint32_t *head_flags;
+    const int32_t *coords;     // video key-coordinate tables, coords_stride words each
     int32_t ntasks;
+    int32_t coords_stride;     // padded to whole 64-key tiles
     int32_t H;
     int32_t L;
     int32_t T, HW, W;          // video geometry (0 if unused)
