@@ -143,7 +143,7 @@ def cpu_baseline(w, Q, K, V, P_total, rows_per_head):
     ms_per_call = dt * 1e3 * P_total / P_sample
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {"value": ms_per_call, "unit": "ms", "cores": cores, "kind": "oracle",
-            "sample": f"{rows.size} random query rows ({rows_per_head} per head, all 24 heads), {P_sample} kept pairs "
+            "sample": f"{rows.size} random query rows ({rows_per_head} per head, all {w.H} heads), {P_sample} kept pairs "
                       f"in {dt:.2f} s, scaled by total/sampled kept pairs ({P_total}/{P_sample})",
             "effective_gflops": 4 * w.d * P_sample / dt / 1e9}
 
@@ -153,7 +153,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-rows-per-head", type=int, default=512)
+    ap.add_argument("--cpu-rows-per-head", type=int, default=12000,
+                    help="oracle rows per head for the CPU baseline (about 10 s of CPU work by default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--runs", default="A,B", help="comma list of runs to time (the headline needs B)")
