@@ -496,7 +496,11 @@ static void map_block_head(const bsa_plan_s &p, const bsa_mask_desc_t &m, int b,
 // VIDEO masks: for each query tile, classify the key tiles of a candidate
 // superset derived from the pattern (frames of the query tile and the anchor
 // frame; key pixels within the window of the query pixels); every tile outside
-// it is provably empty. Candidates are classified exactly.
+// it is provably empty. Candidates are classified exactly. A PARTIAL tile is
+// classified again for each wave's rows, with the same exact-safe test: a wave
+// none of whose pairs is kept skips the tile, a wave all of whose pairs are
+// kept runs it unmasked (Splash Attention's empty-tile skip and boundary-only
+// masking, applied at the granularity one wavefront computes).
 static void map_video_head(const bsa_plan_s &p, int b, int h, int BQ, HeadOut &out)
 {
     const int64_t L = p.L;
@@ -513,6 +517,9 @@ static void map_video_head(const bsa_plan_s &p, int b, int h, int BQ, HeadOut &o
         if (pat == BSA_PAT_TEMPORAL) pixel_rects(g, tm, k0, k1 - 1, ks[tk].r);
     }
     VideoTileSets qs;
+    const int NWV = BQ / kWaveRows;
+    VideoTileSets qw[8];                            // per-wave query sets (NWV <= 8)
+    int64_t qw_rows[8];
     std::vector<std::pair<int64_t, int64_t>> cand;  // key-tile index ranges [t0, t1]
     auto add_keys = [&](int64_t lo, int64_t hi) {   // key positions [lo, hi]
         lo = std::max<int64_t>(lo, 0);
@@ -525,6 +532,13 @@ static void map_video_head(const bsa_plan_s &p, int b, int h, int BQ, HeadOut &o
         const int64_t q0 = tq * BQ, q1 = std::min<int64_t>(q0 + BQ, L);
         if (pat == BSA_PAT_SPATIAL) qs.f = frames_of(g, tm, q0, q1 - 1);
         if (pat == BSA_PAT_TEMPORAL) pixel_rects(g, tm, q0, q1 - 1, qs.r);
+        for (int wv = 0; wv < NWV; ++wv) {
+            const int64_t a = q0 + (int64_t)kWaveRows * wv, e = std::min<int64_t>(a + kWaveRows, q1);
+            qw_rows[wv] = e - a;
+            if (e <= a) continue;
+            if (pat == BSA_PAT_SPATIAL) qw[wv].f = frames_of(g, tm, a, e - 1);
+            if (pat == BSA_PAT_TEMPORAL) pixel_rects(g, tm, a, e - 1, qw[wv].r);
+        }
         cand.clear();
         if (pat == BSA_PAT_SPATIAL && !tm) {
             const int64_t fa = q0 / HW, fb = (q1 - 1) / HW;
@@ -553,9 +567,19 @@ static void map_video_head(const bsa_plan_s &p, int b, int h, int BQ, HeadOut &o
         for (const auto &c : cand) {
             for (int64_t tk = std::max(c.first, last + 1); tk <= c.second; ++tk) {
                 const int64_t k0 = tk * kTileK;
-                int cl = classify_video(pat, p.anchor, p.radius, qs, ks[tk], k0 + kTileK > L);
+                const bool crop = k0 + kTileK > L;
+                int cl = classify_video(pat, p.anchor, p.radius, qs, ks[tk], crop);
                 if (cl == kEmpty) continue;
-                out.tiles.push_back({(int32_t)k0, cl == kFull ? 0u : kPartial});
+                uint32_t aux = 0;
+                if (cl == kPart) {
+                    aux = kPartial;
+                    for (int wv = 0; wv < NWV; ++wv) {
+                        const int wc = qw_rows[wv] <= 0 ? kEmpty : classify_video(pat, p.anchor, p.radius, qw[wv], ks[tk], crop);
+                        if (wc == kEmpty) aux |= 1u << wv;
+                        if (wc == kFull) aux |= 1u << (kWaveFullShift + wv);
+                    }
+                }
+                out.tiles.push_back({(int32_t)k0, aux});
                 if (cl == kFull) ++out.full; else ++out.part;
             }
             last = std::max(last, c.second);
@@ -1295,6 +1319,19 @@ extern "C" int32_t bsa_plan_coverage(bsa_plan_t p, int32_t b, int32_t h, bsa_cov
                 rec.sub_bits = r.aux & kAuxMask;
                 rec.sub_q = p->sub_q;
                 rec.sub_k = p->sub_k;
+            }
+            if (p->mode == kModeVideo && (r.aux & kPartial)) {
+                // one record per wave that runs the tile: FULL or PARTIAL rows
+                rec.sub_bits = 0;
+                const int64_t tq1 = rec.q1;
+                for (int wv = 0; wv < R.tile_q / kWaveRows; ++wv) {
+                    rec.q0 = t.q0 + (int64_t)kWaveRows * wv;
+                    rec.q1 = std::min<int64_t>(rec.q0 + kWaveRows, tq1);
+                    if (rec.q0 >= rec.q1 || ((r.aux >> wv) & 1u)) continue;
+                    rec.kind = ((r.aux >> (kWaveFullShift + wv)) & 1u) ? BSA_TILE_FULL : BSA_TILE_PARTIAL;
+                    if (sink(user, &rec)) return BSA_OK;
+                }
+                continue;
             }
             if (sink(user, &rec)) return BSA_OK;
         }

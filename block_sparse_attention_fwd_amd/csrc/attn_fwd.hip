@@ -308,6 +308,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1
                 if (gather && j + 2 < ntile) load_indices(rs.get(j + 2), idx_nxt);
             }
 
+            // A PARTIAL tile may keep no pair of this wave's rows: the wave
+            // skips it (and still takes its part in the copies and barriers)
+            if (!wave_skips_tile(a, rec.aux, w)) {
             // ---- S^T = K Q^T: s0 = keys 0..31, s1 = keys 32..63 of each row block
             const unsigned char *kt = ksm[cur];
             f32x16 s0[RB], s1[RB];
@@ -331,7 +334,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1
             __builtin_amdgcn_sched_group_barrier(0x008, 4 * RB, 0);
 
             // ---- exact mask on PARTIAL tiles only
-            if (rec.aux & kPartial) mask_partial_tile<RB>(s0, s1, a, rec.k0, rec.aux, video, pat, LDS_PTR(const int, &kcoord[cur][4 * hf]), qt, qwin, q, task.q0, hf);
+            if (wave_masks_tile(a, rec.aux, w)) mask_partial_tile<RB>(s0, s1, a, rec.k0, rec.aux, video, pat, LDS_PTR(const int, &kcoord[cur][4 * hf]), qt, qwin, q, task.q0, hf);
 
             // ---- online softmax per row block
             u32x4 pk[RB][4];  // bf16 pairs, one cvt_pk each
@@ -396,6 +399,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
             }
             __builtin_amdgcn_sched_group_barrier(0x008, 2 * RB, 1);
+            }
 
             if (more) finish_tile(cur ^ 1);
             __syncthreads();

@@ -108,6 +108,8 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_f32(KernelArgs a)
             if (video && tid < BK) kcoord[tid] = video_key_word(rec.k0 + tid, tm, pat, a);
             __syncthreads();
 
+            // a PARTIAL tile may keep no pair of this wave's rows
+            if (wave_skips_tile(a, rec.aux, w)) continue;
             // ---- S^T = K Q^T for keys 0..31 (s0) and 32..63 (s1)
             f32x16 s0[1], s1[1];
             s0[0] = zero16;
@@ -122,7 +124,7 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_f32(KernelArgs a)
             }
 
             // ---- exact mask on PARTIAL tiles only
-            if (rec.aux & kPartial)
+            if (wave_masks_tile(a, rec.aux, w))
                 mask_partial_tile<1>(s0, s1, a, rec.k0, rec.aux, video, pat, LDS_PTR(const int, &kcoord[4 * hf]), qt,
                                      qwin, q, task.q0, hf);
 

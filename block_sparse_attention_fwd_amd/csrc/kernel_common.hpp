@@ -138,6 +138,30 @@ struct RecordStream {
     }
 };
 
+// Per-wave refinement of a PARTIAL tile for wave w (query rows 32w..32w+31 of
+// the task); both are wave-uniform.
+//  - skip: the wave's rows keep no pair of the tile. Video tiles carry the bit
+//    from the plan; block tiles whose sub-block rows are at least 32 queries
+//    tall read it from the sub-block keep bits of the wave's sub-block row.
+//  - mask: the wave's rows need the exact predicate (video tiles carry a bit
+//    for rows that keep every pair).
+__device__ __forceinline__ bool wave_skips_tile(const KernelArgs &a, uint32_t aux, int w)
+{
+    if (!(aux & kPartial)) return false;
+    if (a.mode == kModeVideo) return (aux >> w) & 1u;
+    if (a.mode == kModeBlock && a.bq_shift >= 5) {
+        const int sq = (kWaveRows * w) >> a.bq_shift;
+        return ((aux >> (sq * a.nsk)) & ((1u << a.nsk) - 1u)) == 0u;
+    }
+    return false;
+}
+__device__ __forceinline__ bool wave_masks_tile(const KernelArgs &a, uint32_t aux, int w)
+{
+    if (!(aux & kPartial)) return false;
+    if (a.mode == kModeVideo) return !((aux >> (kWaveFullShift + w)) & 1u);
+    return true;
+}
+
 // Exact predicate of a PARTIAL 64-key tile (Sparse VideoGen / Splash
 // Attention summary, "Splash Attention": exact coordinate masking on boundary
 // tiles only). s0 / s1 are the scores of keys 0..31 / 32..63 of each 32-row

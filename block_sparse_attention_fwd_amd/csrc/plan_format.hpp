@@ -16,6 +16,12 @@ namespace bsa {
 constexpr int kTileK = 64;         // keys per physical key tile
 constexpr uint32_t kPartial = 0x80000000u;
 constexpr uint32_t kAuxMask = 0x0000FFFFu;
+// Video PARTIAL tiles refine their class per wave (a wave owns kWaveRows
+// consecutive query rows of the tile): aux bit w set = wave w keeps no pair
+// of the tile and skips it; bit kWaveFullShift + w set = wave w keeps every
+// pair of the tile and runs it without the mask.
+constexpr int kWaveRows = 32;
+constexpr int kWaveFullShift = 8;
 
 // Which predicate PARTIAL tiles evaluate.
 enum MaskMode : int32_t {
@@ -37,7 +43,7 @@ struct Task {        // 16 bytes
 
 struct TileRec {     // 8 bytes
     int32_t k0;      // first logical key (tile families) or offset into gidx (gather)
-    uint32_t aux;    // kPartial | sub-block bits (block) | valid count (gather)
+    uint32_t aux;    // kPartial | sub-block bits (block) | valid count (gather) | per-wave bits (video)
 };
 
 struct KernelArgs {

@@ -146,7 +146,9 @@ typedef struct {
 
 /* One physical tile of a plan, as computed by the device (test hook for
  * checking that a plan covers every kept pair exactly once). Positions are
- * logical positions of the head. */
+ * logical positions of the head. A video PARTIAL tile is reported once per
+ * wavefront (32 query rows) that computes it, each as FULL or PARTIAL for those
+ * rows; wavefronts that keep no pair of the tile skip it and report nothing. */
 enum { BSA_TILE_FULL = 0, BSA_TILE_PARTIAL = 1 };
 enum { BSA_PRED_NONE = 0, BSA_PRED_SUBBLOCK = 1, BSA_PRED_VIDEO = 2, BSA_PRED_LIST = 3 };
 typedef struct {

@@ -90,7 +90,7 @@ def small_cases():
 
 
 @pytest.mark.parametrize("w", small_cases(), ids=lambda w: w.name)
-@pytest.mark.parametrize("regime", [-1, 0, 1])
+@pytest.mark.parametrize("regime", [-1, 0, 1, 4])
 def test_plan_covers_each_kept_pair_once(w, regime):
     if w.kind == wl.SLICE:
         regime = -1  # slices run only in the gather regime matching M
@@ -101,6 +101,31 @@ def test_plan_covers_each_kept_pair_once(w, regime):
             want = expected(w, b, h)
             bad = np.argwhere(got != want)
             assert bad.size == 0, f"{w.name} h{h}: {len(bad)} pairs wrong, first {bad[:5].tolist()}"
+
+
+@pytest.mark.parametrize("regime", [0, 1, 4])
+def test_video_records_are_tight(regime):
+    """Video plans at wavefront granularity: every record the device computes
+    (whole FULL tiles, and each wavefront's 32 rows of a PARTIAL tile) keeps at
+    least one pair; FULL records keep all of theirs; a PARTIAL record whose
+    keys lie inside the sequence keeps some but not all. So no wavefront runs a
+    tile that holds nothing for its rows, and none masks rows it need not."""
+    n_wave_records = 0
+    for w in [c for c in small_cases() if c.kind == wl.VIDEO]:
+        p = plan_workload(w, device=-1, force_regime=regime)
+        tok_tm = tok_of_logical(w.T, w.Hg * w.Wg)
+        for h in range(w.H):
+            tok = tok_tm if w.layout()[h] == wl.TEMPORAL_MAJOR else np.arange(w.L)
+            em = element_mask(w, 0, h)
+            for r in p.coverage(0, h):
+                kept = em[np.ix_(tok[r["q0"]:r["q1"]], tok[r["k0"]:r["k1"]])]
+                assert kept.any(), (w.name, h, r)
+                if r["kind"] == bsa.TILE_FULL:
+                    assert kept.all(), (w.name, h, r)
+                elif r["k1"] - r["k0"] == 64:
+                    assert not kept.all(), (w.name, h, r)
+                n_wave_records += r["q1"] - r["q0"] <= 32
+    assert n_wave_records > 0
 
 
 def test_block_bits_and_u8_give_the_same_plan():
@@ -156,11 +181,12 @@ def test_svg_plan_exact_on_sampled_query_tiles():
                 qs = tok[q0:min(q0 + tq, w.L)]
                 cnt = np.zeros((qs.size, w.L), np.uint16)
                 for r in recs:
-                    if r["q0"] != q0:
+                    if not (q0 <= r["q0"] < q0 + tq):
                         continue
+                    rows = slice(r["q0"] - q0, r["q1"] - q0)
                     ks = tok[r["k0"]:r["k1"]]
                     if r["kind"] == bsa.TILE_FULL:
-                        cnt[:, ks] += 1
+                        cnt[rows, ks] += 1
                     else:
-                        cnt[:, ks] += em[np.ix_(qs, ks)]
+                        cnt[rows, ks] += em[np.ix_(qs[rows], ks)]
                 assert np.array_equal(cnt, em[qs].astype(np.uint16)), (run, h, q0)
