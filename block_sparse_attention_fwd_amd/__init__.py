@@ -28,6 +28,8 @@ LAYOUT_FRAME_MAJOR, LAYOUT_TEMPORAL_MAJOR = 0, 1
 DTYPE_BF16, DTYPE_F32 = 0, 1
 TILE_FULL, TILE_PARTIAL = 0, 1
 PRED_NONE, PRED_SUBBLOCK, PRED_VIDEO, PRED_LIST = 0, 1, 2, 3
+ORDER_XCD_QUEUES, ORDER_LONGEST_FIRST = 0, 1
+ABI_VERSION = 2  # the structures below mirror this version of bsa.h
 
 EXPORTED = ["bsa_abi_version", "bsa_plan_opts_default", "bsa_plan", "bsa_forward", "bsa_plan_destroy",
             "bsa_plan_info", "bsa_plan_coverage", "bsa_regime_count", "bsa_regime_info", "bsa_status_str",
@@ -43,7 +45,7 @@ class MaskDesc(ctypes.Structure):
 class PlanOpts(ctypes.Structure):
     _fields_ = [("dtype", ctypes.c_int32), ("T", ctypes.c_int32), ("Hg", ctypes.c_int32), ("Wg", ctypes.c_int32),
                 ("head_layout", ctypes.c_void_p), ("force_regime", ctypes.c_int32), ("lut_path", ctypes.c_char_p),
-                ("device", ctypes.c_int32)]
+                ("device", ctypes.c_int32), ("task_order", ctypes.c_int32)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -52,7 +54,7 @@ class PlanInfo(ctypes.Structure):
                 ("tiles_full", ctypes.c_int64),
                 ("tiles_partial", ctypes.c_int64), ("tiles_empty", ctypes.c_int64), ("gather_rows", ctypes.c_int64),
                 ("executed_pairs", ctypes.c_double), ("device_bytes", ctypes.c_int64), ("plan_ns", ctypes.c_int64),
-                ("phase_ns", ctypes.c_int64 * 5)]
+                ("phase_ns", ctypes.c_int64 * 5), ("task_order", ctypes.c_int32), ("queues", ctypes.c_int32)]
 
     def as_dict(self):
         d = {k: getattr(self, k) for k, _ in self._fields_}
@@ -94,6 +96,8 @@ def lib(path: str = LIB_PATH):
         pass
     L = ctypes.CDLL(path)
     L.bsa_abi_version.restype = ctypes.c_int32
+    if L.bsa_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{path}: ABI version {L.bsa_abi_version()}, the binding expects {ABI_VERSION}")
     L.bsa_plan_opts_default.argtypes = [ctypes.POINTER(PlanOpts)]
     L.bsa_plan.restype = ctypes.c_int32
     L.bsa_plan.argtypes = [ctypes.POINTER(MaskDesc), ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
@@ -184,7 +188,7 @@ class Plan:
 def plan(kind: int, B: int, H: int, L: int, d: int, block_q: int, block_k: int, *, data=None, row_ptr=None,
          col_idx=None, head_pattern=None, anchor_frame: int = 0, radius: int = 2, dtype: int = DTYPE_BF16,
          T: int = 0, Hg: int = 0, Wg: int = 0, head_layout=None, force_regime: int = -1,
-         lut_path: Optional[str] = None, device: int = 0) -> Plan:
+         lut_path: Optional[str] = None, device: int = 0, task_order: int = -1) -> Plan:
     """bsa_plan: build a plan for a logical mask (host numpy arrays)."""
     L_ = lib()
     keep = []
@@ -212,6 +216,7 @@ def plan(kind: int, B: int, H: int, L: int, d: int, block_q: int, block_k: int, 
     o.force_regime = force_regime
     o.lut_path = lut_path.encode() if lut_path else None
     o.device = device
+    o.task_order = task_order
     h = ctypes.c_void_p()
     _check(L_.bsa_plan(ctypes.byref(m), B, H, L, d, block_q, block_k, ctypes.byref(o), ctypes.byref(h)))
     return Plan(h.value, L, H, B)

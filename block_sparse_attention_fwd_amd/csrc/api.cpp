@@ -117,14 +117,16 @@ extern "C" int32_t bsa_regime_info(int32_t r, bsa_regime_desc_t *out)
 }
 
 // Lookup-table rule: first matching line wins. Fields:
-//   kind block_q block_k density_lo density_hi L_lo L_hi regime
-// kind is block|slice|video; block sizes may be '*'.
+//   kind block_q block_k density_lo density_hi L_lo L_hi regime [order]
+// kind is block|slice|video; block sizes may be '*'; order is xcd (the
+// default) or lpt (BSA_ORDER_*).
 struct LutRule {
     int kind;  // BSA_MASK_BLOCK_U8 (both block kinds), SLICE, VIDEO
     int bq, bk;  // 0 = any
     double dlo, dhi;
     int64_t Llo, Lhi;
     int regime;
+    int order;
 };
 
 #include "lut_default.inc"  // defines kDefaultLut (text of lut/gfx950.lut)
@@ -150,6 +152,12 @@ static bool parse_lut(const std::string &text, std::vector<LutRule> &rules, std:
         else if (kind == "slice") r.kind = BSA_MASK_SLICE_CSR;
         else if (kind == "video") r.kind = BSA_MASK_VIDEO;
         else { err = "lookup table line " + std::to_string(ln) + ": unknown kind " + kind; return false; }
+        std::string order;
+        r.order = BSA_ORDER_XCD_QUEUES;
+        if (ls >> order) {
+            if (order == "lpt") r.order = BSA_ORDER_LONGEST_FIRST;
+            else if (order != "xcd") { err = "lookup table line " + std::to_string(ln) + ": unknown order " + order; return false; }
+        }
         r.bq = bq == "*" ? 0 : std::atoi(bq.c_str());
         r.bk = bk == "*" ? 0 : std::atoi(bk.c_str());
         if (r.regime < 0 || r.regime >= kNumRegimes) {
@@ -179,17 +187,19 @@ struct bsa_plan_s {
     int32_t T = 0, Hg = 0, Wg = 0, anchor = 0, radius = 0;
     int32_t bq_shift = 0, bk_shift = 0, nsk = 1, sub_q = 0, sub_k = 0;
     int32_t mode = 0;
-    int32_t task_order = 1;  // 0 = XCD segments, 1 = longest first, 2 = longest first in XCD blocks
+    int32_t task_order = 0;  // 0 = one queue per XCD, 1 = one longest-first queue
+    int32_t nqueues = 1;
+    uint32_t launch_seq = 0;  // launches so far (counter slot rotation)
     std::vector<uint8_t> head_layout, head_pattern;
     // image
     uint8_t *img = nullptr;
     size_t img_cap = 0, img_bytes = 0;
     bool img_pinned = false;
     std::vector<uint8_t> img_vec;
-    size_t off_tasks = 0, off_tiles = 0, off_gidx = 0, off_flags = 0, off_coords = 0;
+    size_t off_tasks = 0, off_tiles = 0, off_gidx = 0, off_flags = 0, off_coords = 0, off_queues = 0, off_ctr = 0;
     int64_t coord_stride = 0;                   // words per video key-coordinate table
     std::vector<uint8_t> head_coord_table;      // per head: index of its table
-    int64_t ntasks = 0, ntiles = 0, ngidx = 0;  // ntasks: launched workgroups (incl. padding)
+    int64_t ntasks = 0, ntiles = 0, ngidx = 0;  // ntasks: tasks in the task array
     int64_t nreal_tasks = 0;                    // one per (batch, head, query tile)
     const Task *tasks() const { return (const Task *)(img + off_tasks); }
     const TileRec *tiles() const { return (const TileRec *)(img + off_tiles); }
@@ -644,6 +654,8 @@ static int32_t validate(const bsa_mask_desc_t *m, int32_t B, int32_t H, int64_t 
     }
     if (o.force_regime < -1 || o.force_regime >= kNumRegimes)
         return fail(BSA_ERR_INVALID_ARGUMENT, "force_regime %d out of range", o.force_regime);
+    if (o.task_order < -1 || o.task_order > BSA_ORDER_LONGEST_FIRST)
+        return fail(BSA_ERR_INVALID_ARGUMENT, "task_order %d out of range", o.task_order);
     switch (m->kind) {
     case BSA_MASK_BLOCK_U8:
     case BSA_MASK_BLOCK_BITS:
@@ -737,9 +749,10 @@ static double mask_density(const bsa_mask_desc_t &m, int32_t B, int32_t H, int64
 }
 
 static int32_t choose_regime(const bsa_mask_desc_t &m, int32_t B, int32_t H, int64_t L, int32_t bq, int32_t bk,
-                             const bsa_plan_opts_t &o, int *regime)
+                             const bsa_plan_opts_t &o, int *regime, int *order)
 {
-    if (o.force_regime >= 0) {
+    *order = BSA_ORDER_XCD_QUEUES;
+    if (o.force_regime >= 0 && o.task_order >= 0) {
         *regime = o.force_regime;
     } else {
         std::vector<LutRule> rules;
@@ -762,10 +775,13 @@ static int32_t choose_regime(const bsa_mask_desc_t &m, int32_t B, int32_t H, int
             if (dens >= 0 && (dens < r.dlo || dens > r.dhi)) continue;
             if (L < r.Llo || L > r.Lhi) continue;
             *regime = r.regime;
+            *order = r.order;
             break;
         }
         if (*regime < 0) *regime = m.kind == BSA_MASK_SLICE_CSR ? (bq == 128 ? 3 : 2) : 0;
+        if (o.force_regime >= 0) *regime = o.force_regime;
     }
+    if (o.task_order >= 0) *order = o.task_order;
     const Regime &R = kRegimes[*regime];
     const bool slice = m.kind == BSA_MASK_SLICE_CSR;
     if (slice != (R.family == 1))
@@ -846,27 +862,86 @@ size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // One task per (batch, head, query tile) -- also for query tiles without any
 // key tile, so that every output row is written. The heads' outputs are
-// copied in parallel into the plan image, then ordered for the device:
-//  - XCD order (BSA_TASK_ORDER=xcd): workgroup i of a launch runs on XCD i % X (X = 8 on
-//    MI355X), each XCD with its own L2. Tasks in (head, query tile) order --
-//    neighbouring query tiles share most of their key tiles -- are cut into X
-//    contiguous segments of equal tile count (plus one per task), and slot
-//    i*X + x of the launch takes task i of segment x, so each XCD streams one
-//    contiguous piece of the key space through its L2. Segments shorter than
-//    the longest are padded with no-op tasks (bh = -1).
-//  - LPT order (default): longest task first (a stable counting sort on the tile
-//    count), so the tail of the grid holds the cheapest work.
-static int cu_count(int device)
-{
-    int n = 256;
-    if (device >= 0 && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) n = 256;
-    return std::max(1, n);
-}
-
+// copied in parallel into the plan image, then ordered for the device, whose
+// workgroups draw their tasks from queues (one per XCD by default):
+//  - XCD queues (default): the tasks of a head, in query-tile order, are cut
+//    into chunks of consecutive query tiles, which share most of their key
+//    tiles; the chunks are dealt, most expensive per task first, to the queue
+//    with the least estimated work so far. A workgroup serves the queue of
+//    its own XCD (each XCD has its own L2), so a chunk's tasks run on one XCD
+//    at about the same time; every queue runs its costly tasks first and its
+//    cheap ones last, so that the workgroups run out of work together, and a
+//    workgroup whose queue is empty takes tasks from the others.
+//  - One queue in longest-first order (BSA_TASK_ORDER=lpt): a stable counting
+//    sort on the tile count, so the tail of the run holds the cheapest work.
 static int xcd_count()
 {
     if (const char *e = std::getenv("BSA_XCDS")) return std::max(1, std::atoi(e));
     return 8;
+}
+
+// Chunks of a head's tasks in query-tile order: [first task, count,
+// estimated cost]. 64 tasks are about what one XCD runs at once (32 compute
+// units, two workgroups each), so the tasks running together on an XCD are
+// mostly neighbouring query tiles of one head.
+constexpr int64_t kChunkTasks = 64;
+struct QChunk {
+    int64_t first, n, cost;
+};
+
+// Deal the chunks, most expensive per task first, each to the queue with the
+// least estimated work so far; a queue's chunks stay in the order dealt.
+static void deal_chunks(const bsa_plan_s &p, std::vector<QChunk> &chunks, const std::vector<Task> &unsorted, Task *tasks,
+                        int32_t *queues)
+{
+    const int NQ = p.nqueues;
+    // most expensive per task first; ties keep (head, query tile) order
+    std::stable_sort(chunks.begin(), chunks.end(),
+                     [](const QChunk &a, const QChunk &b) { return a.cost * b.n > b.cost * a.n; });
+    std::vector<std::vector<int32_t>> own(NQ);
+    std::vector<int64_t> load(NQ, 0), len(NQ, 0);
+    for (size_t c = 0; c < chunks.size(); ++c) {
+        int x = 0;
+        for (int y = 1; y < NQ; ++y)
+            if (load[y] < load[x]) x = y;
+        load[x] += chunks[c].cost;
+        len[x] += chunks[c].n;
+        own[x].push_back((int32_t)c);
+    }
+    int64_t pos = 0;
+    for (int x = 0; x < NQ; ++x) {
+        queues[2 * x] = (int32_t)pos;
+        queues[2 * x + 1] = (int32_t)len[x];
+        for (int32_t c : own[x])
+            for (int64_t k = 0; k < chunks[c].n; ++k) tasks[pos++] = unsorted[(size_t)(chunks[c].first + k)];
+    }
+}
+
+static void order_xcd_queues(const bsa_plan_s &p, const std::vector<int64_t> &t_off, const std::vector<Task> &unsorted,
+                             Task *tasks, int32_t *queues)
+{
+    const TileRec *tiles = (const TileRec *)(p.img + p.off_tiles);
+    const int64_t G = kChunkTasks;
+    const size_t nh = t_off.size() - 1;
+    // The estimated cost is in tenths of a FULL tile: 80 per task (query
+    // load, first copy, epilogue), 10 per FULL tile, 14 per PARTIAL tile
+    // (mask, partly skipped waves).
+    std::vector<int64_t> c_off(nh + 1, 0);
+    for (size_t i = 0; i < nh; ++i) c_off[i + 1] = c_off[i] + (t_off[i + 1] - t_off[i] + G - 1) / G;
+    std::vector<QChunk> chunks((size_t)c_off[nh]);
+    parallel_for((int64_t)nh, [&](int64_t i) {
+        int64_t c = c_off[i];
+        for (int64_t s0 = t_off[i]; s0 < t_off[i + 1]; s0 += G, ++c) {
+            QChunk ch{s0, std::min(G, t_off[i + 1] - s0), 0};
+            for (int64_t k = ch.first; k < ch.first + ch.n; ++k) {
+                const Task &t = unsorted[(size_t)k];
+                ch.cost += 80;
+                for (int32_t r = t.tb; r < t.te; ++r) ch.cost += (tiles[r].aux & kPartial) ? 14 : 10;
+            }
+            chunks[(size_t)c] = ch;
+        }
+    });
+    deal_chunks(p, chunks, unsorted, tasks, queues);
 }
 
 static int32_t organise_tasks(bsa_plan_s &p, const std::vector<HeadOut *> &heads)
@@ -888,51 +963,17 @@ static int32_t organise_tasks(bsa_plan_s &p, const std::vector<HeadOut *> &heads
     const int64_t nreal = t_off[nh];
     p.ntiles = r_off[nh];
     p.ngidx = g_off[nh];
-    // XCD segments over the locality-ordered tasks (computed from the per-head
-    // lists before they are copied)
-    const int X = p.task_order == 0 ? xcd_count() : 1;
-    std::vector<int64_t> seg_start(X + 1, nreal);
-    seg_start[0] = 0;
-    int64_t seg_len = nreal;
-    if (X > 1 && nreal > 0) {
-        int64_t total = 0;
-        for (size_t i = 0; i < nh; ++i)
-            for (const Task &t : heads[i]->tasks) total += (t.te - t.tb) + 1;
-        int64_t acc = 0, idx = 0;
-        int x = 1;
-        for (size_t i = 0; i < nh && x < X; ++i)
-            for (const Task &t : heads[i]->tasks) {
-                acc += (t.te - t.tb) + 1;
-                ++idx;
-                while (x < X && acc * X >= total * x) seg_start[x++] = idx;
-            }
-        while (x < X) seg_start[x++] = nreal;
-        seg_len = 0;
-        for (int k = 0; k < X; ++k) seg_len = std::max(seg_len, seg_start[k + 1] - seg_start[k]);
-    }
-    // XCD blocks of the longest-first order: the order is cut into blocks of
-    // G tasks (one round of the XCD's workgroup slots), and block b runs on
-    // XCD b % X, so each XCD works through a contiguous piece of the order --
-    // tasks of similar length, adjacent in (head, query tile), sharing key
-    // tiles in that XCD's L2 -- and every XCD gets blocks of all lengths.
-    const int XB = p.task_order == 2 ? xcd_count() : 1;
-    const int64_t G = std::max<int64_t>(1, 2 * (int64_t)cu_count(p.device) / std::max(1, XB));
-    int64_t blk_len = 0;
-    if (XB > 1) {
-        const int64_t nb = (nreal + G - 1) / G;
-        for (int x = 0; x < XB; ++x) {
-            int64_t len = 0;
-            for (int64_t b = x; b < nb; b += XB) len += std::min(G, nreal - b * G);
-            blk_len = std::max(blk_len, len);
-        }
-    }
-    p.ntasks = X > 1 ? seg_len * X : (XB > 1 ? blk_len * XB : nreal);
+    p.ntasks = nreal;
     p.nreal_tasks = nreal;
     p.off_tasks = 0;
     p.off_tiles = align_up(std::max<int64_t>(1, p.ntasks) * sizeof(Task));
     p.off_gidx = p.off_tiles + align_up(std::max<int64_t>(1, p.ntiles) * sizeof(TileRec));
     p.off_flags = p.off_gidx + align_up(std::max<int64_t>(1, p.ngidx) * sizeof(int32_t));
     p.off_coords = p.off_flags + align_up((size_t)p.H * sizeof(uint32_t));
+    p.nqueues = p.task_order == 0 ? std::min(kMaxQueues, xcd_count()) : 1;
+    p.off_queues = p.off_coords;  // (coordinate tables follow the queue table and the counters)
+    p.off_ctr = p.off_queues + align_up((size_t)kMaxQueues * 2 * sizeof(int32_t));
+    p.off_coords = p.off_ctr + align_up((size_t)kCtrSlots * kCtrWords * sizeof(uint32_t));
     // video masks: one key-coordinate table per (pattern, layout) pair the heads use
     int ntables = 0;
     int table_of[3][2] = {{-1, -1}, {-1, -1}, {-1, -1}};
@@ -979,32 +1020,19 @@ static int32_t organise_tasks(bsa_plan_s &p, const std::vector<HeadOut *> &heads
         if (!h.gidx.empty()) std::memcpy(gidx + g_off[i], h.gidx.data(), h.gidx.size() * sizeof(int32_t));
     });
     Task *tasks = (Task *)(p.img + p.off_tasks);
-    if (X > 1) {
-        const Task noop{-1, 0, 0, 0};
-        for (int x = 0; x < X; ++x)
-            for (int64_t i = 0; i < seg_len; ++i) {
-                const int64_t src = seg_start[x] + i;
-                tasks[i * X + x] = src < seg_start[x + 1] ? unsorted[src] : noop;
-            }
+    int32_t *queues = (int32_t *)(p.img + p.off_queues);
+    std::memset(queues, 0, (size_t)kMaxQueues * 2 * sizeof(int32_t));
+    std::memset(p.img + p.off_ctr, 0, (size_t)kCtrSlots * kCtrWords * sizeof(uint32_t));
+    if (p.nqueues > 1) {
+        order_xcd_queues(p, t_off, unsorted, tasks, queues);
     } else {
         // stable LPT order: counting sort on the tile count, descending
         std::vector<int64_t> bucket((size_t)max_cost + 2, 0);
         for (const Task &t : unsorted) ++bucket[(size_t)(max_cost - (t.te - t.tb)) + 1];
         for (size_t c = 1; c < bucket.size(); ++c) bucket[c] += bucket[c - 1];
-        if (XB == 1) {
-            for (const Task &t : unsorted) tasks[bucket[(size_t)(max_cost - (t.te - t.tb))]++] = t;
-        } else {
-            std::vector<Task> lpt((size_t)nreal);
-            for (const Task &t : unsorted) lpt[bucket[(size_t)(max_cost - (t.te - t.tb))]++] = t;
-            const Task noop{-1, 0, 0, 0};
-            const int64_t nb = (nreal + G - 1) / G;
-            for (int x = 0; x < XB; ++x) {
-                int64_t k = 0;
-                for (int64_t b = x; b < nb; b += XB)
-                    for (int64_t i = b * G; i < std::min(nreal, (b + 1) * G); ++i) tasks[(k++) * XB + x] = lpt[i];
-                for (; k < blk_len; ++k) tasks[k * XB + x] = noop;
-            }
-        }
+        for (const Task &t : unsorted) tasks[bucket[(size_t)(max_cost - (t.te - t.tb))]++] = t;
+        queues[0] = 0;
+        queues[1] = (int32_t)nreal;
     }
     uint32_t *flags = (uint32_t *)(p.img + p.off_flags);
     for (int h = 0; h < p.H; ++h)
@@ -1118,6 +1146,7 @@ extern "C" void bsa_plan_opts_default(bsa_plan_opts_t *o)
     o->dtype = BSA_DTYPE_BF16;
     o->force_regime = -1;
     o->device = 0;
+    o->task_order = -1;
 }
 
 extern "C" int32_t bsa_plan(const bsa_mask_desc_t *logical_mask, int32_t B, int32_t H, int64_t L, int32_t d,
@@ -1139,8 +1168,8 @@ extern "C" int32_t bsa_plan(const bsa_mask_desc_t *logical_mask, int32_t B, int3
         t_ingest = now_ns();
         if (std::getenv("BSA_TEST_FAIL_ALLOC")) return fail(BSA_ERR_OUT_OF_MEMORY, "simulated allocation failure");
         const bsa_mask_desc_t &m = *logical_mask;
-        int regime = 0;
-        st = choose_regime(m, B, H, L, block_q, block_k, o, &regime);
+        int regime = 0, order = 0;
+        st = choose_regime(m, B, H, L, block_q, block_k, o, &regime, &order);
         if (st != BSA_OK) return st;
         t_regime = now_ns();
 
@@ -1151,8 +1180,7 @@ extern "C" int32_t bsa_plan(const bsa_mask_desc_t *logical_mask, int32_t B, int3
         p->T = o.T; p->Hg = o.Hg; p->Wg = o.Wg;
         p->anchor = m.anchor_frame; p->radius = m.radius;
         p->device = o.device;
-        if (const char *e = std::getenv("BSA_TASK_ORDER"))
-            p->task_order = std::strcmp(e, "xcd") == 0 ? 0 : (std::strcmp(e, "xcdlpt") == 0 ? 2 : 1);
+        p->task_order = order;
         p->head_layout.assign(H, 0);
         if (o.head_layout) p->head_layout.assign(o.head_layout, o.head_layout + H);
         p->head_pattern.assign(H, 0);
@@ -1244,6 +1272,12 @@ extern "C" int32_t bsa_forward(bsa_plan_t p, const void *Q, const void *K, const
     a.head_flags = (const uint32_t *)(dev + p->off_flags);
     a.coords = (const int32_t *)(dev + p->off_coords);
     a.coords_stride = (int32_t)p->coord_stride;
+    a.queues = (const int32_t *)(dev + p->off_queues);
+    a.nqueues = p->nqueues > 1 ? p->nqueues : 0;  // one queue: workgroup i runs task i
+    {
+        const uint32_t slot = __atomic_fetch_add(&p->launch_seq, 1u, __ATOMIC_RELAXED) % (uint32_t)kCtrSlots;
+        a.ctr = (uint32_t *)p->dev + p->off_ctr / sizeof(uint32_t) + (size_t)slot * kCtrWords;
+    }
     a.ntasks = (int32_t)p->ntasks;
     a.H = p->H;
     a.L = (int32_t)p->L;
@@ -1288,6 +1322,8 @@ extern "C" int32_t bsa_plan_info(bsa_plan_t p, bsa_plan_info_t *out)
     out->device_bytes = (int64_t)p->dev_cap;
     out->plan_ns = p->plan_ns;
     for (int i = 0; i < 5; ++i) out->phase_ns[i] = p->phase_ns[i];
+    out->task_order = p->task_order;
+    out->queues = p->nqueues;
     return BSA_OK;
 }
 

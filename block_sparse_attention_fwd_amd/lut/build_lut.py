@@ -11,7 +11,8 @@ writes the fastest regime of each bin as one rule of the table.
 
 Inputs are seeded and synthetic (workloads module): BLOCK masks in banded,
 local-window and random layouts, video head routing (half spatial heads,
-half temporal heads in temporal-major order), Q/K/V ~ N(0,1) in bf16.
+half temporal heads in temporal-major order), slice lists, Q/K/V ~ N(0,1) in
+bf16. Each bin's rule names the fastest (regime, task order) pair.
 
 Usage (on the target GPU, from the repository root):
     python3 block_sparse_attention_fwd_amd/lut/build_lut.py [--out lut/gfx950.lut] [--quick]
@@ -32,6 +33,7 @@ import numpy as np  # noqa: E402
 
 TILE_REGIMES = (0, 1, 4)        # contiguous-tile regimes (block and video masks)
 SLICE_RULES = ((64, 2), (128, 3))  # slice masks: the gather regime of the slice height
+ORDERS = ((0, "xcd"), (1, "lpt"))  # task orders (BSA_ORDER_*) and their table names
 # sequence-length bins: (representative token grid T x Hg x Wg, L range of the rule)
 LENGTH_BINS = (
     ((4, 32, 32), (0, 8192)),
@@ -47,16 +49,24 @@ def log(*a):
     print(*a, flush=True)
 
 
+def oname(order):
+    return dict(ORDERS)[order]
+
+
+def vname(x):
+    return f"r{x[0]}/{oname(x[1])}"
+
+
 def time_regimes(bsa, torch, w, regimes, q, k, v, o, reps, rounds=3):
-    """Median forward time (ms) of each regime on workload w. The regimes are
-    timed in interleaved rounds, so that clock and thermal drift during the
-    sweep falls on all of them alike."""
+    """Median forward time (ms) of each (regime, task order) variant on
+    workload w. The variants are timed in interleaved rounds, so that clock
+    and thermal drift during the sweep falls on all of them alike."""
     from bsa_helpers import plan_workload
-    plans = {r: plan_workload(w, force_regime=r) for r in regimes}
+    plans = {(r, od): plan_workload(w, force_regime=r, task_order=od) for r in regimes for od, _ in ORDERS}
     try:
-        times = {r: [] for r in regimes}
+        times = {v: [] for v in plans}
         for _ in range(rounds):
-            for r in regimes:
+            for r in plans:
                 p = plans[r]
                 bsa.forward(p, q, k, v, o)
                 torch.cuda.synchronize()
@@ -94,7 +104,7 @@ def main():
     H, d = args.heads, 128
     length_bins = LENGTH_BINS[:2] if args.quick else LENGTH_BINS
     layouts = LAYOUTS[:1] if args.quick else LAYOUTS
-    rules, notes = [], []
+    rules, notes, slice_rules = [], [], []
     t_start = time.time()
     for (T, Hg, Wg), (llo, lhi) in length_bins:
         L = T * Hg * Wg
@@ -106,35 +116,46 @@ def main():
         wv = wl.svg("B", H=H, T=T, Hg=Hg, Wg=Wg, d=d, cfg=9)
         tv = time_regimes(bsa, torch, wv, TILE_REGIMES, q, k, v, o, args.reps)
         best = min(tv, key=tv.get)
-        log(f"[lut] video L={L}: " + ", ".join(f"r{r} {t:.4f} ms" for r, t in tv.items()) + f" -> {best}")
-        notes.append(f"video L={L}: " + " ".join(f"r{r}={t:.4f}ms" for r, t in tv.items()))
-        rules.append(f"video   *       *       -1         1          {llo:<4d} {lhi:<10d} {best}")
+        log(f"[lut] video L={L}: " + ", ".join(f"{vname(x)} {t:.4f} ms" for x, t in tv.items()) + f" -> {vname(best)}")
+        notes.append(f"video L={L}: " + " ".join(f"{vname(x)}={t:.4f}ms" for x, t in tv.items()))
+        rules.append(f"video   *       *       -1         1          {llo:<4d} {lhi:<10d} {best[0]} {oname(best[1])}")
         for (bq, bk) in BLOCK_SHAPES:
             for rho, (dlo, dhi) in DENSITY_BINS:
-                tot = {r: 0.0 for r in TILE_REGIMES}
+                tot = {}
                 for li, lay in enumerate(layouts):
                     w = wl.block_request(f"lut_{bq}x{bk}_{rho}_{lay}", 9, li, bq, bk, rho, lay, H, T, Hg, Wg, d)
-                    for r, t in time_regimes(bsa, torch, w, TILE_REGIMES, q, k, v, o, args.reps).items():
-                        tot[r] += t
+                    for x, t in time_regimes(bsa, torch, w, TILE_REGIMES, q, k, v, o, args.reps).items():
+                        tot[x] = tot.get(x, 0.0) + t
                 best = min(tot, key=tot.get)
                 log(f"[lut] block {bq}x{bk} density {rho} L={L}: "
-                    + ", ".join(f"r{r} {t:.4f} ms" for r, t in tot.items()) + f" -> {best}")
+                    + ", ".join(f"{vname(x)} {t:.4f} ms" for x, t in tot.items()) + f" -> {vname(best)}")
                 notes.append(f"block {bq}x{bk} rho={rho} L={L} (sum over {len(layouts)} layouts): "
-                             + " ".join(f"r{r}={t:.4f}ms" for r, t in tot.items()))
-                rules.append(f"block   {bq:<7d} {bk:<7d} {dlo:<10g} {dhi:<10g} {llo:<4d} {lhi:<10d} {best}")
+                             + " ".join(f"{vname(x)}={t:.4f}ms" for x, t in tot.items()))
+                rules.append(f"block   {bq:<7d} {bk:<7d} {dlo:<10g} {dhi:<10g} {llo:<4d} {lhi:<10d} {best[0]} {oname(best[1])}")
+        # slice masks: the gather regime is fixed by the slice height; the task
+        # order is timed on the middle length bin (the key lists of the largest
+        # one take gigabytes to generate) and applies to every length
+        if (T, Hg, Wg) == LENGTH_BINS[1][0]:
+            for m, r in SLICE_RULES:
+                ws = wl.fgattn(H=H, T=T, Hg=Hg, Wg=Wg, d=d, M=m, cfg=9)
+                ts = time_regimes(bsa, torch, ws, (r,), q, k, v, o, args.reps)
+                best = min(ts, key=ts.get)
+                log(f"[lut] slice M={m} L={L}: " + ", ".join(f"{vname(x)} {t:.4f} ms" for x, t in ts.items()) + f" -> {vname(best)}")
+                notes.append(f"slice M={m} L={L}: " + " ".join(f"{vname(x)}={t:.4f}ms" for x, t in ts.items()))
+                slice_rules.append(f"slice   {m:<7d} 1       0          1          0    9999999999 {r} {oname(best[1])}")
         del q, k, v, o
         torch.cuda.empty_cache()
-    for m, r in SLICE_RULES:
-        rules.append(f"slice   {m:<7d} 1       0          1          0    9999999999 {r}")
+    rules += slice_rules or [f"slice   {m:<7d} 1       0          1          0    9999999999 {r} xcd" for m, r in SLICE_RULES]
     # anything not covered (other block shapes): the default tile regime
-    rules.append("block   *       *       0          1          0    9999999999 0")
-    rules.append("video   *       *       -1         1          0    9999999999 0")
+    rules.append("block   *       *       0          1          0    9999999999 0 xcd")
+    rules.append("video   *       *       -1         1          0    9999999999 0 lpt")
     head = [
         "# Regime lookup table for gfx950 (MI355X), built by lut/build_lut.py (offline profiling).",
         "# First matching rule wins. Regimes: 0 = 128x64 tiles (4 waves), 1 = 64x64 tiles (2 waves),",
         "# 2 = 64-query gather, 3 = 128-query gather, 4 = 256x64 tiles (8 waves).",
+        "# Task orders: xcd = one task queue per XCD (chunks of neighbouring query tiles), lpt = longest first.",
         f"# Synthetic requests: {H} heads, d = {d}, bf16; median of 3 interleaved rounds of {args.reps} forwards.",
-        "# kind  block_q block_k density_lo density_hi L_lo L_hi      regime",
+        "# kind  block_q block_k density_lo density_hi L_lo L_hi      regime order",
     ]
     text = "\n".join(head + rules + ["#", "# measurements:"] + ["# " + n for n in notes]) + "\n"
     with open(args.out, "w") as f:

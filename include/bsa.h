@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define BSA_ABI_VERSION 1
+#define BSA_ABI_VERSION 2
 
 typedef struct bsa_plan_s *bsa_plan_t;
 
@@ -115,7 +115,14 @@ typedef struct {
     const char *lut_path;          /* NULL = the table compiled into the library   */
     int32_t device;                /* HIP device ordinal; -1 = host-only plan for
                                       inspection (bsa_forward rejects it)          */
+    int32_t task_order;            /* BSA_ORDER_*; -1 = from the lookup table      */
 } bsa_plan_opts_t;
+
+/* Task orders. XCD_QUEUES: one queue per XCD (accelerator die, each with its
+ * own L2), filled with chunks of neighbouring query tiles of a head; each
+ * workgroup draws its task from its own XCD's queue first. LONGEST_FIRST:
+ * workgroup i runs task i of a longest-first order. */
+enum { BSA_ORDER_XCD_QUEUES = 0, BSA_ORDER_LONGEST_FIRST = 1 };
 
 /* Fill *opts with the defaults listed above. */
 void bsa_plan_opts_default(bsa_plan_opts_t *opts);
@@ -125,7 +132,7 @@ typedef struct {
     int32_t tile_q, tile_k;        /* physical tile shape                          */
     int32_t gather;                /* 1 if key tiles are gathered row lists        */
     int64_t tasks;                 /* tasks: one per (batch, head, query tile)     */
-    int64_t workgroups;            /* launched workgroups (tasks + XCD padding)    */
+    int64_t workgroups;            /* launched workgroups (one per task)           */
     int64_t tiles_full;            /* key tiles computed without a mask            */
     int64_t tiles_partial;         /* key tiles with exact masking                 */
     int64_t tiles_empty;           /* (query tile, key tile) pairs skipped         */
@@ -135,6 +142,8 @@ typedef struct {
     int64_t plan_ns;               /* wall time of bsa_plan                         */
     int64_t phase_ns[5];           /* of which: ingest/validation, regime lookup,
                                       physical mapping, task organisation, upload */
+    int32_t task_order;            /* BSA_ORDER_* the plan uses                    */
+    int32_t queues;                /* task queues (1 for LONGEST_FIRST)            */
 } bsa_plan_info_t;
 
 typedef struct {

@@ -5,9 +5,9 @@ import block_sparse_attention_fwd_amd as bsa
 import workloads as wl
 
 
-def plan_workload(w, device=0, force_regime=-1, bits=False, lut_path=None, dtype=bsa.DTYPE_BF16):
+def plan_workload(w, device=0, force_regime=-1, bits=False, lut_path=None, dtype=bsa.DTYPE_BF16, task_order=-1):
     kw = dict(T=w.T, Hg=w.Hg, Wg=w.Wg, head_layout=w.head_layout, force_regime=force_regime, device=device,
-              lut_path=lut_path, dtype=dtype)
+              lut_path=lut_path, dtype=dtype, task_order=task_order)
     if w.kind == wl.BLOCK:
         if bits:
             return bsa.plan(bsa.MASK_BLOCK_BITS, w.B, w.H, w.L, w.d, w.bq, w.bk, data=w.block_bits(), **kw)

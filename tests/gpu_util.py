@@ -32,12 +32,13 @@ def to_device(x: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(x)).to("cuda:0")
 
 
-def run_gpu(w, Q, K, V, force_regime=-1, plan=None, fill=float("nan")):
+def run_gpu(w, Q, K, V, force_regime=-1, plan=None, fill=float("nan"), task_order=-1):
     """Plan + forward on cuda:0 in the inputs' dtype (bf16 bits or float32);
     returns (O as float64 numpy [B][H][L][d], plan)."""
     f32 = Q.dtype == np.float32
     dtype = bsa.DTYPE_F32 if f32 else bsa.DTYPE_BF16
-    p = plan if plan is not None else plan_workload(w, device=0, force_regime=force_regime, dtype=dtype)
+    p = plan if plan is not None else plan_workload(w, device=0, force_regime=force_regime, dtype=dtype,
+                                                    task_order=task_order)
     q, k, v = to_device(Q), to_device(K), to_device(V)
     o = torch.full(q.shape, fill, dtype=torch.float32 if f32 else torch.bfloat16, device="cuda:0")
     bsa.forward(p, q, k, v, o)

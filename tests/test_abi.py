@@ -9,6 +9,7 @@ import pytest
 
 import block_sparse_attention_fwd_amd as bsa
 import workloads as wl
+from bsa_helpers import plan_workload
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -30,7 +31,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     L = bsa.lib()
-    assert L.bsa_abi_version() == 1
+    assert L.bsa_abi_version() == bsa.ABI_VERSION == 2
     assert L.bsa_status_str(bsa.ERR_INVALID_MASK) == b"BSA_ERR_INVALID_MASK"
     assert L.bsa_status_str(99) == b"BSA_ERR_UNKNOWN"
     assert len(bsa.regimes()) == L.bsa_regime_count() >= 3
@@ -127,3 +128,34 @@ def test_lookup_table_file(tmp_path):
            device=-1, match="malformed")
     expect(bsa.ERR_INVALID_ARGUMENT, bsa.plan, bsa.MASK_BLOCK_U8, 1, 2, 256, 64, 64, 64, data=m,
            lut_path=str(tmp_path / "nope"), device=-1)
+    # the optional order column; an explicit task_order option overrides it
+    f.write_text("block 64 64 0 1 0 99999 1 lpt\n")
+    info = bsa.plan(bsa.MASK_BLOCK_U8, 1, 2, 256, 64, 64, 64, data=m, lut_path=str(f), device=-1).info()
+    assert (info["regime"], info["task_order"], info["queues"]) == (1, bsa.ORDER_LONGEST_FIRST, 1)
+    info = bsa.plan(bsa.MASK_BLOCK_U8, 1, 2, 256, 64, 64, 64, data=m, lut_path=str(f), device=-1,
+                    task_order=bsa.ORDER_XCD_QUEUES).info()
+    assert (info["regime"], info["task_order"], info["queues"]) == (1, bsa.ORDER_XCD_QUEUES, 8)
+    f.write_text("block 64 64 0 1 0 99999 1 xcd\n")
+    assert bsa.plan(bsa.MASK_BLOCK_U8, 1, 2, 256, 64, 64, 64, data=m, lut_path=str(f), device=-1).info()["task_order"] == 0
+    f.write_text("block 64 64 0 1 0 99999 1 fifo\n")
+    expect(bsa.ERR_INVALID_ARGUMENT, bsa.plan, bsa.MASK_BLOCK_U8, 1, 2, 256, 64, 64, 64, data=m, lut_path=str(f),
+           device=-1, match="unknown order")
+    expect(bsa.ERR_INVALID_ARGUMENT, bsa.plan, bsa.MASK_BLOCK_U8, 1, 2, 256, 64, 64, 64, data=m, device=-1,
+           task_order=2, match="task_order")
+
+
+@pytest.mark.parametrize("order", [0, 1])
+def test_task_queues_partition_the_tasks(order):
+    """Each task (batch, head, query tile) appears exactly once in the plan's
+    task array, whatever the order; the XCD queues' chunks keep neighbouring
+    query tiles of a head together."""
+    w = wl.svg("B", H=6, T=5, Hg=7, Wg=13)
+    p = plan_workload(w, device=-1, task_order=order)
+    info = p.info()
+    assert info["task_order"] == order and info["queues"] == (8 if order == 0 else 1)
+    seen = {}
+    for h in range(w.H):
+        for r in p.coverage(0, h):
+            q0 = r["q0"] - r["q0"] % info["tile_q"]
+            seen.setdefault((h, q0), 0)
+    assert len(seen) == info["tasks"] == w.H * -(-w.L // info["tile_q"])

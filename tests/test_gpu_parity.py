@@ -20,7 +20,9 @@ def _gpu():
     bsa.lib()  # fail loudly if the library is missing
 
 
-from gpu_util import compare, log, run_gpu, sample_rows  # noqa: E402
+import block_sparse_attention_fwd_amd as bsa  # noqa: E402
+from bsa_helpers import plan_workload  # noqa: E402
+from gpu_util import compare, log, run_gpu, sample_rows, to_device  # noqa: E402
 
 
 def _small_block_cases():
@@ -38,22 +40,27 @@ def _small_block_cases():
     return out
 
 
+ORDERS = [bsa.ORDER_XCD_QUEUES, bsa.ORDER_LONGEST_FIRST]
+
+
+@pytest.mark.parametrize("order", ORDERS)
 @pytest.mark.parametrize("regime", [-1, 0, 1, 4])
-def test_tiny_config(regime):
+def test_tiny_config(regime, order):
     w = wl.tiny()
     Q, K, V = wl.make_qkv(w)
-    log(f"[case] tiny regime={regime}")
-    O, p = run_gpu(w, Q, K, V, force_regime=regime)
-    compare(w, Q, K, V, O, label=f"tiny r{regime} {p.info()['regime']}")
+    log(f"[case] tiny regime={regime} order={order}")
+    O, p = run_gpu(w, Q, K, V, force_regime=regime, task_order=order)
+    compare(w, Q, K, V, O, label=f"tiny r{regime} {p.info()['regime']} order {order}")
 
 
 @pytest.mark.parametrize("w", _small_block_cases(), ids=lambda w: w.name)
 @pytest.mark.parametrize("regime", [0, 1, 4])
 def test_small_block_masks(w, regime):
     Q, K, V = wl.make_qkv(w)
-    log(f"[case] {w.name} regime={regime}")
-    O, _ = run_gpu(w, Q, K, V, force_regime=regime)
-    compare(w, Q, K, V, O, label=f"{w.name} r{regime}")
+    for order in ORDERS:
+        log(f"[case] {w.name} regime={regime} order={order}")
+        O, _ = run_gpu(w, Q, K, V, force_regime=regime, task_order=order)
+        compare(w, Q, K, V, O, label=f"{w.name} r{regime} order {order}")
 
 
 @pytest.mark.parametrize("run", ["A", "B"])
@@ -65,9 +72,10 @@ def test_small_video(run, d):
     w.head_layout = np.array([0, 1, 1, 1], np.uint8) if run == "B" else np.zeros(4, np.uint8)
     Q, K, V = wl.make_qkv(w)
     for regime in (0, 1, 4):
-        log(f"[case] small video run={run} d={d} regime={regime}")
-        O, _ = run_gpu(w, Q, K, V, force_regime=regime)
-        compare(w, Q, K, V, O, label=f"video{run} d{d} r{regime}")
+        for order in ORDERS:
+            log(f"[case] small video run={run} d={d} regime={regime} order={order}")
+            O, _ = run_gpu(w, Q, K, V, force_regime=regime, task_order=order)
+            compare(w, Q, K, V, O, label=f"video{run} d{d} r{regime} order {order}")
 
 
 @pytest.mark.parametrize("M", [64, 128])
@@ -83,9 +91,10 @@ def test_small_slices(M, d):
     w.col_idx = np.delete(w.col_idx, np.arange(w.row_ptr[e], w.row_ptr[e + 1]))
     w.row_ptr[e + 1:] -= n1
     Q, K, V = wl.make_qkv(w)
-    log(f"[case] slices M={M} d={d} L={L}")
-    O, _ = run_gpu(w, Q, K, V)
-    compare(w, Q, K, V, O, label=f"slice M{M} d{d}")
+    for order in ORDERS:
+        log(f"[case] slices M={M} d={d} L={L} order={order}")
+        O, _ = run_gpu(w, Q, K, V, task_order=order)
+        compare(w, Q, K, V, O, label=f"slice M{M} d{d} order {order}")
 
 
 def test_all_empty_mask_writes_zeros():
@@ -102,6 +111,33 @@ def test_deterministic_repeat():
     O1, p = run_gpu(w, Q, K, V)
     O2, _ = run_gpu(w, Q, K, V, plan=p)
     assert np.array_equal(O1, O2)
+
+
+def test_task_queues_across_many_launches():
+    """XCD task queues: every launch draws tickets from a counter slot that
+    the launch leaves zeroed; 150 launches of one plan (the 64 slots wrap
+    around twice), interleaved with launches of a second plan, all write the
+    same output, equal to that of the longest-first order."""
+    w = wl.tiny()
+    Q, K, V = wl.make_qkv(w)
+    q, k, v = to_device(Q), to_device(K), to_device(V)
+    p_lpt = plan_workload(w, task_order=bsa.ORDER_LONGEST_FIRST)
+    p_xcd = plan_workload(w, task_order=bsa.ORDER_XCD_QUEUES)
+    p_other = plan_workload(w, task_order=bsa.ORDER_XCD_QUEUES, force_regime=1)
+    assert p_xcd.info()["queues"] > 1 and p_lpt.info()["queues"] == 1
+    ref = torch.empty_like(q)
+    bsa.forward(p_lpt, q, k, v, ref)
+    other = torch.empty_like(q)
+    outs = []
+    for i in range(150):
+        o = torch.full_like(q, float("nan"))
+        bsa.forward(p_xcd, q, k, v, o)
+        bsa.forward(p_other, q, k, v, other)
+        if i % 10 == 0 or i == 149:
+            outs.append(o)
+    torch.cuda.synchronize()
+    for o in outs:
+        assert torch.equal(o, ref)
 
 
 @pytest.mark.parametrize("regime", [-1, 4])

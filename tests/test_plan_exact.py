@@ -91,10 +91,11 @@ def small_cases():
 
 @pytest.mark.parametrize("w", small_cases(), ids=lambda w: w.name)
 @pytest.mark.parametrize("regime", [-1, 0, 1, 4])
-def test_plan_covers_each_kept_pair_once(w, regime):
+@pytest.mark.parametrize("order", [0, 1])
+def test_plan_covers_each_kept_pair_once(w, regime, order):
     if w.kind == wl.SLICE:
         regime = -1  # slices run only in the gather regime matching M
-    p = plan_workload(w, device=-1, force_regime=regime)
+    p = plan_workload(w, device=-1, force_regime=regime, task_order=order)
     for b in range(w.B):
         for h in range(w.H):
             got = coverage_counts(p, w, b, h)
