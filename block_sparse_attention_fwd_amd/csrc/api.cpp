@@ -1337,7 +1337,7 @@ extern "C" int32_t bsa_plan_coverage(bsa_plan_t p, int32_t b, int32_t h, bsa_cov
     const TileRec *tiles = p->tiles();
     for (int64_t ti = 0; ti < p->ntasks; ++ti) {
         const Task &t = tasks[ti];
-        if (t.bh != bh) continue;  // (no-op padding tasks have bh = -1)
+        if (t.bh != bh) continue;
         for (int32_t i = t.tb; i < t.te; ++i) {
             const TileRec &r = tiles[i];
             bsa_tile_record_t rec{};

@@ -47,7 +47,7 @@ constexpr int kCtrDone = 15;
 constexpr int kCtrSlots = 64;
 
 struct Task {        // 16 bytes
-    int32_t bh;      // b * H + h; -1 = no-op padding task
+    int32_t bh;      // b * H + h
     int32_t q0;      // first logical query position of the tile
     int32_t tb, te;  // key-tile records [tb, te)
 };

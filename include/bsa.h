@@ -28,7 +28,10 @@
  *    so the caller may free the mask as soon as bsa_plan returns.
  *  - A plan owns its host and device memory and is immutable; it may be used
  *    by any number of bsa_forward calls on any streams of its device, also
- *    concurrently. Destroy it only after the streams that use it are done.
+ *    concurrently: up to 64 of its launches may be in flight at once (a
+ *    launch that draws tasks from XCD queues takes one of the plan's 64
+ *    ticket-counter slots, in turn, and leaves it zeroed when it ends).
+ *    Destroy it only after the streams that use it are done.
  */
 #ifndef BSA_H
 #define BSA_H
