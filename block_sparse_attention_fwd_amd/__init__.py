@@ -28,7 +28,7 @@ LAYOUT_FRAME_MAJOR, LAYOUT_TEMPORAL_MAJOR = 0, 1
 DTYPE_BF16, DTYPE_F32 = 0, 1
 TILE_FULL, TILE_PARTIAL = 0, 1
 PRED_NONE, PRED_SUBBLOCK, PRED_VIDEO, PRED_LIST = 0, 1, 2, 3
-ORDER_XCD_QUEUES, ORDER_LONGEST_FIRST = 0, 1
+ORDER_XCD_GROUPED, ORDER_LONGEST_FIRST = 0, 1
 ABI_VERSION = 2  # the structures below mirror this version of bsa.h
 
 EXPORTED = ["bsa_abi_version", "bsa_plan_opts_default", "bsa_plan", "bsa_forward", "bsa_plan_destroy",
@@ -54,7 +54,7 @@ class PlanInfo(ctypes.Structure):
                 ("tiles_full", ctypes.c_int64),
                 ("tiles_partial", ctypes.c_int64), ("tiles_empty", ctypes.c_int64), ("gather_rows", ctypes.c_int64),
                 ("executed_pairs", ctypes.c_double), ("device_bytes", ctypes.c_int64), ("plan_ns", ctypes.c_int64),
-                ("phase_ns", ctypes.c_int64 * 5), ("task_order", ctypes.c_int32), ("queues", ctypes.c_int32)]
+                ("phase_ns", ctypes.c_int64 * 5), ("task_order", ctypes.c_int32)]
 
     def as_dict(self):
         d = {k: getattr(self, k) for k, _ in self._fields_}
@@ -71,7 +71,7 @@ class TileRecord(ctypes.Structure):
     _fields_ = [("q0", ctypes.c_int64), ("q1", ctypes.c_int64), ("kind", ctypes.c_int32),
                 ("predicate", ctypes.c_int32), ("k0", ctypes.c_int64), ("k1", ctypes.c_int64),
                 ("keys", ctypes.POINTER(ctypes.c_int32)), ("nkeys", ctypes.c_int64), ("sub_bits", ctypes.c_uint32),
-                ("sub_q", ctypes.c_int32), ("sub_k", ctypes.c_int32)]
+                ("sub_q", ctypes.c_int32), ("sub_k", ctypes.c_int32), ("task", ctypes.c_int64)]
 
 
 SINK = ctypes.CFUNCTYPE(ctypes.c_int, ctypes.c_void_p, ctypes.POINTER(TileRecord))
@@ -163,7 +163,7 @@ class Plan:
         def sink(user, rp):
             r = rp.contents
             d = {"q0": r.q0, "q1": r.q1, "kind": r.kind, "predicate": r.predicate, "k0": r.k0, "k1": r.k1,
-                 "sub_bits": r.sub_bits, "sub_q": r.sub_q, "sub_k": r.sub_k}
+                 "sub_bits": r.sub_bits, "sub_q": r.sub_q, "sub_k": r.sub_k, "task": r.task}
             if r.predicate == PRED_LIST:
                 d["keys"] = np.ctypeslib.as_array(r.keys, shape=(r.nkeys,)).copy() if r.nkeys else np.zeros(0, np.int32)
             recs.append(d)

@@ -153,7 +153,7 @@ static bool parse_lut(const std::string &text, std::vector<LutRule> &rules, std:
         else if (kind == "video") r.kind = BSA_MASK_VIDEO;
         else { err = "lookup table line " + std::to_string(ln) + ": unknown kind " + kind; return false; }
         std::string order;
-        r.order = BSA_ORDER_XCD_QUEUES;
+        r.order = BSA_ORDER_XCD_GROUPED;
         if (ls >> order) {
             if (order == "lpt") r.order = BSA_ORDER_LONGEST_FIRST;
             else if (order != "xcd") { err = "lookup table line " + std::to_string(ln) + ": unknown order " + order; return false; }
@@ -187,16 +187,14 @@ struct bsa_plan_s {
     int32_t T = 0, Hg = 0, Wg = 0, anchor = 0, radius = 0;
     int32_t bq_shift = 0, bk_shift = 0, nsk = 1, sub_q = 0, sub_k = 0;
     int32_t mode = 0;
-    int32_t task_order = 0;  // 0 = one queue per XCD, 1 = one longest-first queue
-    int32_t nqueues = 1;
-    uint32_t launch_seq = 0;  // launches so far (counter slot rotation)
+    int32_t task_order = BSA_ORDER_XCD_GROUPED;
     std::vector<uint8_t> head_layout, head_pattern;
     // image
     uint8_t *img = nullptr;
     size_t img_cap = 0, img_bytes = 0;
     bool img_pinned = false;
     std::vector<uint8_t> img_vec;
-    size_t off_tasks = 0, off_tiles = 0, off_gidx = 0, off_flags = 0, off_coords = 0, off_queues = 0, off_ctr = 0;
+    size_t off_tasks = 0, off_tiles = 0, off_gidx = 0, off_flags = 0, off_coords = 0;
     int64_t coord_stride = 0;                   // words per video key-coordinate table
     std::vector<uint8_t> head_coord_table;      // per head: index of its table
     int64_t ntasks = 0, ntiles = 0, ngidx = 0;  // ntasks: tasks in the task array
@@ -751,7 +749,7 @@ static double mask_density(const bsa_mask_desc_t &m, int32_t B, int32_t H, int64
 static int32_t choose_regime(const bsa_mask_desc_t &m, int32_t B, int32_t H, int64_t L, int32_t bq, int32_t bk,
                              const bsa_plan_opts_t &o, int *regime, int *order)
 {
-    *order = BSA_ORDER_XCD_QUEUES;
+    *order = BSA_ORDER_XCD_GROUPED;
     if (o.force_regime >= 0 && o.task_order >= 0) {
         *regime = o.force_regime;
     } else {
@@ -861,87 +859,50 @@ size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 // ---------------------------------------------------------------------------
 
 // One task per (batch, head, query tile) -- also for query tiles without any
-// key tile, so that every output row is written. The heads' outputs are
-// copied in parallel into the plan image, then ordered for the device, whose
-// workgroups draw their tasks from queues (one per XCD by default):
-//  - XCD queues (default): the tasks of a head, in query-tile order, are cut
-//    into chunks of consecutive query tiles, which share most of their key
-//    tiles; the chunks are dealt, most expensive per task first, to the queue
-//    with the least estimated work so far. A workgroup serves the queue of
-//    its own XCD (each XCD has its own L2), so a chunk's tasks run on one XCD
-//    at about the same time; every queue runs its costly tasks first and its
-//    cheap ones last, so that the workgroups run out of work together, and a
-//    workgroup whose queue is empty takes tasks from the others.
-//  - One queue in longest-first order (BSA_TASK_ORDER=lpt): a stable counting
-//    sort on the tile count, so the tail of the run holds the cheapest work.
+// key tile, so that every output row is written; workgroup i of the launch
+// runs task i. The heads' outputs are copied in parallel into the plan image,
+// then ordered for the device: longest first (a stable counting sort on the
+// tile count, so that the tail of the launch holds the cheapest work) and, by
+// default, grouped for the XCDs (below).
 static int xcd_count()
 {
     if (const char *e = std::getenv("BSA_XCDS")) return std::max(1, std::atoi(e));
     return 8;
 }
 
-// Chunks of a head's tasks in query-tile order: [first task, count,
-// estimated cost]. 64 tasks are about what one XCD runs at once (32 compute
-// units, two workgroups each), so the tasks running together on an XCD are
-// mostly neighbouring query tiles of one head.
-constexpr int64_t kChunkTasks = 64;
-struct QChunk {
-    int64_t first, n, cost;
-};
+// XCD grouping of a longest-first order. The order is cut into runs of
+// tasks of similar cost (tile counts within a factor kCostClass); inside a
+// run the tasks are put back in (head, query tile) order, split into X equal
+// segments, and interleaved: slot s + X i + x of the run takes task i of
+// segment x (the remainder of an uneven split forms the run's last, partial
+// round). Workgroup j of a launch goes to XCD j mod X, so every segment --
+// neighbouring query tiles of a head, which share most of their key tiles --
+// runs on one XCD and shares its L2, while at every point of the launch all
+// XCDs are handed tasks of the same cost, as in the plain longest-first
+// order (the hardware hands workgroups to the XCDs in turn, so an XCD that
+// is handed longer tasks than the others would hold them up).
+constexpr double kCostClass = 1.3;
 
-// Deal the chunks, most expensive per task first, each to the queue with the
-// least estimated work so far; a queue's chunks stay in the order dealt.
-static void deal_chunks(const bsa_plan_s &p, std::vector<QChunk> &chunks, const std::vector<Task> &unsorted, Task *tasks,
-                        int32_t *queues)
+static void group_for_xcds(Task *tasks, int64_t n, int X)
 {
-    const int NQ = p.nqueues;
-    // most expensive per task first; ties keep (head, query tile) order
-    std::stable_sort(chunks.begin(), chunks.end(),
-                     [](const QChunk &a, const QChunk &b) { return a.cost * b.n > b.cost * a.n; });
-    std::vector<std::vector<int32_t>> own(NQ);
-    std::vector<int64_t> load(NQ, 0), len(NQ, 0);
-    for (size_t c = 0; c < chunks.size(); ++c) {
-        int x = 0;
-        for (int y = 1; y < NQ; ++y)
-            if (load[y] < load[x]) x = y;
-        load[x] += chunks[c].cost;
-        len[x] += chunks[c].n;
-        own[x].push_back((int32_t)c);
+    auto cls = [](const Task &t) {
+        const int c = t.te - t.tb;
+        return c <= 0 ? -1 : (int)(std::log((double)c) / std::log(kCostClass));
+    };
+    std::vector<Task> run;
+    for (int64_t a = 0; a < n;) {
+        int64_t b = a + 1;
+        while (b < n && cls(tasks[b]) == cls(tasks[a])) ++b;
+        run.assign(tasks + a, tasks + b);
+        std::stable_sort(run.begin(), run.end(),
+                         [](const Task &u, const Task &v) { return u.bh != v.bh ? u.bh < v.bh : u.q0 < v.q0; });
+        const int64_t m = b - a, q = m / X;
+        int64_t pos = a;
+        for (int64_t i = 0; i < q; ++i)
+            for (int x = 0; x < X; ++x) tasks[pos++] = run[(size_t)(x * q + i)];
+        for (int64_t k = X * q; k < m; ++k) tasks[pos++] = run[(size_t)k];
+        a = b;
     }
-    int64_t pos = 0;
-    for (int x = 0; x < NQ; ++x) {
-        queues[2 * x] = (int32_t)pos;
-        queues[2 * x + 1] = (int32_t)len[x];
-        for (int32_t c : own[x])
-            for (int64_t k = 0; k < chunks[c].n; ++k) tasks[pos++] = unsorted[(size_t)(chunks[c].first + k)];
-    }
-}
-
-static void order_xcd_queues(const bsa_plan_s &p, const std::vector<int64_t> &t_off, const std::vector<Task> &unsorted,
-                             Task *tasks, int32_t *queues)
-{
-    const TileRec *tiles = (const TileRec *)(p.img + p.off_tiles);
-    const int64_t G = kChunkTasks;
-    const size_t nh = t_off.size() - 1;
-    // The estimated cost is in tenths of a FULL tile: 80 per task (query
-    // load, first copy, epilogue), 10 per FULL tile, 14 per PARTIAL tile
-    // (mask, partly skipped waves).
-    std::vector<int64_t> c_off(nh + 1, 0);
-    for (size_t i = 0; i < nh; ++i) c_off[i + 1] = c_off[i] + (t_off[i + 1] - t_off[i] + G - 1) / G;
-    std::vector<QChunk> chunks((size_t)c_off[nh]);
-    parallel_for((int64_t)nh, [&](int64_t i) {
-        int64_t c = c_off[i];
-        for (int64_t s0 = t_off[i]; s0 < t_off[i + 1]; s0 += G, ++c) {
-            QChunk ch{s0, std::min(G, t_off[i + 1] - s0), 0};
-            for (int64_t k = ch.first; k < ch.first + ch.n; ++k) {
-                const Task &t = unsorted[(size_t)k];
-                ch.cost += 80;
-                for (int32_t r = t.tb; r < t.te; ++r) ch.cost += (tiles[r].aux & kPartial) ? 14 : 10;
-            }
-            chunks[(size_t)c] = ch;
-        }
-    });
-    deal_chunks(p, chunks, unsorted, tasks, queues);
 }
 
 static int32_t organise_tasks(bsa_plan_s &p, const std::vector<HeadOut *> &heads)
@@ -970,10 +931,6 @@ static int32_t organise_tasks(bsa_plan_s &p, const std::vector<HeadOut *> &heads
     p.off_gidx = p.off_tiles + align_up(std::max<int64_t>(1, p.ntiles) * sizeof(TileRec));
     p.off_flags = p.off_gidx + align_up(std::max<int64_t>(1, p.ngidx) * sizeof(int32_t));
     p.off_coords = p.off_flags + align_up((size_t)p.H * sizeof(uint32_t));
-    p.nqueues = p.task_order == 0 ? std::min(kMaxQueues, xcd_count()) : 1;
-    p.off_queues = p.off_coords;  // (coordinate tables follow the queue table and the counters)
-    p.off_ctr = p.off_queues + align_up((size_t)kMaxQueues * 2 * sizeof(int32_t));
-    p.off_coords = p.off_ctr + align_up((size_t)kCtrSlots * kCtrWords * sizeof(uint32_t));
     // video masks: one key-coordinate table per (pattern, layout) pair the heads use
     int ntables = 0;
     int table_of[3][2] = {{-1, -1}, {-1, -1}, {-1, -1}};
@@ -1020,20 +977,12 @@ static int32_t organise_tasks(bsa_plan_s &p, const std::vector<HeadOut *> &heads
         if (!h.gidx.empty()) std::memcpy(gidx + g_off[i], h.gidx.data(), h.gidx.size() * sizeof(int32_t));
     });
     Task *tasks = (Task *)(p.img + p.off_tasks);
-    int32_t *queues = (int32_t *)(p.img + p.off_queues);
-    std::memset(queues, 0, (size_t)kMaxQueues * 2 * sizeof(int32_t));
-    std::memset(p.img + p.off_ctr, 0, (size_t)kCtrSlots * kCtrWords * sizeof(uint32_t));
-    if (p.nqueues > 1) {
-        order_xcd_queues(p, t_off, unsorted, tasks, queues);
-    } else {
-        // stable LPT order: counting sort on the tile count, descending
-        std::vector<int64_t> bucket((size_t)max_cost + 2, 0);
-        for (const Task &t : unsorted) ++bucket[(size_t)(max_cost - (t.te - t.tb)) + 1];
-        for (size_t c = 1; c < bucket.size(); ++c) bucket[c] += bucket[c - 1];
-        for (const Task &t : unsorted) tasks[bucket[(size_t)(max_cost - (t.te - t.tb))]++] = t;
-        queues[0] = 0;
-        queues[1] = (int32_t)nreal;
-    }
+    // longest first: a stable counting sort on the tile count, descending
+    std::vector<int64_t> bucket((size_t)max_cost + 2, 0);
+    for (const Task &t : unsorted) ++bucket[(size_t)(max_cost - (t.te - t.tb)) + 1];
+    for (size_t c = 1; c < bucket.size(); ++c) bucket[c] += bucket[c - 1];
+    for (const Task &t : unsorted) tasks[bucket[(size_t)(max_cost - (t.te - t.tb))]++] = t;
+    if (p.task_order == BSA_ORDER_XCD_GROUPED) group_for_xcds(tasks, nreal, xcd_count());
     uint32_t *flags = (uint32_t *)(p.img + p.off_flags);
     for (int h = 0; h < p.H; ++h)
         flags[h] = (p.head_layout[h] ? kHeadTemporalMajor : 0u) | ((uint32_t)p.head_pattern[h] << kHeadPatShift) |
@@ -1272,12 +1221,6 @@ extern "C" int32_t bsa_forward(bsa_plan_t p, const void *Q, const void *K, const
     a.head_flags = (const uint32_t *)(dev + p->off_flags);
     a.coords = (const int32_t *)(dev + p->off_coords);
     a.coords_stride = (int32_t)p->coord_stride;
-    a.queues = (const int32_t *)(dev + p->off_queues);
-    a.nqueues = p->nqueues > 1 ? p->nqueues : 0;  // one queue: workgroup i runs task i
-    {
-        const uint32_t slot = __atomic_fetch_add(&p->launch_seq, 1u, __ATOMIC_RELAXED) % (uint32_t)kCtrSlots;
-        a.ctr = (uint32_t *)p->dev + p->off_ctr / sizeof(uint32_t) + (size_t)slot * kCtrWords;
-    }
     a.ntasks = (int32_t)p->ntasks;
     a.H = p->H;
     a.L = (int32_t)p->L;
@@ -1323,7 +1266,6 @@ extern "C" int32_t bsa_plan_info(bsa_plan_t p, bsa_plan_info_t *out)
     out->plan_ns = p->plan_ns;
     for (int i = 0; i < 5; ++i) out->phase_ns[i] = p->phase_ns[i];
     out->task_order = p->task_order;
-    out->queues = p->nqueues;
     return BSA_OK;
 }
 
@@ -1341,6 +1283,7 @@ extern "C" int32_t bsa_plan_coverage(bsa_plan_t p, int32_t b, int32_t h, bsa_cov
         for (int32_t i = t.tb; i < t.te; ++i) {
             const TileRec &r = tiles[i];
             bsa_tile_record_t rec{};
+            rec.task = ti;
             rec.q0 = t.q0;
             rec.q1 = std::min<int64_t>(t.q0 + R.tile_q, p->L);
             rec.kind = (r.aux & kPartial) ? BSA_TILE_PARTIAL : BSA_TILE_FULL;

@@ -125,30 +125,6 @@ __device__ __forceinline__ bf16x8 load_bf16x8(const __bf16 *p)
     return __builtin_bit_cast(bf16x8, v);
 }
 
-// XCD (accelerator complex die) that runs this wave: each has its own L2.
-__device__ __forceinline__ int xcc_id()
-{
-    unsigned x;
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
-#pragma clang diagnostic pop
-    return (int)(x & 0xFu);
-}
-
-// Queue walk of a workgroup (run by one thread): ticket was drawn from queue q;
-// returns the task it names, or moves on to the next queue (a queue found
-// empty stays empty: tickets only grow) and returns -1 once all are empty.
-__device__ __forceinline__ int next_task(const KernelArgs &a, int &q, int &moves, int ticket)
-{
-    for (;;) {
-        if (ticket < a.queues[2 * q + 1]) return a.queues[2 * q] + ticket;
-        if (++moves >= a.nqueues) return -1;
-        q = q + 1 == a.nqueues ? 0 : q + 1;
-        ticket = (int)atomicAdd(a.ctr + q, 1u);
-    }
-}
-
 // Kernel: NW waves per workgroup, each wave owns RB consecutive blocks of 32
 // query rows. Every K operand read from LDS feeds RB score MFMAs and every V
 // operand read feeds RB output MFMAs, so LDS bytes per MFMA fall as 1/RB.
@@ -160,32 +136,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1
     __shared__ __attribute__((aligned(1024))) unsigned char ksm[2][C::TILEB];  // [buffer] swizzled K tile
     __shared__ __attribute__((aligned(1024))) unsigned char vsm[2][C::TILEB];  // [buffer] swizzled V tile
 
-    __shared__ int s_task;  // the workgroup's task
-
     const int tid = threadIdx.x;
     const int lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
-
-    // Task queues (nqueues > 0): thread 0 draws a ticket from the queue of
-    // this workgroup's XCD, whose tasks share key tiles in that XCD's L2, and
-    // from the other queues once it is empty. The launch has one workgroup
-    // per task, so every workgroup finds one. Without queues, workgroup i
-    // runs task i.
-    int ti = blockIdx.x;
-    if (a.nqueues > 0) {
-        if (tid == 0) {
-            int wq = xcc_id() % a.nqueues, moves = 0;
-            s_task = next_task(a, wq, moves, (int)atomicAdd(a.ctr + wq, 1u));
-        }
-        __syncthreads();
-        ti = __builtin_amdgcn_readfirstlane(s_task);
-    }
-    if (ti >= 0) {
     // task fields and head flags are workgroup-uniform: scalar registers
-    const Task tl = a.tasks[ti];
+    const Task tl = a.tasks[blockIdx.x];
     const Task task{__builtin_amdgcn_readfirstlane(tl.bh), __builtin_amdgcn_readfirstlane(tl.q0),
                     __builtin_amdgcn_readfirstlane(tl.tb), __builtin_amdgcn_readfirstlane(tl.te)};
-    {
+    if (task.bh < 0) return;  // padding task of an XCD segment
     const int bh = task.bh;
     const int h = bh % a.H;
     const uint32_t hflag = (uint32_t)__builtin_amdgcn_readfirstlane((int)a.head_flags[h]);
@@ -478,17 +436,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1
                 }
         }
     }
-    }
-    }
-
-    // the last workgroup out leaves the counter slot zeroed for a later launch
-    if (a.nqueues > 0 && tid == 0) {
-        const unsigned done = __hip_atomic_fetch_add(a.ctr + kCtrDone, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-        if (done == gridDim.x - 1) {
-            for (int i = 0; i < kCtrWords; ++i)
-                __hip_atomic_store(a.ctr + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
 }
 
 template <int NW, int RB, int D>
@@ -500,7 +447,7 @@ static hipError_t launch(const KernelArgs &a, hipStream_t stream)
 
 hipError_t launch_forward(const KernelArgs &a, int waves, int rb, int d, int dtype, hipStream_t stream)
 {
-    if (dtype != 0 || a.nqueues < 0 || a.nqueues > kMaxQueues) return hipErrorInvalidValue;
+    if (dtype != 0) return hipErrorInvalidValue;
     if (rb == 1) {
         if (waves == 8 && d == 128) return launch<8, 1, 128>(a, stream);
         if (waves == 8 && d == 64) return launch<8, 1, 64>(a, stream);

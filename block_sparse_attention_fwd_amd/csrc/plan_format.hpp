@@ -35,19 +35,8 @@ constexpr uint32_t kHeadTemporalMajor = 1u;   // bit 0: logical j = p*T + t
 constexpr uint32_t kHeadPatShift = 1;         // bits 1..2: video pattern
 constexpr uint32_t kHeadCoordShift = 3;       // bits 3..4: video key-coordinate table of the head
 
-// Task queues of the bf16 kernel: queue q holds the tasks [queues[2q],
-// queues[2q] + queues[2q + 1]) of the task array, and a workgroup takes its
-// task by drawing a ticket from a queue. A launch draws from one slot of
-// kCtrWords counters (queue q's counter at word q, the count of finished
-// workgroups at word kCtrDone) and leaves it zeroed; successive launches of a
-// plan rotate over kCtrSlots slots.
-constexpr int kMaxQueues = 15;
-constexpr int kCtrWords = 16;
-constexpr int kCtrDone = 15;
-constexpr int kCtrSlots = 64;
-
 struct Task {        // 16 bytes
-    int32_t bh;      // b * H + h
+    int32_t bh;      // b * H + h; -1 = no-op padding task
     int32_t q0;      // first logical query position of the tile
     int32_t tb, te;  // key-tile records [tb, te)
 };
@@ -65,9 +54,6 @@ struct KernelArgs {
     const int32_t *gidx;
     const uint32_t *head_flags;
     const int32_t *coords;     // video key-coordinate tables, coords_stride words each
-    const int32_t *queues;     // [nqueues][2]: first task, task count
-    uint32_t *ctr;             // this launch's counter slot (kCtrWords words, zero at launch)
-    int32_t nqueues;
     int32_t ntasks;
     int32_t coords_stride;     // padded to whole 64-key tiles
     int32_t H;

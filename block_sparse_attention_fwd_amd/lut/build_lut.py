@@ -33,7 +33,7 @@ import numpy as np  # noqa: E402
 
 TILE_REGIMES = (0, 1, 4)        # contiguous-tile regimes (block and video masks)
 SLICE_RULES = ((64, 2), (128, 3))  # slice masks: the gather regime of the slice height
-ORDERS = ((0, "xcd"), (1, "lpt"))  # task orders (BSA_ORDER_*) and their table names
+ORDERS = ((0, "xcd"), (1, "lpt"))  # task orders (BSA_ORDER_*: XCD-grouped, plain longest first) and table names
 # sequence-length bins: (representative token grid T x Hg x Wg, L range of the rule)
 LENGTH_BINS = (
     ((4, 32, 32), (0, 8192)),
@@ -148,12 +148,12 @@ def main():
     rules += slice_rules or [f"slice   {m:<7d} 1       0          1          0    9999999999 {r} xcd" for m, r in SLICE_RULES]
     # anything not covered (other block shapes): the default tile regime
     rules.append("block   *       *       0          1          0    9999999999 0 xcd")
-    rules.append("video   *       *       -1         1          0    9999999999 0 lpt")
+    rules.append("video   *       *       -1         1          0    9999999999 0 xcd")
     head = [
         "# Regime lookup table for gfx950 (MI355X), built by lut/build_lut.py (offline profiling).",
         "# First matching rule wins. Regimes: 0 = 128x64 tiles (4 waves), 1 = 64x64 tiles (2 waves),",
         "# 2 = 64-query gather, 3 = 128-query gather, 4 = 256x64 tiles (8 waves).",
-        "# Task orders: xcd = one task queue per XCD (chunks of neighbouring query tiles), lpt = longest first.",
+        "# Task orders: xcd = longest first, grouped so neighbouring query tiles share an XCD; lpt = longest first.",
         f"# Synthetic requests: {H} heads, d = {d}, bf16; median of 3 interleaved rounds of {args.reps} forwards.",
         "# kind  block_q block_k density_lo density_hi L_lo L_hi      regime order",
     ]

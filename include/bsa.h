@@ -28,10 +28,7 @@
  *    so the caller may free the mask as soon as bsa_plan returns.
  *  - A plan owns its host and device memory and is immutable; it may be used
  *    by any number of bsa_forward calls on any streams of its device, also
- *    concurrently: up to 64 of its launches may be in flight at once (a
- *    launch that draws tasks from XCD queues takes one of the plan's 64
- *    ticket-counter slots, in turn, and leaves it zeroed when it ends).
- *    Destroy it only after the streams that use it are done.
+ *    concurrently. Destroy it only after the streams that use it are done.
  */
 #ifndef BSA_H
 #define BSA_H
@@ -121,11 +118,12 @@ typedef struct {
     int32_t task_order;            /* BSA_ORDER_*; -1 = from the lookup table      */
 } bsa_plan_opts_t;
 
-/* Task orders. XCD_QUEUES: one queue per XCD (accelerator die, each with its
- * own L2), filled with chunks of neighbouring query tiles of a head; each
- * workgroup draws its task from its own XCD's queue first. LONGEST_FIRST:
- * workgroup i runs task i of a longest-first order. */
-enum { BSA_ORDER_XCD_QUEUES = 0, BSA_ORDER_LONGEST_FIRST = 1 };
+/* Task orders (workgroup i of a launch runs task i). LONGEST_FIRST: tasks by
+ * decreasing tile count. XCD_GROUPED: the same, with each run of tasks of
+ * similar cost interleaved so that neighbouring query tiles of a head land on
+ * one XCD (accelerator die with its own L2; the hardware deals workgroups to
+ * the XCDs in turn). */
+enum { BSA_ORDER_XCD_GROUPED = 0, BSA_ORDER_LONGEST_FIRST = 1 };
 
 /* Fill *opts with the defaults listed above. */
 void bsa_plan_opts_default(bsa_plan_opts_t *opts);
@@ -146,7 +144,6 @@ typedef struct {
     int64_t phase_ns[5];           /* of which: ingest/validation, regime lookup,
                                       physical mapping, task organisation, upload */
     int32_t task_order;            /* BSA_ORDER_* the plan uses                    */
-    int32_t queues;                /* task queues (1 for LONGEST_FIRST)            */
 } bsa_plan_info_t;
 
 typedef struct {
@@ -175,6 +172,8 @@ typedef struct {
     uint32_t sub_bits;             /* BSA_PRED_SUBBLOCK: keep bit of sub-block
                                       (sq * sub_nk + sk)                           */
     int32_t sub_q, sub_k;          /* sub-block shape; sub_nk = tile_k / sub_k     */
+    int64_t task;                  /* the record's task = workgroup index in the
+                                      launch                                      */
 } bsa_tile_record_t;
 
 /* Return nonzero to stop the walk early. */

@@ -131,10 +131,10 @@ def test_lookup_table_file(tmp_path):
     # the optional order column; an explicit task_order option overrides it
     f.write_text("block 64 64 0 1 0 99999 1 lpt\n")
     info = bsa.plan(bsa.MASK_BLOCK_U8, 1, 2, 256, 64, 64, 64, data=m, lut_path=str(f), device=-1).info()
-    assert (info["regime"], info["task_order"], info["queues"]) == (1, bsa.ORDER_LONGEST_FIRST, 1)
+    assert (info["regime"], info["task_order"]) == (1, bsa.ORDER_LONGEST_FIRST)
     info = bsa.plan(bsa.MASK_BLOCK_U8, 1, 2, 256, 64, 64, 64, data=m, lut_path=str(f), device=-1,
-                    task_order=bsa.ORDER_XCD_QUEUES).info()
-    assert (info["regime"], info["task_order"], info["queues"]) == (1, bsa.ORDER_XCD_QUEUES, 8)
+                    task_order=bsa.ORDER_XCD_GROUPED).info()
+    assert (info["regime"], info["task_order"]) == (1, bsa.ORDER_XCD_GROUPED)
     f.write_text("block 64 64 0 1 0 99999 1 xcd\n")
     assert bsa.plan(bsa.MASK_BLOCK_U8, 1, 2, 256, 64, 64, 64, data=m, lut_path=str(f), device=-1).info()["task_order"] == 0
     f.write_text("block 64 64 0 1 0 99999 1 fifo\n")
@@ -144,18 +144,44 @@ def test_lookup_table_file(tmp_path):
            task_order=2, match="task_order")
 
 
-@pytest.mark.parametrize("order", [0, 1])
-def test_task_queues_partition_the_tasks(order):
-    """Each task (batch, head, query tile) appears exactly once in the plan's
-    task array, whatever the order; the XCD queues' chunks keep neighbouring
-    query tiles of a head together."""
-    w = wl.svg("B", H=6, T=5, Hg=7, Wg=13)
-    p = plan_workload(w, device=-1, task_order=order)
-    info = p.info()
-    assert info["task_order"] == order and info["queues"] == (8 if order == 0 else 1)
-    seen = {}
+def _task_slots(p, w):
+    """{(head, q0 of the task): launch slot} from the coverage walk, and the
+    task's tile count."""
+    slot, ntiles = {}, {}
+    tq = p.info()["tile_q"]
     for h in range(w.H):
         for r in p.coverage(0, h):
-            q0 = r["q0"] - r["q0"] % info["tile_q"]
-            seen.setdefault((h, q0), 0)
-    assert len(seen) == info["tasks"] == w.H * -(-w.L // info["tile_q"])
+            key = (h, r["q0"] - r["q0"] % tq)
+            assert slot.setdefault(key, r["task"]) == r["task"]
+            ntiles.setdefault(key, set()).add(r["k0"])
+    return slot, {k: len(v) for k, v in ntiles.items()}
+
+
+@pytest.mark.parametrize("order", [0, 1])
+def test_task_orders(order):
+    """Workgroup i runs task i. Both orders put the tasks longest first (a
+    task's cost class never rises along the launch); the XCD grouping puts,
+    within a run of one cost class, query tiles of one head in slots 8 apart
+    (one XCD), in query-tile order."""
+    w = wl.svg("B")
+    p = plan_workload(w, device=-1, task_order=order)
+    info = p.info()
+    assert info["task_order"] == order
+    slot, ntiles = _task_slots(p, w)
+    n = info["tasks"]
+    assert len(set(slot.values())) == len(slot) == n == w.H * -(-w.L // info["tile_q"])
+    assert sorted(slot.values()) == list(range(n))
+    pos = {s: k for k, s in slot.items()}
+    counts = [ntiles[pos[s]] for s in range(n)]
+    if order == 1:
+        assert counts == sorted(counts, reverse=True)
+        return
+    cls = [int(np.log(c) / np.log(1.3)) for c in counts]
+    assert cls == sorted(cls, reverse=True)
+    pairs = same = 0
+    for s in range(n - 8):
+        if cls[s] == cls[s + 8]:
+            pairs += 1
+            (h, q0), (h2, q2) = pos[s], pos[s + 8]
+            same += h2 == h and q2 > q0
+    assert pairs > 0.9 * n and same > 0.95 * pairs, (pairs, same, n)
