@@ -35,6 +35,8 @@
 #include <sstream>
 #include <string>
 #include <thread>
+
+#include <sched.h>
 #include <vector>
 
 #include "../../include/bsa.h"
@@ -378,7 +380,7 @@ class WorkerPool {
             n_ = n;
             next_.store(0);
             pending_ = (int)workers_.size();
-            ++gen_;
+            gen_.store(gen_.load(std::memory_order_relaxed) + 1, std::memory_order_release);
         }
         cv_.notify_all();
         drain();
@@ -390,7 +392,12 @@ class WorkerPool {
   private:
     WorkerPool()
     {
+        // threads = the CPUs this process may run on (affinity mask), at most
+        // OMP_NUM_THREADS when that is set, at most 32
         unsigned hc = std::thread::hardware_concurrency();
+        cpu_set_t cs;
+        if (sched_getaffinity(0, sizeof cs, &cs) == 0 && CPU_COUNT(&cs) > 0) hc = (unsigned)CPU_COUNT(&cs);
+        if (const char *e = std::getenv("OMP_NUM_THREADS"); e && std::atoi(e) > 0) hc = std::min(hc, (unsigned)std::atoi(e));
         const int nt = (int)std::max(1u, std::min(hc, 32u)) - 1;
         for (int t = 0; t < nt; ++t) workers_.emplace_back([this] { loop(); });
         for (auto &w : workers_) w.detach();
@@ -406,10 +413,16 @@ class WorkerPool {
         in_worker_ = true;
         uint64_t seen = 0;
         for (;;) {
+            // a planner runs several parallel regions in a row, and plans often
+            // follow each other closely: look for the next region for a short
+            // while before sleeping (a wake-up costs tens of microseconds)
+            const auto spin_end = std::chrono::steady_clock::now() + std::chrono::microseconds(kSpinUs);
+            while (gen_.load(std::memory_order_acquire) == seen && std::chrono::steady_clock::now() < spin_end)
+                std::this_thread::yield();
             {
                 std::unique_lock<std::mutex> g(mu_);
-                cv_.wait(g, [&] { return gen_ != seen; });
-                seen = gen_;
+                cv_.wait(g, [&] { return gen_.load(std::memory_order_acquire) != seen; });
+                seen = gen_.load(std::memory_order_acquire);
             }
             drain();
             {
@@ -426,7 +439,8 @@ class WorkerPool {
     int64_t n_ = 0;
     std::atomic<int64_t> next_{0};
     int pending_ = 0;
-    uint64_t gen_ = 0;
+    std::atomic<uint64_t> gen_{0};
+    static constexpr int kSpinUs = 300;
     static thread_local bool in_worker_;
 };
 thread_local bool WorkerPool::in_worker_ = false;
@@ -447,7 +461,8 @@ void parallel_for(int64_t n, F &&f)
 // BLOCK masks: retain (bq = tile_q, bk = tile_k), combine (smaller logical
 // blocks merged into one tile, kept sub-blocks recorded as bits) or subdivide
 // (larger logical blocks split over several tiles).
-static void map_block_head(const bsa_plan_s &p, const bsa_mask_desc_t &m, int b, int h, int BQ, HeadOut &out)
+static void map_block_head(const bsa_plan_s &p, const bsa_mask_desc_t &m, int b, int h, int BQ, int64_t tq_lo,
+                           int64_t tq_hi, HeadOut &out)
 {
     const int64_t L = p.L;
     const int64_t nqb = (L + p.block_q - 1) / p.block_q, nkb = (L + p.block_k - 1) / p.block_k;
@@ -459,8 +474,9 @@ static void map_block_head(const bsa_plan_s &p, const bsa_mask_desc_t &m, int b,
     const uint8_t *u8 = m.kind == BSA_MASK_BLOCK_U8 ? (const uint8_t *)m.data + bh * nqb * nkb : nullptr;
     const uint64_t *bits = m.kind == BSA_MASK_BLOCK_BITS ? (const uint64_t *)m.data + bh * nqb * words : nullptr;
     std::vector<uint32_t> acc(nkt, 0);
-    out.tasks.reserve(nqt);
-    for (int64_t tq = 0; tq < nqt; ++tq) {
+    (void)nqt;
+    out.tasks.reserve((size_t)(tq_hi - tq_lo));
+    for (int64_t tq = tq_lo; tq < tq_hi; ++tq) {
         const int64_t q0 = tq * BQ, q1 = std::min<int64_t>(q0 + BQ, L);
         const int64_t qb0 = q0 / p.block_q, qb1 = (q1 - 1) / p.block_q;
         std::fill(acc.begin(), acc.end(), 0u);
@@ -509,21 +525,16 @@ static void map_block_head(const bsa_plan_s &p, const bsa_mask_desc_t &m, int b,
 // none of whose pairs is kept skips the tile, a wave all of whose pairs are
 // kept runs it unmasked (Splash Attention's empty-tile skip and boundary-only
 // masking, applied at the granularity one wavefront computes).
-static void map_video_head(const bsa_plan_s &p, int b, int h, int BQ, HeadOut &out)
+static void map_video_head(const bsa_plan_s &p, int b, int h, int BQ, int64_t tq_lo, int64_t tq_hi, HeadOut &out)
 {
     const int64_t L = p.L;
     const Geo g{L, p.T, (int64_t)p.Hg * p.Wg, p.Wg};
     const bool tm = p.head_layout[h] == BSA_LAYOUT_TEMPORAL_MAJOR;
     const int pat = p.head_pattern[h];
-    const int64_t nqt = (L + BQ - 1) / BQ, nkt = (L + kTileK - 1) / kTileK;
+    const int64_t nkt = (L + kTileK - 1) / kTileK;
     const int64_t bh = (int64_t)b * p.H + h;
     const int64_t r = p.radius, W = p.Wg, Hg = p.Hg, HW = g.HW;
-    std::vector<VideoTileSets> ks(nkt);
-    for (int64_t tk = 0; tk < nkt; ++tk) {
-        int64_t k0 = tk * kTileK, k1 = std::min<int64_t>(k0 + kTileK, L);
-        if (pat == BSA_PAT_SPATIAL) ks[tk].f = frames_of(g, tm, k0, k1 - 1);
-        if (pat == BSA_PAT_TEMPORAL) pixel_rects(g, tm, k0, k1 - 1, ks[tk].r);
-    }
+    VideoTileSets ks;  // frames or pixels of the key tile being classified
     VideoTileSets qs;
     const int NWV = BQ / kWaveRows;
     VideoTileSets qw[8];                            // per-wave query sets (NWV <= 8)
@@ -534,9 +545,9 @@ static void map_video_head(const bsa_plan_s &p, int b, int h, int BQ, HeadOut &o
         hi = std::min<int64_t>(hi, L - 1);
         if (lo <= hi) cand.push_back({lo / kTileK, hi / kTileK});
     };
-    out.tasks.reserve(nqt);
+    out.tasks.reserve((size_t)(tq_hi - tq_lo));
     int64_t computed = 0;
-    for (int64_t tq = 0; tq < nqt; ++tq) {
+    for (int64_t tq = tq_lo; tq < tq_hi; ++tq) {
         const int64_t q0 = tq * BQ, q1 = std::min<int64_t>(q0 + BQ, L);
         if (pat == BSA_PAT_SPATIAL) qs.f = frames_of(g, tm, q0, q1 - 1);
         if (pat == BSA_PAT_TEMPORAL) pixel_rects(g, tm, q0, q1 - 1, qs.r);
@@ -574,15 +585,17 @@ static void map_video_head(const bsa_plan_s &p, int b, int h, int BQ, HeadOut &o
         int64_t last = -1;
         for (const auto &c : cand) {
             for (int64_t tk = std::max(c.first, last + 1); tk <= c.second; ++tk) {
-                const int64_t k0 = tk * kTileK;
+                const int64_t k0 = tk * kTileK, k1 = std::min<int64_t>(k0 + kTileK, L);
                 const bool crop = k0 + kTileK > L;
-                int cl = classify_video(pat, p.anchor, p.radius, qs, ks[tk], crop);
+                if (pat == BSA_PAT_SPATIAL) ks.f = frames_of(g, tm, k0, k1 - 1);
+                if (pat == BSA_PAT_TEMPORAL) pixel_rects(g, tm, k0, k1 - 1, ks.r);
+                int cl = classify_video(pat, p.anchor, p.radius, qs, ks, crop);
                 if (cl == kEmpty) continue;
                 uint32_t aux = 0;
                 if (cl == kPart) {
                     aux = kPartial;
                     for (int wv = 0; wv < NWV; ++wv) {
-                        const int wc = qw_rows[wv] <= 0 ? kEmpty : classify_video(pat, p.anchor, p.radius, qw[wv], ks[tk], crop);
+                        const int wc = qw_rows[wv] <= 0 ? kEmpty : classify_video(pat, p.anchor, p.radius, qw[wv], ks, crop);
                         if (wc == kEmpty) aux |= 1u << wv;
                         if (wc == kFull) aux |= 1u << (kWaveFullShift + wv);
                     }
@@ -596,20 +609,21 @@ static void map_video_head(const bsa_plan_s &p, int b, int h, int BQ, HeadOut &o
         t.te = (int32_t)out.tiles.size();
         out.tasks.push_back(t);
     }
-    out.empty = nqt * nkt - computed;
+    out.empty = (tq_hi - tq_lo) * nkt - computed;
 }
 
 // SLICE masks: each M-query block's sorted key list packed into gather tiles
 // of kTileK keys; only the last tile of a list can be short (masked).
-static void map_slice_head(const bsa_plan_s &p, const bsa_mask_desc_t &m, int b, int h, HeadOut &out)
+static void map_slice_head(const bsa_plan_s &p, const bsa_mask_desc_t &m, int b, int h, int64_t tq_lo, int64_t tq_hi,
+                           HeadOut &out)
 {
     const int64_t L = p.L, M = p.block_q, nqb = (L + M - 1) / M;
     const int64_t bh = (int64_t)b * p.H + h;
-    const int64_t base = m.row_ptr[bh * nqb];
-    const int64_t n_all = m.row_ptr[bh * nqb + nqb] - base;
+    const int64_t base = m.row_ptr[bh * nqb + tq_lo];
+    const int64_t n_all = m.row_ptr[bh * nqb + tq_hi] - base;
     out.gidx.assign(m.col_idx + base, m.col_idx + base + n_all);
     out.grows = n_all;
-    for (int64_t i = 0; i < nqb; ++i) {
+    for (int64_t i = tq_lo; i < tq_hi; ++i) {
         const int64_t s = m.row_ptr[bh * nqb + i] - base, e = m.row_ptr[bh * nqb + i + 1] - base;
         Task t{(int32_t)bh, (int32_t)(i * M), (int32_t)out.tiles.size(), 0};
         for (int64_t o = s; o < e; o += kTileK) {
@@ -753,16 +767,25 @@ static int32_t choose_regime(const bsa_mask_desc_t &m, int32_t B, int32_t H, int
     if (o.force_regime >= 0 && o.task_order >= 0) {
         *regime = o.force_regime;
     } else {
-        std::vector<LutRule> rules;
-        std::string err, text = kDefaultLut;
+        // the compiled-in table is parsed once; a table file on every call
+        static const std::vector<LutRule> default_rules = [] {
+            std::vector<LutRule> r;
+            std::string e;
+            if (!parse_lut(kDefaultLut, r, e)) r.clear();
+            return r;
+        }();
+        std::vector<LutRule> file_rules;
+        const std::vector<LutRule> *rules_p = &default_rules;
         if (o.lut_path) {
             std::ifstream f(o.lut_path);
             if (!f) return fail(BSA_ERR_INVALID_ARGUMENT, "cannot read lookup table %s", o.lut_path);
             std::stringstream ss;
             ss << f.rdbuf();
-            text = ss.str();
+            std::string err;
+            if (!parse_lut(ss.str(), file_rules, err)) return fail(BSA_ERR_INVALID_ARGUMENT, "%s", err.c_str());
+            rules_p = &file_rules;
         }
-        if (!parse_lut(text, rules, err)) return fail(BSA_ERR_INVALID_ARGUMENT, "%s", err.c_str());
+        const std::vector<LutRule> &rules = *rules_p;
         const int kind = m.kind == BSA_MASK_BLOCK_BITS ? BSA_MASK_BLOCK_U8 : m.kind;
         const double dens = mask_density(m, B, H, L, bq, bk);
         *regime = -1;
@@ -883,12 +906,11 @@ static int xcd_count()
 // is handed longer tasks than the others would hold them up).
 constexpr double kCostClass = 1.3;
 
-static void group_for_xcds(Task *tasks, int64_t n, int X)
+static void group_for_xcds(Task *tasks, int64_t n, int X, int32_t max_cost)
 {
-    auto cls = [](const Task &t) {
-        const int c = t.te - t.tb;
-        return c <= 0 ? -1 : (int)(std::log((double)c) / std::log(kCostClass));
-    };
+    std::vector<int> cls_of((size_t)max_cost + 1, -1);  // cost class of each tile count
+    for (int32_t c = 1; c <= max_cost; ++c) cls_of[(size_t)c] = (int)(std::log((double)c) / std::log(kCostClass));
+    auto cls = [&](const Task &t) { return cls_of[(size_t)std::max(0, t.te - t.tb)]; };
     std::vector<Task> run;
     for (int64_t a = 0; a < n;) {
         int64_t b = a + 1;
@@ -905,7 +927,7 @@ static void group_for_xcds(Task *tasks, int64_t n, int X)
     }
 }
 
-static int32_t organise_tasks(bsa_plan_s &p, const std::vector<HeadOut *> &heads)
+static int32_t organise_tasks(bsa_plan_s &p, const std::vector<HeadOut *> &heads, const std::vector<int32_t> &head_bh)
 {
     const size_t nh = heads.size();
     std::vector<int64_t> t_off(nh + 1, 0), r_off(nh + 1, 0), g_off(nh + 1, 0);
@@ -964,6 +986,7 @@ static int32_t organise_tasks(bsa_plan_s &p, const std::vector<HeadOut *> &heads
         Task *td = unsorted.data() + t_off[i];
         for (size_t k = 0; k < h.tasks.size(); ++k) {
             Task t = h.tasks[k];
+            t.bh = head_bh[i];  // (a head may share its mapping with another)
             t.tb += toff;
             t.te += toff;
             td[k] = t;
@@ -982,7 +1005,7 @@ static int32_t organise_tasks(bsa_plan_s &p, const std::vector<HeadOut *> &heads
     for (const Task &t : unsorted) ++bucket[(size_t)(max_cost - (t.te - t.tb)) + 1];
     for (size_t c = 1; c < bucket.size(); ++c) bucket[c] += bucket[c - 1];
     for (const Task &t : unsorted) tasks[bucket[(size_t)(max_cost - (t.te - t.tb))]++] = t;
-    if (p.task_order == BSA_ORDER_XCD_GROUPED) group_for_xcds(tasks, nreal, xcd_count());
+    if (p.task_order == BSA_ORDER_XCD_GROUPED) group_for_xcds(tasks, nreal, xcd_count(), max_cost);
     uint32_t *flags = (uint32_t *)(p.img + p.off_flags);
     for (int h = 0; h < p.H; ++h)
         flags[h] = (p.head_layout[h] ? kHeadTemporalMajor : 0u) | ((uint32_t)p.head_pattern[h] << kHeadPatShift) |
@@ -998,16 +1021,32 @@ static int32_t organise_tasks(bsa_plan_s &p, const std::vector<HeadOut *> &heads
             for (int lay = 0; lay < 2; ++lay) {
                 if (table_of[pat][lay] < 0) continue;
                 int32_t *c = coords + table_of[pat][lay] * p.coord_stride;
-                // walk the positions in order with running coordinates (no divisions)
-                int32_t t = 0, y = 0, x = 0;
-                for (int64_t k = 0; k < p.L; ++k) {
-                    c[k] = pat == BSA_PAT_SPATIAL ? t : (pat == BSA_PAT_TEMPORAL ? ((y << 16) | x) : 0);
-                    if (lay) {  // j = pixel * T + frame: frame first, then the pixel
-                        if (++t == p.T) { t = 0; if (++x == p.Wg) { x = 0; ++y; } }
-                    } else {    // token = frame * HW + y * Wg + x
-                        if (++x == p.Wg) { x = 0; if (++y == p.Hg) { y = 0; ++t; } }
+                // chunks of positions in parallel; inside a chunk, running
+                // coordinates (no divisions)
+                constexpr int64_t kChunk = 4096;
+                parallel_for((p.L + kChunk - 1) / kChunk, [&, pat, lay, c](int64_t ci) {
+                    const int64_t k0 = ci * kChunk, k1 = std::min<int64_t>(p.L, k0 + kChunk);
+                    const int64_t HWp = (int64_t)p.Hg * p.Wg;
+                    int32_t t, y, x;
+                    if (lay) {
+                        t = (int32_t)(k0 % p.T);
+                        const int64_t px = k0 / p.T;
+                        y = (int32_t)(px / p.Wg);
+                        x = (int32_t)(px % p.Wg);
+                    } else {
+                        t = (int32_t)(k0 / HWp);
+                        y = (int32_t)((k0 % HWp) / p.Wg);
+                        x = (int32_t)(k0 % p.Wg);
                     }
-                }
+                    for (int64_t k = k0; k < k1; ++k) {
+                        c[k] = pat == BSA_PAT_SPATIAL ? t : (pat == BSA_PAT_TEMPORAL ? ((y << 16) | x) : 0);
+                        if (lay) {  // j = pixel * T + frame: frame first, then the pixel
+                            if (++t == p.T) { t = 0; if (++x == p.Wg) { x = 0; ++y; } }
+                        } else {    // token = frame * HW + y * Wg + x
+                            if (++x == p.Wg) { x = 0; if (++y == p.Hg) { y = 0; ++t; } }
+                        }
+                    }
+                });
                 for (int64_t k = p.L; k < p.coord_stride; ++k) c[k] = 0x7FFF7FFF;
             }
     }
@@ -1147,20 +1186,72 @@ extern "C" int32_t bsa_plan(const bsa_mask_desc_t *logical_mask, int32_t B, int3
         std::unique_ptr<Builder, void (*)(Builder *)> builder_guard(builder, give_builder);
         std::vector<HeadOut> &heads = builder->heads;
         if (heads.size() < (size_t)B * H) heads.resize((size_t)B * H);
-        parallel_for((int64_t)B * H, [&](int64_t bh) {
-            heads[bh].clear();
+        // Heads with identical logical masks share one mapping: video heads of
+        // one pattern and layout (in every batch), and BLOCK heads whose mask
+        // bytes equal the previous head's (a mask broadcast over heads). Only
+        // the first of each group is mapped; the task array takes the others'
+        // tasks and tiles from it.
+        const int64_t NBH = (int64_t)B * H;
+        std::vector<int64_t> src((size_t)NBH);
+        const int64_t nqb_m = (L + block_q - 1) / block_q, nkb_m = (L + block_k - 1) / block_k;
+        const size_t head_bytes = m.kind == BSA_MASK_BLOCK_U8 ? (size_t)(nqb_m * nkb_m)
+                                  : m.kind == BSA_MASK_BLOCK_BITS ? (size_t)(nqb_m * ((nkb_m + 63) / 64)) * 8 : 0;
+        for (int64_t bh = 0; bh < NBH; ++bh) {
+            src[(size_t)bh] = bh;
+            if (p->mode == kModeVideo) {
+                const int h = (int)(bh % H);
+                for (int64_t o = 0; o < bh; ++o) {
+                    const int ho = (int)(o % H);
+                    if (src[(size_t)o] == o && p->head_pattern[ho] == p->head_pattern[h] && p->head_layout[ho] == p->head_layout[h]) {
+                        src[(size_t)bh] = o;
+                        break;
+                    }
+                }
+            } else if (p->mode == kModeBlock && bh > 0) {
+                const uint8_t *d = (const uint8_t *)m.data;
+                if (std::memcmp(d + (size_t)(bh - 1) * head_bytes, d + (size_t)bh * head_bytes, head_bytes) == 0)
+                    src[(size_t)bh] = src[(size_t)(bh - 1)];
+            }
+        }
+        // work items: chunks of kMapChunk query tiles of the heads to map, so
+        // that a few distinct heads still spread over all worker threads
+        constexpr int64_t kMapChunk = 16;
+        const int64_t nqt = p->mode == kModeGather ? (L + block_q - 1) / block_q : (L + R.tile_q - 1) / R.tile_q;
+        const int64_t per_head = (nqt + kMapChunk - 1) / kMapChunk;
+        std::vector<int64_t> first_item((size_t)NBH, -1);
+        int64_t nitems = 0;
+        for (int64_t bh = 0; bh < NBH; ++bh)
+            if (src[(size_t)bh] == bh) { first_item[(size_t)bh] = nitems; nitems += per_head; }
+        if (heads.size() < (size_t)nitems) heads.resize((size_t)nitems);
+        std::vector<int64_t> item_head((size_t)nitems);
+        for (int64_t bh = 0; bh < NBH; ++bh)
+            for (int64_t c = 0; first_item[(size_t)bh] >= 0 && c < per_head; ++c) item_head[(size_t)(first_item[(size_t)bh] + c)] = bh;
+        parallel_for(nitems, [&](int64_t it) {
+            HeadOut &out = heads[(size_t)it];
+            out.clear();
+            const int64_t bh = item_head[(size_t)it], c = it - first_item[(size_t)bh];
+            const int64_t lo = c * kMapChunk, hi = std::min(nqt, lo + kMapChunk);
             const int b = (int)(bh / H), h = (int)(bh % H);
-            if (p->mode == kModeBlock) map_block_head(*p, m, b, h, R.tile_q, heads[bh]);
-            else if (p->mode == kModeVideo) map_video_head(*p, b, h, R.tile_q, heads[bh]);
-            else map_slice_head(*p, m, b, h, heads[bh]);
+            if (p->mode == kModeBlock) map_block_head(*p, m, b, h, R.tile_q, lo, hi, out);
+            else if (p->mode == kModeVideo) map_video_head(*p, b, h, R.tile_q, lo, hi, out);
+            else map_slice_head(*p, m, b, h, lo, hi, out);
         });
         size_t total_tiles = 0;
-        for (int64_t i = 0; i < (int64_t)B * H; ++i) total_tiles += heads[i].tiles.size();
+        for (int64_t i = 0; i < NBH; ++i)
+            for (int64_t c = 0; c < per_head; ++c) total_tiles += heads[(size_t)(first_item[(size_t)src[(size_t)i]] + c)].tiles.size();
         if (total_tiles >= (size_t)INT32_MAX) return fail(BSA_ERR_UNSUPPORTED, "plan has more than 2^31 tiles");
         t_map = now_ns();
-        std::vector<HeadOut *> hp((size_t)B * H);
-        for (int64_t i = 0; i < (int64_t)B * H; ++i) hp[i] = &heads[i];
-        st = organise_tasks(*p, hp);
+        // the task array takes every head's chunks in (head, query tile) order
+        std::vector<HeadOut *> hp;
+        std::vector<int32_t> hp_bh;
+        hp.reserve((size_t)(NBH * per_head));
+        hp_bh.reserve((size_t)(NBH * per_head));
+        for (int64_t i = 0; i < NBH; ++i)
+            for (int64_t c = 0; c < per_head; ++c) {
+                hp.push_back(&heads[(size_t)(first_item[(size_t)src[(size_t)i]] + c)]);
+                hp_bh.push_back((int32_t)i);
+            }
+        st = organise_tasks(*p, hp, hp_bh);
         t_tasks = now_ns();
         if (st == BSA_OK) st = upload(*p);
         if (st != BSA_OK) {

@@ -334,7 +334,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1
             __builtin_amdgcn_sched_group_barrier(0x008, 4 * RB, 0);
 
             // ---- exact mask on PARTIAL tiles only
-            if (wave_masks_tile(a, rec.aux, w)) mask_partial_tile<RB>(s0, s1, a, rec.k0, rec.aux, video, pat, LDS_PTR(const int, &kcoord[cur][4 * hf]), qt, qwin, q, task.q0, hf);
+            if (wave_masks_tile(a, rec.aux, w)) mask_partial_tile<RB>(s0, s1, a, rec.k0, rec.aux, video, pat, LDS_PTR(const int, &kcoord[cur][4 * hf]), qt, qwin, 32 * w * RB, hf);
 
             // ---- online softmax per row block
             u32x4 pk[RB][4];  // bf16 pairs, one cvt_pk each

@@ -126,7 +126,7 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_f32(KernelArgs a)
             // ---- exact mask on PARTIAL tiles only
             if (wave_masks_tile(a, rec.aux, w))
                 mask_partial_tile<1>(s0, s1, a, rec.k0, rec.aux, video, pat, LDS_PTR(const int, &kcoord[4 * hf]), qt,
-                                     qwin, q, task.q0, hf);
+                                     qwin, 32 * w, hf);
 
             // ---- online softmax (reference max moves only by more than kSlack)
             float mx = fmaxf(s0[0][0], s1[0][0]);

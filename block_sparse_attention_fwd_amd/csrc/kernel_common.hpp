@@ -176,8 +176,7 @@ __device__ __forceinline__ bool wave_masks_tile(const KernelArgs &a, uint32_t au
 template <int RB>
 __device__ __forceinline__ void mask_partial_tile(f32x16 (&s0)[RB], f32x16 (&s1)[RB], const KernelArgs &a,
                                                   int rec_k0, uint32_t rec_aux, bool video, int pat, const __attribute__((address_space(3))) int *kc,
-                                                  const int (&qt)[RB], const unsigned (&qwin)[RB], const int (&q)[RB],
-                                                  int q0, int hf)
+                                                  const int (&qt)[RB], const unsigned (&qwin)[RB], int wrow0, int hf)
 {
     if (video) {
         const unsigned win2 = 2u * (unsigned)a.radius;
@@ -235,7 +234,9 @@ __device__ __forceinline__ void mask_partial_tile(f32x16 (&s0)[RB], f32x16 (&s1)
     for (int rb = 0; rb < RB; ++rb) {
         uint32_t lo = vlo, hi = vhi;
         if (a.mode == kModeBlock) {
-            const int sq = (q[rb] - q0) >> a.bq_shift;
+            // logical blocks are at least 32 queries tall, so a 32-row block
+            // (rows wrow0 + 32 rb .. + 31 of the task) lies in one sub-block row
+            const int sq = (wrow0 + 32 * rb) >> a.bq_shift;
             const uint32_t rowbits = rec_aux >> (sq * a.nsk);
             lo &= (rowbits & 1u) ? ~0u : 0u;
             hi &= ((rowbits >> (a.nsk - 1)) & 1u) ? ~0u : 0u;
