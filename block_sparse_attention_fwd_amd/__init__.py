@@ -31,7 +31,7 @@ PRED_NONE, PRED_SUBBLOCK, PRED_VIDEO, PRED_LIST = 0, 1, 2, 3
 ORDER_XCD_GROUPED, ORDER_LONGEST_FIRST = 0, 1
 ABI_VERSION = 2  # the structures below mirror this version of bsa.h
 
-EXPORTED = ["bsa_abi_version", "bsa_plan_opts_default", "bsa_plan", "bsa_forward", "bsa_plan_destroy",
+EXPORTED = ["bsa_abi_version", "bsa_plan_opts_default", "bsa_plan", "bsa_plan_device", "bsa_forward", "bsa_plan_destroy",
             "bsa_plan_info", "bsa_plan_coverage", "bsa_regime_count", "bsa_regime_info", "bsa_status_str",
             "bsa_last_error"]
 
@@ -102,6 +102,10 @@ def lib(path: str = LIB_PATH):
     L.bsa_plan.restype = ctypes.c_int32
     L.bsa_plan.argtypes = [ctypes.POINTER(MaskDesc), ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
                            ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(PlanOpts), ctypes.POINTER(ctypes.c_void_p)]
+    L.bsa_plan_device.restype = ctypes.c_int32
+    L.bsa_plan_device.argtypes = [ctypes.POINTER(MaskDesc), ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                  ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(PlanOpts),
+                                  ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p)]
     L.bsa_forward.restype = ctypes.c_int32
     L.bsa_forward.argtypes = [ctypes.c_void_p] * 6
     L.bsa_plan_destroy.argtypes = [ctypes.c_void_p]
@@ -222,15 +226,54 @@ def plan(kind: int, B: int, H: int, L: int, d: int, block_q: int, block_k: int, 
     return Plan(h.value, L, H, B)
 
 
+def _stream_handle(stream) -> int:
+    """hipStream_t of a torch stream, a raw handle (int), or None (the
+    current torch stream)."""
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def plan_device(kind: int, B: int, H: int, L: int, d: int, block_q: int, block_k: int, data, *, stream=None,
+                dtype: int = DTYPE_BF16, T: int = 0, Hg: int = 0, Wg: int = 0, head_layout=None,
+                force_regime: int = -1, lut_path: Optional[str] = None, device: int = 0,
+                task_order: int = -1) -> Plan:
+    """bsa_plan_device: build a plan on the device from a BLOCK mask in device
+    memory (a contiguous torch tensor, or a raw device address: bytes for
+    BLOCK_U8, 64-bit rows for BLOCK_BITS), enqueued on `stream`. The returned
+    plan keeps a reference to the mask tensor."""
+    L_ = lib()
+    keep = []
+    m = MaskDesc()
+    m.kind = kind
+    m.data = _dptr(data)
+    o = PlanOpts()
+    L_.bsa_plan_opts_default(ctypes.byref(o))
+    o.dtype = dtype
+    o.T, o.Hg, o.Wg = T, Hg, Wg
+    if head_layout is not None:
+        hl = np.ascontiguousarray(head_layout, dtype=np.uint8)
+        keep.append(hl)
+        o.head_layout = _ptr(hl)
+    o.force_regime = force_regime
+    o.lut_path = lut_path.encode() if lut_path else None
+    o.device = device
+    o.task_order = task_order
+    h = ctypes.c_void_p()
+    _check(L_.bsa_plan_device(ctypes.byref(m), B, H, L, d, block_q, block_k, ctypes.byref(o), _stream_handle(stream),
+                              ctypes.byref(h)))
+    pl = Plan(h.value, L, H, B)
+    pl._mask = data
+    return pl
+
+
 def forward(p: Plan, q, k, v, o, stream=None) -> None:
     """bsa_forward: enqueue the forward pass on `stream` (torch stream, raw
     hipStream_t as int, or None for the current torch stream)."""
-    if stream is None:
-        import torch
-        stream = torch.cuda.current_stream().cuda_stream
-    elif not isinstance(stream, int):
-        stream = stream.cuda_stream
-    _check(lib().bsa_forward(p.handle, _dptr(q), _dptr(k), _dptr(v), _dptr(o), stream))
+    _check(lib().bsa_forward(p.handle, _dptr(q), _dptr(k), _dptr(v), _dptr(o), _stream_handle(stream)))
 
 
 def regimes():

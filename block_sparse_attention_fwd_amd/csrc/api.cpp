@@ -41,6 +41,7 @@
 
 #include "../../include/bsa.h"
 #include "mempool.hpp"
+#include "plan_device.hpp"
 #include "plan_format.hpp"
 
 namespace bsa {
@@ -213,6 +214,15 @@ struct bsa_plan_s {
     void *dev = nullptr;
     size_t dev_cap = 0;
     hipEvent_t uploaded = nullptr;
+    // plans built on the device (bsa_plan_device): the image exists only in
+    // device memory until a host query reads back its statistics (and, for
+    // the coverage, the task and record sections)
+    bool device_planned = false;
+    bool stats_read = false;
+    bool host_copy = false;
+    size_t off_stats = 0;
+    uint8_t *small = nullptr;  // pinned upload source of the head flags and cost classes
+    size_t small_cap = 0;
 };
 
 static int ilog2(int v)
@@ -641,7 +651,7 @@ static void map_slice_head(const bsa_plan_s &p, const bsa_mask_desc_t &m, int b,
 // ---------------------------------------------------------------------------
 
 static int32_t validate(const bsa_mask_desc_t *m, int32_t B, int32_t H, int64_t L, int32_t d, int32_t bq, int32_t bk,
-                        const bsa_plan_opts_t &o)
+                        const bsa_plan_opts_t &o, bool device_mask = false)
 {
     if (!m) return fail(BSA_ERR_INVALID_ARGUMENT, "logical_mask is NULL");
     if (B < 1 || H < 1 || L < 1) return fail(BSA_ERR_INVALID_ARGUMENT, "B, H, L must be >= 1 (got %d, %d, %lld)", B, H, (long long)L);
@@ -674,7 +684,7 @@ static int32_t validate(const bsa_mask_desc_t *m, int32_t B, int32_t H, int64_t 
         if (!m->data) return fail(BSA_ERR_INVALID_ARGUMENT, "block mask data is NULL");
         if (!is_pow2(bq) || !is_pow2(bk) || bq < 32 || bk < 32 || bq > 1024 || bk > 1024)
             return fail(BSA_ERR_UNSUPPORTED, "block shape %d x %d (supported: powers of two in [32, 1024])", bq, bk);
-        if (m->kind == BSA_MASK_BLOCK_BITS) {
+        if (m->kind == BSA_MASK_BLOCK_BITS && !device_mask) {
             const int64_t nqb = (L + bq - 1) / bq, nkb = (L + bk - 1) / bk, words = (nkb + 63) / 64;
             if (nkb % 64) {
                 const uint64_t stray = ~0ull << (nkb % 64);
@@ -761,7 +771,7 @@ static double mask_density(const bsa_mask_desc_t &m, int32_t B, int32_t H, int64
 }
 
 static int32_t choose_regime(const bsa_mask_desc_t &m, int32_t B, int32_t H, int64_t L, int32_t bq, int32_t bk,
-                             const bsa_plan_opts_t &o, int *regime, int *order)
+                             const bsa_plan_opts_t &o, int *regime, int *order, bool density_known = true)
 {
     *order = BSA_ORDER_XCD_GROUPED;
     if (o.force_regime >= 0 && o.task_order >= 0) {
@@ -787,7 +797,7 @@ static int32_t choose_regime(const bsa_mask_desc_t &m, int32_t B, int32_t H, int
         }
         const std::vector<LutRule> &rules = *rules_p;
         const int kind = m.kind == BSA_MASK_BLOCK_BITS ? BSA_MASK_BLOCK_U8 : m.kind;
-        const double dens = mask_density(m, B, H, L, bq, bk);
+        const double dens = density_known ? mask_density(m, B, H, L, bq, bk) : -1.0;
         *regime = -1;
         for (const LutRule &r : rules) {
             if (r.kind != kind) continue;
@@ -1097,6 +1107,8 @@ static void release_plan_memory(bsa_plan_s *p)
     }
     if (p->img && p->img_pinned) pinned_pool().release(p->img, p->img_cap);
     p->img = nullptr;
+    if (p->small) pinned_pool().release(p->small, p->small_cap);
+    p->small = nullptr;
 }
 
 // Reused per-head mapping buffers (their capacity survives across plans).
@@ -1276,6 +1288,200 @@ extern "C" int32_t bsa_plan(const bsa_mask_desc_t *logical_mask, int32_t B, int3
     }
 }
 
+// ---------------------------------------------------------------------------
+// device-side planning (BLOCK masks in device memory)
+// ---------------------------------------------------------------------------
+
+extern "C" int32_t bsa_plan_device(const bsa_mask_desc_t *logical_mask, int32_t B, int32_t H, int64_t L, int32_t d,
+                                   int32_t block_q, int32_t block_k, const bsa_plan_opts_t *opts, void *stream,
+                                   bsa_plan_t *out_plan)
+{
+    if (!out_plan) return fail(BSA_ERR_INVALID_ARGUMENT, "out_plan is NULL");
+    *out_plan = nullptr;
+    const auto t_start = std::chrono::steady_clock::now();
+    try {
+        bsa_plan_opts_t o;
+        bsa_plan_opts_default(&o);
+        if (opts) o = *opts;
+        if (!logical_mask) return fail(BSA_ERR_INVALID_ARGUMENT, "logical_mask is NULL");
+        if (logical_mask->kind != BSA_MASK_BLOCK_U8 && logical_mask->kind != BSA_MASK_BLOCK_BITS)
+            return fail(BSA_ERR_UNSUPPORTED, "device planning takes BLOCK masks (kind %d)", logical_mask->kind);
+        if (o.device < 0) return fail(BSA_ERR_INVALID_ARGUMENT, "device planning needs a device (opts.device = %d)", o.device);
+        int32_t st = validate(logical_mask, B, H, L, d, block_q, block_k, o, true);
+        if (st != BSA_OK) return st;
+        const bsa_mask_desc_t &m = *logical_mask;
+        int regime = 0, order = 0;
+        st = choose_regime(m, B, H, L, block_q, block_k, o, &regime, &order, false);
+        if (st != BSA_OK) return st;
+        const Regime &R = kRegimes[regime];
+
+        std::unique_ptr<bsa_plan_s> p(new bsa_plan_s);
+        p->B = B; p->H = H; p->L = L; p->d = d; p->dtype = o.dtype;
+        p->kind = m.kind; p->block_q = block_q; p->block_k = block_k;
+        p->regime = regime;
+        p->T = o.T; p->Hg = o.Hg; p->Wg = o.Wg;
+        p->device = o.device;
+        p->task_order = order;
+        p->head_layout.assign(H, 0);
+        if (o.head_layout) p->head_layout.assign(o.head_layout, o.head_layout + H);
+        p->head_pattern.assign(H, 0);
+        p->mode = kModeBlock;
+        p->sub_q = std::min(block_q, R.tile_q);
+        p->sub_k = std::min(block_k, kTileK);
+        p->bq_shift = ilog2(p->sub_q);
+        p->bk_shift = ilog2(p->sub_k);
+        p->nsk = kTileK / p->sub_k;
+        p->device_planned = true;
+
+        const int64_t nqt = (L + R.tile_q - 1) / R.tile_q, nkt = (L + kTileK - 1) / kTileK;
+        const int64_t NT = (int64_t)B * H * nqt, cap = NT * nkt;
+        if (cap >= (int64_t)INT32_MAX) return fail(BSA_ERR_UNSUPPORTED, "device plan capacity above 2^31 tiles");
+        if (NT >= ((int64_t)1 << 24)) return fail(BSA_ERR_UNSUPPORTED, "device planning of more than 2^24 tasks");
+        p->ntasks = p->nreal_tasks = NT;
+        p->ntiles = -1;  // known once read back
+
+        // cost classes of tile counts: the same table as the host's XCD grouping;
+        // plain longest first is the class = count case on one XCD
+        const bool grouped = order == BSA_ORDER_XCD_GROUPED;
+        const int64_t nchunks = (NT + kDevPlanChunk - 1) / kDevPlanChunk;
+        const size_t small_bytes = (size_t)H * sizeof(uint32_t) + (size_t)(nkt + 1) * sizeof(int32_t);
+        p->small = (uint8_t *)pinned_pool().acquire(small_bytes, &p->small_cap);
+        if (!p->small) return fail(BSA_ERR_OUT_OF_MEMORY, "pinned host allocation of %zu bytes failed", small_bytes);
+        uint32_t *flags = (uint32_t *)p->small;
+        for (int h = 0; h < H; ++h) flags[h] = p->head_layout[h] ? kHeadTemporalMajor : 0u;
+        int32_t *cls_of = (int32_t *)(p->small + (size_t)H * sizeof(uint32_t));
+        cls_of[0] = -1;
+        int32_t nclass = 0;
+        for (int64_t c = 1; c <= nkt; ++c) {
+            cls_of[c] = grouped ? (int32_t)(std::log((double)c) / std::log(kCostClass)) : (int32_t)c;
+            nclass = std::max(nclass, cls_of[c] + 1);
+        }
+        const int32_t nkeys = nclass + 1;
+        if (nkeys > kDevPlanMaxKeys) {
+            release_plan_memory(p.get());
+            return fail(BSA_ERR_UNSUPPORTED, "device planning in longest-first order of more than %d key tiles",
+                        kDevPlanMaxKeys - 2);
+        }
+
+        // device image: the host plan's sections (each task's tile records at
+        // its worst-case size, task t's from record t * nkt), then the
+        // planner's scratch
+        p->off_tasks = 0;
+        p->off_tiles = align_up((size_t)std::max<int64_t>(1, NT) * sizeof(Task));
+        p->off_gidx = p->off_tiles + align_up((size_t)std::max<int64_t>(1, cap) * sizeof(TileRec));
+        p->off_flags = p->off_gidx + align_up(sizeof(int32_t));
+        p->off_coords = p->off_flags + align_up((size_t)H * sizeof(uint32_t));
+        const size_t off_cnt = p->off_coords + align_up(sizeof(int32_t));
+        const size_t off_full = off_cnt + align_up((size_t)NT * sizeof(int32_t));
+        const size_t off_hist = off_full + align_up((size_t)NT * sizeof(int32_t));
+        const size_t off_csum = off_hist + align_up((size_t)(nkeys * nchunks + 1) * sizeof(int32_t));
+        const size_t off_cls = off_csum + align_up((size_t)nchunks * 2 * sizeof(int64_t));
+        p->off_stats = off_cls + align_up((size_t)(nkt + 1) * sizeof(int32_t));
+        p->img_bytes = p->off_stats + align_up(3 * sizeof(int64_t));
+
+        int cur = 0;
+        (void)hipGetDevice(&cur);
+        hipError_t e = hipSetDevice(p->device);
+        if (e != hipSuccess) return fail(BSA_ERR_HIP, "hipSetDevice(%d): %s", p->device, hipGetErrorString(e));
+        std::string err;
+        DeviceRt *rt = device_rt(p->device, err);
+        if (!rt) st = fail(BSA_ERR_HIP, "%s", err.c_str());
+        else if (!(p->dev = rt->pool->acquire(p->img_bytes, &p->dev_cap)))
+            st = fail(BSA_ERR_OUT_OF_MEMORY, "device allocation of %zu bytes failed", p->img_bytes);
+        else if ((e = hipEventCreateWithFlags(&p->uploaded, hipEventDisableTiming)) != hipSuccess) {
+            p->uploaded = nullptr;
+            st = fail(BSA_ERR_HIP, "hipEventCreateWithFlags: %s", hipGetErrorString(e));
+        }
+        if (st == BSA_OK) {
+            uint8_t *dv = (uint8_t *)p->dev;
+            const hipStream_t s = (hipStream_t)stream;
+            DevPlanArgs a{};
+            a.u8 = m.kind == BSA_MASK_BLOCK_U8 ? (const uint8_t *)m.data : nullptr;
+            a.bits = m.kind == BSA_MASK_BLOCK_BITS ? (const uint64_t *)m.data : nullptr;
+            a.L = L;
+            a.BQ = R.tile_q;
+            a.bq = block_q;
+            a.bk = block_k;
+            a.bqe = p->sub_q;
+            a.bke = p->sub_k;
+            a.nsq = R.tile_q / p->sub_q;
+            a.nsk = p->nsk;
+            a.lbq = ilog2(block_q);
+            a.lbk = ilog2(block_k);
+            a.lbqe = p->bq_shift;
+            a.lbke = p->bk_shift;
+            a.nqb = (L + block_q - 1) / block_q;
+            a.nkb = (L + block_k - 1) / block_k;
+            a.words = (a.nkb + 63) / 64;
+            a.nqt = nqt;
+            a.nkt = nkt;
+            a.ntasks = NT;
+            a.nchunks = nchunks;
+            a.cnt = (int32_t *)(dv + off_cnt);
+            a.full = (int32_t *)(dv + off_full);
+            a.hist = (int32_t *)(dv + off_hist);
+            a.csum = (int64_t *)(dv + off_csum);
+            a.tasks = (Task *)(dv + p->off_tasks);
+            a.tiles = (TileRec *)(dv + p->off_tiles);
+            a.cls_of = (const int32_t *)(dv + off_cls);
+            a.nclass = nclass;
+            a.nkeys = nkeys;
+            a.X = grouped ? xcd_count() : 1;
+            a.stats = (int64_t *)(dv + p->off_stats);
+            if ((e = hipMemcpyAsync(dv + p->off_flags, flags, (size_t)H * sizeof(uint32_t), hipMemcpyHostToDevice, s)) != hipSuccess ||
+                (e = hipMemcpyAsync(dv + off_cls, cls_of, (size_t)(nkt + 1) * sizeof(int32_t), hipMemcpyHostToDevice, s)) != hipSuccess ||
+                (e = launch_device_plan(a, s)) != hipSuccess || (e = hipEventRecord(p->uploaded, s)) != hipSuccess)
+                st = fail(BSA_ERR_HIP, "device planning: %s", hipGetErrorString(e));
+        }
+        (void)hipSetDevice(cur);
+        if (st != BSA_OK) {
+            release_plan_memory(p.get());
+            return st;
+        }
+        p->plan_ns = (int64_t)std::chrono::duration_cast<std::chrono::nanoseconds>(std::chrono::steady_clock::now() - t_start).count();
+        *out_plan = p.release();
+        return BSA_OK;
+    } catch (const std::bad_alloc &) {
+        return fail(BSA_ERR_OUT_OF_MEMORY, "host allocation failed while planning");
+    } catch (const std::exception &ex) {
+        return fail(BSA_ERR_INTERNAL, "%s", ex.what());
+    }
+}
+
+// Host view of a device-built plan: waits for the planning kernels, then
+// reads back the statistics and, with `image`, the task and record sections.
+static int32_t read_back_device_plan(bsa_plan_s *p, bool image)
+{
+    if (!p->device_planned || (p->stats_read && (!image || p->host_copy))) return BSA_OK;
+    int cur = 0;
+    (void)hipGetDevice(&cur);
+    (void)hipSetDevice(p->device);
+    hipError_t e = hipEventSynchronize(p->uploaded);
+    if (e == hipSuccess && !p->stats_read) {
+        int64_t stats[3] = {0, 0, 0};
+        e = hipMemcpy(stats, (uint8_t *)p->dev + p->off_stats, sizeof stats, hipMemcpyDeviceToHost);
+        if (e == hipSuccess) {
+            p->ntiles = stats[0];
+            p->tiles_full = stats[1];
+            p->tiles_partial = stats[0] - stats[1];
+            p->tiles_empty = stats[2];
+            p->stats_read = true;
+        }
+    }
+    if (e == hipSuccess && image && !p->host_copy) {
+        p->img_vec.assign(p->off_gidx, 0);
+        e = hipMemcpy(p->img_vec.data(), p->dev, p->img_vec.size(), hipMemcpyDeviceToHost);
+        if (e == hipSuccess) {
+            p->img = p->img_vec.data();
+            p->img_cap = p->img_vec.size();
+            p->host_copy = true;
+        }
+    }
+    (void)hipSetDevice(cur);
+    if (e != hipSuccess) return fail(BSA_ERR_HIP, "reading back a device plan: %s", hipGetErrorString(e));
+    return BSA_OK;
+}
+
 extern "C" void bsa_plan_destroy(bsa_plan_t p)
 {
     if (!p) return;
@@ -1341,6 +1547,7 @@ extern "C" int32_t bsa_forward(bsa_plan_t p, const void *Q, const void *K, const
 extern "C" int32_t bsa_plan_info(bsa_plan_t p, bsa_plan_info_t *out)
 {
     if (!p || !out) return fail(BSA_ERR_INVALID_ARGUMENT, "plan or out is NULL");
+    if (int32_t st = read_back_device_plan(p, false); st != BSA_OK) return st;
     const Regime &R = kRegimes[p->regime];
     out->regime = p->regime;
     out->tile_q = R.tile_q;
@@ -1364,6 +1571,7 @@ extern "C" int32_t bsa_plan_coverage(bsa_plan_t p, int32_t b, int32_t h, bsa_cov
 {
     if (!p || !sink) return fail(BSA_ERR_INVALID_ARGUMENT, "plan or sink is NULL");
     if (b < 0 || b >= p->B || h < 0 || h >= p->H) return fail(BSA_ERR_INVALID_ARGUMENT, "head (%d, %d) out of range", b, h);
+    if (int32_t st = read_back_device_plan(p, true); st != BSA_OK) return st;
     const Regime &R = kRegimes[p->regime];
     const int32_t bh = b * p->H + h;
     const Task *tasks = p->tasks();

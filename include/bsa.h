@@ -195,6 +195,30 @@ int32_t bsa_plan(const bsa_mask_desc_t *logical_mask, int32_t B, int32_t H, int6
                  int32_t block_q, int32_t block_k, const bsa_plan_opts_t *opts, bsa_plan_t *out_plan);
 
 /*
+ * Build a plan on the device for a BLOCK mask (BLOCK_U8 or BLOCK_BITS) whose
+ * data is already in DEVICE memory (logical_mask->data is a device pointer
+ * of the layout described above): the tile mapping and the task order run as
+ * kernels on `stream` (a hipStream_t; NULL = the default stream of
+ * opts->device), with no copy of the mask to the host (Tessera, arXiv
+ * 2609.25869, abstract: dynamic masks, preparation kept cheap). Returns after
+ * enqueueing; a bsa_forward on the same stream runs after the planning, one
+ * on another stream waits for it. The mask must stay valid until the planning
+ * work has run. The plan equals the one bsa_plan builds from the same mask,
+ * except that the regime and order come from the table without the mask
+ * density, and bits past the last key block of a BLOCK_BITS row are ignored.
+ * Device memory: every task has room for a record per key tile (8 bytes per
+ * (task, key tile) pair). bsa_plan_info waits for the planning work and reads
+ * back its statistics; bsa_plan_coverage also reads back the task and record
+ * arrays. Errors: INVALID_ARGUMENT (as bsa_plan; host-only device -1),
+ * UNSUPPORTED (other mask kinds, 2^31 or more (task, key tile) pairs, 2^24 or
+ * more tasks, the longest-first order with more than 8190 key tiles),
+ * OUT_OF_MEMORY, HIP.
+ */
+int32_t bsa_plan_device(const bsa_mask_desc_t *logical_mask, int32_t B, int32_t H, int64_t L, int32_t d,
+                        int32_t block_q, int32_t block_k, const bsa_plan_opts_t *opts, void *stream,
+                        bsa_plan_t *out_plan);
+
+/*
  * Enqueue the forward pass of `plan` on `stream` (a hipStream_t; NULL = the
  * default stream of the plan's device). Q, K, V, O as described above. Never
  * synchronises and never allocates; returns after the launch. Launch errors

@@ -22,3 +22,18 @@ def plan_workload(w, device=0, force_regime=-1, bits=False, lut_path=None, dtype
 
 def tok_of_logical(T, HW):
     return np.arange(T * HW).reshape(T, HW).T.reshape(-1)
+
+
+def plan_workload_device(w, device=0, force_regime=-1, bits=False, lut_path=None, dtype=bsa.DTYPE_BF16,
+                         task_order=-1, stream=None, mask=None):
+    """bsa_plan_device on a BLOCK workload: the mask is first copied to the
+    device (or taken from ``mask``, a device tensor of the kind's layout)."""
+    import torch
+    assert w.kind == wl.BLOCK
+    kind = bsa.MASK_BLOCK_BITS if bits else bsa.MASK_BLOCK_U8
+    if mask is None:
+        host = w.block_bits().view(np.int64) if bits else np.ascontiguousarray(w.block, dtype=np.uint8)
+        mask = torch.from_numpy(host).to(f"cuda:{device}")
+    return bsa.plan_device(kind, w.B, w.H, w.L, w.d, w.bq, w.bk, mask, stream=stream, dtype=dtype, T=w.T, Hg=w.Hg,
+                           Wg=w.Wg, head_layout=w.head_layout, force_regime=force_regime, lut_path=lut_path,
+                           device=device, task_order=task_order)

@@ -110,6 +110,20 @@ def test_forward_rejects_host_only_plan_and_null_pointers():
     L.bsa_plan_destroy(None)  # NULL-safe
 
 
+def test_device_planning_argument_errors():
+    """bsa_plan_device rejects what it cannot plan before touching the device
+    (the mask address is never read here)."""
+    PD = bsa.plan_device
+    expect(bsa.ERR_UNSUPPORTED, PD, bsa.MASK_VIDEO, 1, 2, 256, 64, 1, 1, 16, stream=0, match="BLOCK")
+    expect(bsa.ERR_UNSUPPORTED, PD, bsa.MASK_SLICE_CSR, 1, 2, 256, 64, 64, 1, 16, stream=0, match="BLOCK")
+    expect(bsa.ERR_INVALID_ARGUMENT, PD, bsa.MASK_BLOCK_U8, 1, 2, 256, 64, 64, 64, 16, stream=0, device=-1,
+           match="device")
+    expect(bsa.ERR_INVALID_ARGUMENT, PD, bsa.MASK_BLOCK_U8, 1, 2, 256, 64, 64, 64, 0, stream=0, match="NULL")
+    expect(bsa.ERR_UNSUPPORTED, PD, bsa.MASK_BLOCK_U8, 1, 2, 256, 64, 48, 64, 16, stream=0, match="block shape")
+    L = bsa.lib()
+    assert L.bsa_plan_device(None, 1, 1, 64, 64, 64, 64, None, None, None) == bsa.ERR_INVALID_ARGUMENT
+
+
 def test_simulated_allocation_failure(monkeypatch):
     monkeypatch.setenv("BSA_TEST_FAIL_ALLOC", "1")
     expect(bsa.ERR_OUT_OF_MEMORY, bsa.plan, bsa.MASK_BLOCK_U8, 1, 2, 256, 64, 64, 64, data=_block(), device=-1)

@@ -1,0 +1,199 @@
+"""Device-side planning (bsa_plan_device) of BLOCK masks held in device memory.
+
+The plan the kernels build is checked against the host planner's plan of the
+same mask, which the plan-exactness tests pin to the brute-force mapping and
+the parity tests to the fp64 oracle: the same statistics, the same tile
+records of every head in the same launch slots (so the same task order), and
+bit-identical forward outputs. Plans whose regime comes from the lookup table
+(chosen without the mask density) are checked against the oracle directly."""
+import time
+
+import numpy as np
+import pytest
+
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_sparse_attention_fwd_amd as bsa
+    bsa.lib()
+
+
+import block_sparse_attention_fwd_amd as bsa  # noqa: E402
+from bsa_helpers import plan_workload, plan_workload_device  # noqa: E402
+from gpu_util import compare, compare_f32, log, run_gpu, sample_rows, to_device  # noqa: E402
+
+ORDERS = [bsa.ORDER_XCD_GROUPED, bsa.ORDER_LONGEST_FIRST]
+INFO_KEYS = ("regime", "tile_q", "tile_k", "gather", "tasks", "workgroups", "tiles_full", "tiles_partial",
+             "tiles_empty", "gather_rows", "executed_pairs", "task_order")
+
+
+def _same_plan(w, ph, pd, heads=None):
+    ih, idv = ph.info(), pd.info()
+    for k in INFO_KEYS:
+        assert ih[k] == idv[k], (k, ih[k], idv[k])
+    heads = heads if heads is not None else [(b, h) for b in range(w.B) for h in range(w.H)]
+    for b, h in heads:
+        assert ph.coverage(b, h) == pd.coverage(b, h), (b, h)
+
+
+def _ragged_cases():
+    g = np.random.default_rng(23)
+    out = []
+    for (bq, bk) in [(64, 64), (32, 32), (128, 128), (64, 256), (256, 32), (32, 128)]:
+        T, Hg, Wg = 3, 10, 11
+        L = T * Hg * Wg  # 330: ragged for every tile and block size
+        w = wl.Workload(f"blk{bq}x{bk}", 90, 2, 2, L, 64, T, Hg, Wg, wl.BLOCK, bq, bk)
+        w.block = (g.random((2, 2, w.nqb, w.nkb)) < 0.4).astype(np.uint8)
+        w.block[0, 1, 0, :] = 0      # a query block with no kept key
+        w.block[1, 0] = 1            # a dense head
+        w.block[1, 1] = w.block[1, 0]  # a head equal to the previous one
+        w.head_layout = np.array([0, 1], np.uint8)
+        out.append(w)
+    return out
+
+
+@pytest.mark.parametrize("w", _ragged_cases(), ids=lambda w: w.name)
+@pytest.mark.parametrize("regime", [0, 1, 4])
+def test_device_plan_equals_host_plan(w, regime):
+    for bits in (False, True):
+        for order in ORDERS:
+            log(f"[case] {w.name} regime={regime} order={order} bits={bits}")
+            ph = plan_workload(w, force_regime=regime, bits=bits, task_order=order)
+            pd = plan_workload_device(w, force_regime=regime, bits=bits, task_order=order)
+            _same_plan(w, ph, pd)
+
+
+@pytest.mark.parametrize("w", _ragged_cases()[:3], ids=lambda w: w.name)
+def test_device_plan_forward_matches_oracle(w):
+    Q, K, V = wl.make_qkv(w)
+    for regime in (-1, 0, 4):
+        log(f"[case] {w.name} device plan regime={regime}")
+        pd = plan_workload_device(w, force_regime=regime)
+        O, _ = run_gpu(w, Q, K, V, plan=pd)
+        compare(w, Q, K, V, O, label=f"{w.name} device plan r{regime}")
+        if regime >= 0:
+            Oh, _ = run_gpu(w, Q, K, V, plan=plan_workload(w, force_regime=regime))
+            assert np.array_equal(O, Oh)
+
+
+def test_device_plan_f32():
+    w = _ragged_cases()[0]
+    Q, K, V = wl.make_qkv(w, dtype="f32")
+    log("[case] device plan f32")
+    pd = plan_workload_device(w, dtype=bsa.DTYPE_F32)
+    O, _ = run_gpu(w, Q, K, V, plan=pd)
+    compare_f32(w, Q, K, V, O, label="device plan f32")
+
+
+def test_device_plan_empty_mask():
+    w = wl.tiny()
+    w.block = np.zeros_like(w.block)
+    Q, K, V = wl.make_qkv(w)
+    pd = plan_workload_device(w)
+    info = pd.info()
+    assert info["tiles_full"] == 0 and info["tiles_partial"] == 0
+    O, _ = run_gpu(w, Q, K, V, plan=pd)
+    assert np.all(O == 0)
+
+
+@pytest.mark.parametrize("i", [0, 1, 2, 3, 13, 22, 27, 40])
+def test_tessera_masks_full_size(i):
+    """Full-size Tessera requests (24 heads, 21 x 45x80 tokens): the device
+    plan equals the host plan of the regime the host chose; the forward of a
+    device plan with its own regime matches the oracle on sampled rows."""
+    w = wl.tessera(i)
+    log(f"[case] tessera {i} {w.bq}x{w.bk}")
+    ph = plan_workload(w)
+    reg = ph.info()["regime"]
+    for order in ORDERS:
+        ph_o = plan_workload(w, force_regime=reg, task_order=order)
+        pd_o = plan_workload_device(w, force_regime=reg, task_order=order)
+        _same_plan(w, ph_o, pd_o, heads=[(0, 0), (0, 11), (0, w.H - 1)])
+    pd = plan_workload_device(w)
+    Q, K, V = wl.make_qkv(w)
+    q, k, v = to_device(Q), to_device(K), to_device(V)
+    od = torch.full_like(q, float("nan"))
+    bsa.forward(pd, q, k, v, od)
+    if pd.info()["regime"] == reg:
+        oh = torch.full_like(q, float("nan"))
+        bsa.forward(ph, q, k, v, oh)
+        torch.cuda.synchronize()
+        assert torch.equal(od, oh)
+    torch.cuda.synchronize()
+    O = od.float().cpu().numpy().astype(np.float64)
+    compare(w, Q, K, V, O, rows=sample_rows(w, per_head=16, seed=i), label=f"tessera{i} device plan")
+
+
+def test_mask_made_on_device_and_planned_on_a_side_stream():
+    """A mask produced by device work (a threshold of device-random scores),
+    planned on a second stream while the forward is enqueued on the current
+    one: the forward waits for the planning, and the result equals the forward
+    of the host plan of the same mask."""
+    w = wl.tessera(5)
+    gen = torch.Generator(device="cuda:0")
+    gen.manual_seed(1234)
+    side = torch.cuda.Stream()
+    scores = torch.rand((w.B, w.H, w.nqb, w.nkb), generator=gen, device="cuda:0")
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        mask = (scores < 0.2).to(torch.uint8)
+        pd = plan_workload_device(w, stream=side, mask=mask, force_regime=0)
+    Q, K, V = wl.make_qkv(w)
+    q, k, v = to_device(Q), to_device(K), to_device(V)
+    od = torch.full_like(q, float("nan"))
+    bsa.forward(pd, q, k, v, od)  # current stream; ordered after the planning
+    torch.cuda.synchronize()
+    w.block = mask.cpu().numpy()
+    ph = plan_workload(w, force_regime=0)
+    oh = torch.full_like(q, float("nan"))
+    bsa.forward(ph, q, k, v, oh)
+    torch.cuda.synchronize()
+    assert torch.equal(od, oh)
+    _same_plan(w, ph, pd, heads=[(0, 0), (0, 7), (0, w.H - 1)])
+
+
+def test_device_planning_rejects_other_kinds():
+    w = wl.tiny()
+    m = torch.zeros(16, dtype=torch.uint8, device="cuda:0")
+    with pytest.raises(bsa.BSAError) as e:
+        bsa.plan_device(bsa.MASK_VIDEO, w.B, w.H, w.L, w.d, 1, 1, m)
+    assert e.value.status == bsa.ERR_UNSUPPORTED
+
+
+def test_device_planning_time():
+    """Planning cost of the Tessera requests: host planner (mask in host
+    memory) against device planning (mask in device memory), both to a plan
+    ready for the forward. Logged; the device path must not be slower than
+    the host one by more than the launch overheads."""
+    rows = []
+    for i in (0, 1, 2, 3, 13, 26, 40):
+        w = wl.tessera(i)
+        md = torch.from_numpy(np.ascontiguousarray(w.block)).to("cuda:0")
+        reg = plan_workload(w).info()["regime"]
+        for _ in range(2):
+            plan_workload(w, force_regime=reg)
+            plan_workload_device(w, force_regime=reg, mask=md)
+        torch.cuda.synchronize()
+        n = 10
+        t0 = time.perf_counter()
+        for _ in range(n):
+            p = plan_workload(w, force_regime=reg)
+        torch.cuda.synchronize()
+        th = (time.perf_counter() - t0) / n
+        t0 = time.perf_counter()
+        for _ in range(n):
+            p = plan_workload_device(w, force_regime=reg, mask=md)
+        torch.cuda.synchronize()
+        td = (time.perf_counter() - t0) / n
+        del p
+        rows.append((i, w.bq, w.bk, th * 1e3, td * 1e3))
+        log(f"[plan time] tessera{i} {w.bq}x{w.bk} host {th * 1e3:.3f} ms device {td * 1e3:.3f} ms")
+    assert all(r[4] < r[3] + 2.0 for r in rows)
