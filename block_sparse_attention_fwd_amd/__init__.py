@@ -29,9 +29,11 @@ DTYPE_BF16, DTYPE_F32 = 0, 1
 TILE_FULL, TILE_PARTIAL = 0, 1
 PRED_NONE, PRED_SUBBLOCK, PRED_VIDEO, PRED_LIST = 0, 1, 2, 3
 ORDER_XCD_GROUPED, ORDER_LONGEST_FIRST = 0, 1
-ABI_VERSION = 2  # the structures below mirror this version of bsa.h
+ABI_VERSION = 3  # the structures below mirror this version of bsa.h
 
 EXPORTED = ["bsa_abi_version", "bsa_plan_opts_default", "bsa_plan", "bsa_plan_device", "bsa_forward", "bsa_plan_destroy",
+            "bsa_request_create", "bsa_request_submit", "bsa_request_finish", "bsa_request_stats",
+            "bsa_request_destroy",
             "bsa_plan_info", "bsa_plan_coverage", "bsa_regime_count", "bsa_regime_info", "bsa_status_str",
             "bsa_last_error"]
 
@@ -60,6 +62,16 @@ class PlanInfo(ctypes.Structure):
         d = {k: getattr(self, k) for k, _ in self._fields_}
         d["phase_ns"] = dict(zip(("ingest", "regime", "mapping", "tasks", "upload"), list(self.phase_ns)))
         return d
+
+
+class RequestDesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("L", ctypes.c_int64), ("d", ctypes.c_int32),
+                ("opts", PlanOpts), ("stream", ctypes.c_void_p), ("plan_stream", ctypes.c_void_p),
+                ("depth", ctypes.c_int32)]
+
+
+class RequestStats(ctypes.Structure):
+    _fields_ = [("submitted", ctypes.c_int64), ("plan_ns", ctypes.c_int64), ("wait_ns", ctypes.c_int64)]
 
 
 class RegimeDesc(ctypes.Structure):
@@ -106,6 +118,18 @@ def lib(path: str = LIB_PATH):
     L.bsa_plan_device.argtypes = [ctypes.POINTER(MaskDesc), ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                                   ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(PlanOpts),
                                   ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p)]
+    L.bsa_request_create.restype = ctypes.c_int32
+    L.bsa_request_create.argtypes = [ctypes.POINTER(RequestDesc), ctypes.POINTER(ctypes.c_void_p)]
+    L.bsa_request_submit.restype = ctypes.c_int32
+    L.bsa_request_submit.argtypes = [ctypes.c_void_p, ctypes.POINTER(MaskDesc), ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_void_p]
+    L.bsa_request_finish.restype = ctypes.c_int32
+    L.bsa_request_finish.argtypes = [ctypes.c_void_p]
+    L.bsa_request_stats.restype = ctypes.c_int32
+    L.bsa_request_stats.argtypes = [ctypes.c_void_p, ctypes.POINTER(RequestStats)]
+    L.bsa_request_destroy.restype = None
+    L.bsa_request_destroy.argtypes = [ctypes.c_void_p]
     L.bsa_forward.restype = ctypes.c_int32
     L.bsa_forward.argtypes = [ctypes.c_void_p] * 6
     L.bsa_plan_destroy.argtypes = [ctypes.c_void_p]
@@ -189,41 +213,107 @@ class Plan:
             pass
 
 
+def _arr(x, dt, keep):
+    if x is None:
+        return None
+    a = np.ascontiguousarray(x, dtype=dt)
+    keep.append(a)
+    return a
+
+
+def _host_mask(kind, data, row_ptr, col_idx, head_pattern, anchor_frame, radius, keep) -> MaskDesc:
+    m = MaskDesc()
+    m.kind = kind
+    m.data = _ptr(_arr(data, np.uint8 if kind == MASK_BLOCK_U8 else np.uint64, keep))
+    m.row_ptr = _ptr(_arr(row_ptr, np.int64, keep))
+    m.col_idx = _ptr(_arr(col_idx, np.int32, keep))
+    m.head_pattern = _ptr(_arr(head_pattern, np.uint8, keep))
+    m.anchor_frame = anchor_frame
+    m.radius = radius
+    return m
+
+
+def _opts(dtype, T, Hg, Wg, head_layout, force_regime, lut_path, device, task_order, keep) -> PlanOpts:
+    o = PlanOpts()
+    lib().bsa_plan_opts_default(ctypes.byref(o))
+    o.dtype = dtype
+    o.T, o.Hg, o.Wg = T, Hg, Wg
+    o.head_layout = _ptr(_arr(head_layout, np.uint8, keep))
+    o.force_regime = force_regime
+    o.lut_path = lut_path.encode() if lut_path else None
+    keep.append(o.lut_path)
+    o.device = device
+    o.task_order = task_order
+    return o
+
+
 def plan(kind: int, B: int, H: int, L: int, d: int, block_q: int, block_k: int, *, data=None, row_ptr=None,
          col_idx=None, head_pattern=None, anchor_frame: int = 0, radius: int = 2, dtype: int = DTYPE_BF16,
          T: int = 0, Hg: int = 0, Wg: int = 0, head_layout=None, force_regime: int = -1,
          lut_path: Optional[str] = None, device: int = 0, task_order: int = -1) -> Plan:
     """bsa_plan: build a plan for a logical mask (host numpy arrays)."""
-    L_ = lib()
     keep = []
-
-    def arr(x, dt):
-        if x is None:
-            return None
-        a = np.ascontiguousarray(x, dtype=dt)
-        keep.append(a)
-        return a
-
-    m = MaskDesc()
-    m.kind = kind
-    m.data = _ptr(arr(data, np.uint8 if kind == MASK_BLOCK_U8 else np.uint64))
-    m.row_ptr = _ptr(arr(row_ptr, np.int64))
-    m.col_idx = _ptr(arr(col_idx, np.int32))
-    m.head_pattern = _ptr(arr(head_pattern, np.uint8))
-    m.anchor_frame = anchor_frame
-    m.radius = radius
-    o = PlanOpts()
-    L_.bsa_plan_opts_default(ctypes.byref(o))
-    o.dtype = dtype
-    o.T, o.Hg, o.Wg = T, Hg, Wg
-    o.head_layout = _ptr(arr(head_layout, np.uint8))
-    o.force_regime = force_regime
-    o.lut_path = lut_path.encode() if lut_path else None
-    o.device = device
-    o.task_order = task_order
+    m = _host_mask(kind, data, row_ptr, col_idx, head_pattern, anchor_frame, radius, keep)
+    o = _opts(dtype, T, Hg, Wg, head_layout, force_regime, lut_path, device, task_order, keep)
     h = ctypes.c_void_p()
-    _check(L_.bsa_plan(ctypes.byref(m), B, H, L, d, block_q, block_k, ctypes.byref(o), ctypes.byref(h)))
+    _check(lib().bsa_plan(ctypes.byref(m), B, H, L, d, block_q, block_k, ctypes.byref(o), ctypes.byref(h)))
     return Plan(h.value, L, H, B)
+
+
+class Request:
+    """bsa_request_*: plan + forward over a sequence of masks of one shape,
+    with the planning of each mask overlapping the forwards already enqueued
+    (at most `depth` plans alive). Masks are host numpy arrays, or, with
+    on_device=True, BLOCK masks in device memory (torch tensors)."""
+
+    def __init__(self, B: int, H: int, L: int, d: int, *, depth: int = 3, stream=None, plan_stream=None,
+                 dtype: int = DTYPE_BF16, T: int = 0, Hg: int = 0, Wg: int = 0, head_layout=None,
+                 force_regime: int = -1, lut_path: Optional[str] = None, device: int = 0, task_order: int = -1):
+        keep = []
+        desc = RequestDesc()
+        desc.B, desc.H, desc.L, desc.d = B, H, L, d
+        desc.opts = _opts(dtype, T, Hg, Wg, head_layout, force_regime, lut_path, device, task_order, keep)
+        desc.stream = _stream_handle(stream)
+        desc.plan_stream = _stream_handle(plan_stream) if plan_stream is not None else None
+        desc.depth = depth
+        h = ctypes.c_void_p()
+        _check(lib().bsa_request_create(ctypes.byref(desc), ctypes.byref(h)))
+        self._h = h.value
+        self._masks = []  # device masks, kept until the request finishes
+
+    def submit(self, kind: int, block_q: int, block_k: int, q, k, v, o, *, data=None, row_ptr=None, col_idx=None,
+               head_pattern=None, anchor_frame: int = 0, radius: int = 2, on_device: bool = False) -> None:
+        keep = []
+        if on_device:
+            m = MaskDesc()
+            m.kind = kind
+            m.data = _dptr(data)
+            self._masks.append(data)
+        else:
+            m = _host_mask(kind, data, row_ptr, col_idx, head_pattern, anchor_frame, radius, keep)
+        _check(lib().bsa_request_submit(self._h, ctypes.byref(m), block_q, block_k, int(on_device), _dptr(q), _dptr(k),
+                                        _dptr(v), _dptr(o)))
+
+    def finish(self) -> None:
+        _check(lib().bsa_request_finish(self._h))
+        self._masks.clear()
+
+    def stats(self) -> dict:
+        st = RequestStats()
+        _check(lib().bsa_request_stats(self._h, ctypes.byref(st)))
+        return {"submitted": st.submitted, "plan_ns": st.plan_ns, "wait_ns": st.wait_ns}
+
+    def close(self) -> None:
+        if self._h:
+            lib().bsa_request_destroy(self._h)
+            self._h = None
+            self._masks.clear()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def _stream_handle(stream) -> int:
@@ -250,18 +340,7 @@ def plan_device(kind: int, B: int, H: int, L: int, d: int, block_q: int, block_k
     m = MaskDesc()
     m.kind = kind
     m.data = _dptr(data)
-    o = PlanOpts()
-    L_.bsa_plan_opts_default(ctypes.byref(o))
-    o.dtype = dtype
-    o.T, o.Hg, o.Wg = T, Hg, Wg
-    if head_layout is not None:
-        hl = np.ascontiguousarray(head_layout, dtype=np.uint8)
-        keep.append(hl)
-        o.head_layout = _ptr(hl)
-    o.force_regime = force_regime
-    o.lut_path = lut_path.encode() if lut_path else None
-    o.device = device
-    o.task_order = task_order
+    o = _opts(dtype, T, Hg, Wg, head_layout, force_regime, lut_path, device, task_order, keep)
     h = ctypes.c_void_p()
     _check(L_.bsa_plan_device(ctypes.byref(m), B, H, L, d, block_q, block_k, ctypes.byref(o), _stream_handle(stream),
                               ctypes.byref(h)))

@@ -1616,3 +1616,160 @@ extern "C" int32_t bsa_plan_coverage(bsa_plan_t p, int32_t b, int32_t h, bsa_cov
     }
     return BSA_OK;
 }
+
+// ---------------------------------------------------------------------------
+// requests: plan + forward over a sequence of masks, pipelined
+// ---------------------------------------------------------------------------
+
+struct bsa_request_s {
+    bsa_request_desc_t desc{};
+    std::vector<uint8_t> head_layout;  // owned copies of the option pointers
+    std::string lut_path;
+    struct Slot {
+        bsa_plan_t plan = nullptr;
+        hipEvent_t done = nullptr;  // recorded after the plan's forward
+    };
+    std::vector<Slot> ring;  // circular, `depth` slots
+    int64_t oldest = 0, inflight = 0;
+    bsa_request_stats_t stats{};
+};
+
+namespace {
+
+struct DeviceScope {
+    int prev = 0;
+    explicit DeviceScope(int dev)
+    {
+        (void)hipGetDevice(&prev);
+        if (prev != dev) (void)hipSetDevice(dev);
+    }
+    ~DeviceScope() { (void)hipSetDevice(prev); }
+};
+
+// Wait for the oldest in-flight forward, then destroy its plan.
+int32_t retire_oldest(bsa_request_s *r)
+{
+    bsa_request_s::Slot &s = r->ring[(size_t)(r->oldest % r->desc.depth)];
+    hipError_t e;
+    {
+        DeviceScope ds(r->desc.opts.device);
+        e = hipEventSynchronize(s.done);
+    }
+    bsa_plan_destroy(s.plan);
+    s.plan = nullptr;
+    ++r->oldest;
+    --r->inflight;
+    if (e != hipSuccess) return fail(BSA_ERR_HIP, "waiting for a request's forward: %s", hipGetErrorString(e));
+    return BSA_OK;
+}
+
+}  // namespace
+
+extern "C" int32_t bsa_request_create(const bsa_request_desc_t *desc, bsa_request_t *out)
+{
+    if (!out) return fail(BSA_ERR_INVALID_ARGUMENT, "out is NULL");
+    *out = nullptr;
+    if (!desc) return fail(BSA_ERR_INVALID_ARGUMENT, "desc is NULL");
+    if (desc->depth < 1) return fail(BSA_ERR_INVALID_ARGUMENT, "request depth %d (at least 1)", desc->depth);
+    if (desc->opts.device < 0) return fail(BSA_ERR_INVALID_ARGUMENT, "a request runs forwards: opts.device must be a device");
+    if (desc->B < 1 || desc->H < 1 || desc->L < 1 || (desc->d != 64 && desc->d != 128))
+        return fail(BSA_ERR_INVALID_ARGUMENT, "request shape B=%d H=%d L=%lld d=%d", desc->B, desc->H, (long long)desc->L,
+                    desc->d);
+    try {
+        std::unique_ptr<bsa_request_s> r(new bsa_request_s);
+        r->desc = *desc;
+        if (desc->opts.head_layout) {
+            r->head_layout.assign(desc->opts.head_layout, desc->opts.head_layout + desc->H);
+            r->desc.opts.head_layout = r->head_layout.data();
+        }
+        if (desc->opts.lut_path) {
+            r->lut_path = desc->opts.lut_path;
+            r->desc.opts.lut_path = r->lut_path.c_str();
+        }
+        r->ring.resize((size_t)desc->depth);
+        DeviceScope ds(desc->opts.device);
+        for (auto &s : r->ring) {
+            const hipError_t e = hipEventCreateWithFlags(&s.done, hipEventDisableTiming);
+            if (e != hipSuccess) {
+                s.done = nullptr;
+                for (auto &t : r->ring)
+                    if (t.done) (void)hipEventDestroy(t.done);
+                return fail(BSA_ERR_HIP, "hipEventCreateWithFlags: %s", hipGetErrorString(e));
+            }
+        }
+        *out = r.release();
+        return BSA_OK;
+    } catch (const std::bad_alloc &) {
+        return fail(BSA_ERR_OUT_OF_MEMORY, "host allocation failed");
+    }
+}
+
+extern "C" int32_t bsa_request_submit(bsa_request_t r, const bsa_mask_desc_t *mask, int32_t block_q, int32_t block_k,
+                                      int32_t mask_on_device, const void *Q, const void *K, const void *V, void *O)
+{
+    if (!r || !mask) return fail(BSA_ERR_INVALID_ARGUMENT, "request or mask is NULL");
+    const bsa_request_desc_t &d = r->desc;
+    const auto t0 = std::chrono::steady_clock::now();
+    if (r->inflight >= d.depth)
+        if (int32_t st = retire_oldest(r); st != BSA_OK) return st;
+    const auto t1 = std::chrono::steady_clock::now();
+    bsa_plan_t p = nullptr;
+    int32_t st = mask_on_device
+                     ? bsa_plan_device(mask, d.B, d.H, d.L, d.d, block_q, block_k, &d.opts,
+                                       d.plan_stream ? d.plan_stream : d.stream, &p)
+                     : bsa_plan(mask, d.B, d.H, d.L, d.d, block_q, block_k, &d.opts, &p);
+    const auto t2 = std::chrono::steady_clock::now();
+    r->stats.wait_ns += (int64_t)std::chrono::duration_cast<std::chrono::nanoseconds>(t1 - t0).count();
+    r->stats.plan_ns += (int64_t)std::chrono::duration_cast<std::chrono::nanoseconds>(t2 - t1).count();
+    if (st != BSA_OK) return st;
+    st = bsa_forward(p, Q, K, V, O, d.stream);
+    if (st != BSA_OK) {
+        bsa_plan_destroy(p);  // nothing of it was launched
+        return st;
+    }
+    bsa_request_s::Slot &s = r->ring[(size_t)((r->oldest + r->inflight) % d.depth)];
+    hipError_t e;
+    {
+        DeviceScope ds(d.opts.device);
+        e = hipEventRecord(s.done, (hipStream_t)d.stream);
+        if (e != hipSuccess) (void)hipStreamSynchronize((hipStream_t)d.stream);
+    }
+    if (e != hipSuccess) {
+        bsa_plan_destroy(p);
+        return fail(BSA_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
+    }
+    s.plan = p;
+    ++r->inflight;
+    ++r->stats.submitted;
+    return BSA_OK;
+}
+
+extern "C" int32_t bsa_request_finish(bsa_request_t r)
+{
+    if (!r) return fail(BSA_ERR_INVALID_ARGUMENT, "request is NULL");
+    int32_t first = BSA_OK;
+    while (r->inflight > 0) {
+        const int32_t st = retire_oldest(r);
+        if (first == BSA_OK) first = st;
+    }
+    return first;
+}
+
+extern "C" int32_t bsa_request_stats(bsa_request_t r, bsa_request_stats_t *out)
+{
+    if (!r || !out) return fail(BSA_ERR_INVALID_ARGUMENT, "request or out is NULL");
+    *out = r->stats;
+    return BSA_OK;
+}
+
+extern "C" void bsa_request_destroy(bsa_request_t r)
+{
+    if (!r) return;
+    (void)bsa_request_finish(r);
+    {
+        DeviceScope ds(r->desc.opts.device);
+        for (auto &s : r->ring)
+            if (s.done) (void)hipEventDestroy(s.done);
+    }
+    delete r;
+}

@@ -16,6 +16,10 @@
  *                  tasks and uploads the result to the device once.
  *   bsa_forward -- device side: runs a plan on caller-owned Q, K, V, O.
  *
+ * bsa_plan_device builds the same plan on the GPU from a BLOCK mask already
+ * in device memory, and a request (bsa_request_*) pipelines the planning of
+ * one mask with the forwards of the previous ones.
+ *
  * Conventions
  *  - All functions are plain C, never throw, and report errors through their
  *    return value; bsa_last_error() gives a thread-local message for the last
@@ -24,8 +28,9 @@
  *    [B][H][L][d] in the plan's dtype (bf16 or fp32), rows in frame-major token
  *    order (token i = t*Hg*Wg + y*Wg + x), 16-byte aligned. Q, K, V are only
  *    read. O is fully overwritten, including rows with no kept key (zeros).
- *  - Masks are HOST memory owned by the caller; bsa_plan copies what it needs,
- *    so the caller may free the mask as soon as bsa_plan returns.
+ *  - Masks given to bsa_plan are HOST memory owned by the caller; bsa_plan
+ *    copies what it needs, so the caller may free the mask as soon as it
+ *    returns (bsa_plan_device reads a device mask; see there).
  *  - A plan owns its host and device memory and is immutable; it may be used
  *    by any number of bsa_forward calls on any streams of its device, also
  *    concurrently. Destroy it only after the streams that use it are done.
@@ -39,7 +44,7 @@
 extern "C" {
 #endif
 
-#define BSA_ABI_VERSION 2
+#define BSA_ABI_VERSION 3
 
 typedef struct bsa_plan_s *bsa_plan_t;
 
@@ -238,6 +243,57 @@ int32_t bsa_plan_info(bsa_plan_t plan, bsa_plan_info_t *out);
 /* Walk the tiles the device will compute for head (b, h), in task order.
  * Errors: INVALID_ARGUMENT (null plan/sink, b or h out of range). */
 int32_t bsa_plan_coverage(bsa_plan_t plan, int32_t b, int32_t h, bsa_cov_sink_t sink, void *user);
+
+/*
+ * Requests: a sequence of forward calls over one shape, each with its own
+ * mask, pipelined (Tessera, arXiv 2609.25869, abstract: a request runs many
+ * dynamic masks, and preparing each must cost little next to running it).
+ * bsa_request_submit plans the mask, enqueues its forward on the request's
+ * stream and returns, so the planning of the next mask overlaps the forwards
+ * already enqueued. At most `depth` plans are alive: a submit that finds
+ * `depth` plans in flight first waits for the oldest one's forward and
+ * destroys that plan. The request owns its plans.
+ */
+typedef struct bsa_request_s *bsa_request_t;
+
+typedef struct {
+    int32_t B, H;
+    int64_t L;
+    int32_t d;
+    bsa_plan_opts_t opts;   /* for every plan (copied, pointers included); opts.device >= 0 */
+    void *stream;           /* forward stream (hipStream_t); NULL = the device's default stream */
+    void *plan_stream;      /* stream of device planning (bsa_plan_device); NULL = `stream` */
+    int32_t depth;          /* plans alive at most, >= 1 */
+} bsa_request_desc_t;
+
+typedef struct {
+    int64_t submitted;      /* forwards enqueued */
+    int64_t plan_ns;        /* host time spent planning (device planning: enqueueing) */
+    int64_t wait_ns;        /* host time spent waiting for a ring slot */
+} bsa_request_stats_t;
+
+/* Errors: INVALID_ARGUMENT (null pointers, depth < 1, host-only device,
+ * bad shape), OUT_OF_MEMORY, HIP. */
+int32_t bsa_request_create(const bsa_request_desc_t *desc, bsa_request_t *out);
+
+/*
+ * Plan `mask` (host memory: bsa_plan; mask_on_device = 1: a BLOCK mask in
+ * device memory, bsa_plan_device on the request's plan stream, after any work
+ * the caller enqueued there) and enqueue the forward on Q, K, V, O (as
+ * bsa_forward). Errors: those of bsa_plan / bsa_plan_device / bsa_forward, and
+ * HIP; a failed submit leaves the request usable.
+ */
+int32_t bsa_request_submit(bsa_request_t req, const bsa_mask_desc_t *mask, int32_t block_q, int32_t block_k,
+                           int32_t mask_on_device, const void *Q, const void *K, const void *V, void *O);
+
+/* Wait for every forward submitted so far and destroy their plans. Errors: HIP. */
+int32_t bsa_request_finish(bsa_request_t req);
+
+/* Errors: INVALID_ARGUMENT. */
+int32_t bsa_request_stats(bsa_request_t req, bsa_request_stats_t *out);
+
+/* Finish, then free the request (NULL is allowed). */
+void bsa_request_destroy(bsa_request_t req);
 
 /* Number of execution regimes compiled in, and their shapes. */
 int32_t bsa_regime_count(void);

@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     L = bsa.lib()
-    assert L.bsa_abi_version() == bsa.ABI_VERSION == 2
+    assert L.bsa_abi_version() == bsa.ABI_VERSION == 3
     assert L.bsa_status_str(bsa.ERR_INVALID_MASK) == b"BSA_ERR_INVALID_MASK"
     assert L.bsa_status_str(99) == b"BSA_ERR_UNKNOWN"
     assert len(bsa.regimes()) == L.bsa_regime_count() >= 3
@@ -122,6 +122,19 @@ def test_device_planning_argument_errors():
     expect(bsa.ERR_UNSUPPORTED, PD, bsa.MASK_BLOCK_U8, 1, 2, 256, 64, 48, 64, 16, stream=0, match="block shape")
     L = bsa.lib()
     assert L.bsa_plan_device(None, 1, 1, 64, 64, 64, 64, None, None, None) == bsa.ERR_INVALID_ARGUMENT
+
+
+def test_request_argument_errors():
+    """bsa_request_create rejects bad descriptions before touching the device."""
+    expect(bsa.ERR_INVALID_ARGUMENT, bsa.Request, 1, 2, 256, 64, depth=0, stream=0, match="depth")
+    expect(bsa.ERR_INVALID_ARGUMENT, bsa.Request, 1, 2, 256, 64, device=-1, stream=0, match="device")
+    expect(bsa.ERR_INVALID_ARGUMENT, bsa.Request, 1, 2, 256, 96, stream=0, match="shape")
+    expect(bsa.ERR_INVALID_ARGUMENT, bsa.Request, 0, 2, 256, 64, stream=0, match="shape")
+    L = bsa.lib()
+    assert L.bsa_request_create(None, None) == bsa.ERR_INVALID_ARGUMENT
+    assert L.bsa_request_submit(None, None, 64, 64, 0, None, None, None, None) == bsa.ERR_INVALID_ARGUMENT
+    assert L.bsa_request_finish(None) == bsa.ERR_INVALID_ARGUMENT
+    L.bsa_request_destroy(None)  # NULL-safe
 
 
 def test_simulated_allocation_failure(monkeypatch):
