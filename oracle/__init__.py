@@ -23,6 +23,7 @@ from __future__ import annotations
 import ctypes
 import os
 import subprocess
+import types
 
 import numpy as np
 
@@ -163,3 +164,28 @@ def block_union(w, b, h, blk, M=64, lib_path: str = _LIB):
     used = np.zeros(w.L, np.uint8)
     L_.om_block_union(ctypes.byref(mk.m), b, h, blk, M, _ptr(used))
     return used
+
+
+def route_heads(Q, K, V, T: int, Hg: int, Wg: int, rows, anchor: int = 0, radius: int = 2, lib_path: str = _LIB):
+    """Head routing, fp64 (Sparse VideoGen / Splash Attention summary, "Sparse
+    VideoGen": each head is routed on the fly to a spatial or a temporal
+    sparse pattern; the pages give no rule). Reading: per head, the pattern
+    whose masked attention output is nearer the dense output, as the mean
+    squared difference over the batch, the sampled query tokens ``rows``
+    (frame-major) and the head dimension; ties go to spatial. The outputs are
+    this oracle's masked attention under the video patterns (all heads dense,
+    all spatial, all temporal). Returns (pattern uint8 [H]: 1 spatial,
+    2 temporal; err float64 [H][2]: spatial, temporal)."""
+    B, H, L, d = Q.shape
+    rows = np.asarray(rows, dtype=np.int64)
+    flat = ((np.arange(B)[:, None, None] * H + np.arange(H)[None, :, None]) * L + rows[None, None, :]).reshape(-1)
+    outs = []
+    for pat in (0, 1, 2):
+        spec = types.SimpleNamespace(kind=4, B=B, H=H, L=L, bq=1, bk=1, head_pattern=np.full(H, pat, np.uint8),
+                                     anchor=anchor, radius=radius, T=T, Hg=Hg, Wg=Wg, head_layout=None)
+        outs.append(attend(spec, Q, K, V, rows=flat, lib_path=lib_path).reshape(B, H, rows.size, d))
+    err = np.zeros((H, 2), np.float64)
+    err[:, 0] = ((outs[1] - outs[0]) ** 2).mean(axis=(0, 2, 3))
+    err[:, 1] = ((outs[2] - outs[0]) ** 2).mean(axis=(0, 2, 3))
+    pattern = np.where(err[:, 0] <= err[:, 1], 1, 2).astype(np.uint8)
+    return pattern, err

@@ -396,3 +396,46 @@ def highres(H=24, T=21, Hg=90, Wg=160, d=128, blk=128, cfg=5) -> Workload:
     w.block = np.stack([sp] * ns + [tp] * (H - ns))[None]
     w.head_layout = np.array([FRAME_MAJOR] * ns + [TEMPORAL_MAJOR] * (H - ns), np.uint8)
     return w
+
+
+# ----------------------------------------------------------------------------
+# inputs with a known head routing
+# ----------------------------------------------------------------------------
+
+PURPOSE_BOOST = 4
+
+
+def routed_qkv(w: Workload, kinds, alpha: float, base: float = 0.5, dtype: str = "bf16"):
+    """Q, K, V [B][H][L][d] for head routing: Q and K are base * N(0,1) plus,
+    per head, alpha times a seeded unit vector shared by all tokens of one
+    frame (kinds[h] == SPATIAL) or of one pixel (kinds[h] == TEMPORAL), so that
+    that head's attention concentrates within frames or along pixel tracks;
+    V is N(0,1). bf16 as uint16 bits (rounded once, after the sum)."""
+    HW = w.Hg * w.Wg
+    tok = np.arange(w.L)
+    frame, pixel = tok // HW, tok % HW
+    Q = np.zeros((w.B, w.H, w.L, w.d), np.float32)
+    K = np.zeros_like(Q)
+    V = np.zeros_like(Q)
+    for b in range(w.B):
+        for h in range(w.H):
+            g = rng(w.cfg * 1000 + b, PURPOSE_BOOST, h)
+            Q[b, h] = base * g.standard_normal((w.L, w.d), dtype=np.float32)
+            K[b, h] = base * g.standard_normal((w.L, w.d), dtype=np.float32)
+            V[b, h] = g.standard_normal((w.L, w.d), dtype=np.float32)
+            if kinds[h] == DENSE:
+                continue
+            groups = w.T if kinds[h] == SPATIAL else HW
+            u = g.standard_normal((groups, w.d)).astype(np.float32)
+            u /= np.linalg.norm(u, axis=1, keepdims=True)
+            sel = u[frame if kinds[h] == SPATIAL else pixel]
+            Q[b, h] += alpha * sel
+            K[b, h] += alpha * sel
+    if dtype == "bf16":
+        return f32_to_bf16_bits(Q), f32_to_bf16_bits(K), f32_to_bf16_bits(V)
+    return Q, K, V
+
+
+def sample_tokens(L: int, n: int, seed: int) -> np.ndarray:
+    """n distinct query tokens drawn uniformly from [0, L), sorted."""
+    return np.sort(np.random.default_rng([seed, 77]).choice(L, size=min(n, L), replace=False)).astype(np.int32)
