@@ -33,7 +33,7 @@ ABI_VERSION = 3  # the structures below mirror this version of bsa.h
 
 EXPORTED = ["bsa_abi_version", "bsa_plan_opts_default", "bsa_plan", "bsa_plan_device", "bsa_forward", "bsa_plan_destroy",
             "bsa_request_create", "bsa_request_submit", "bsa_request_finish", "bsa_request_stats",
-            "bsa_request_destroy",
+            "bsa_request_destroy", "bsa_route_heads",
             "bsa_plan_info", "bsa_plan_coverage", "bsa_regime_count", "bsa_regime_info", "bsa_status_str",
             "bsa_last_error"]
 
@@ -72,6 +72,12 @@ class RequestDesc(ctypes.Structure):
 
 class RequestStats(ctypes.Structure):
     _fields_ = [("submitted", ctypes.c_int64), ("plan_ns", ctypes.c_int64), ("wait_ns", ctypes.c_int64)]
+
+
+class RouteDesc(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("Hg", ctypes.c_int32), ("Wg", ctypes.c_int32),
+                ("anchor_frame", ctypes.c_int32), ("radius", ctypes.c_int32), ("rows", ctypes.c_void_p),
+                ("n_rows", ctypes.c_int32), ("device", ctypes.c_int32)]
 
 
 class RegimeDesc(ctypes.Structure):
@@ -130,6 +136,10 @@ def lib(path: str = LIB_PATH):
     L.bsa_request_stats.argtypes = [ctypes.c_void_p, ctypes.POINTER(RequestStats)]
     L.bsa_request_destroy.restype = None
     L.bsa_request_destroy.argtypes = [ctypes.c_void_p]
+    L.bsa_route_heads.restype = ctypes.c_int32
+    L.bsa_route_heads.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                  ctypes.c_int64, ctypes.c_int32, ctypes.POINTER(RouteDesc), ctypes.c_void_p,
+                                  ctypes.c_void_p, ctypes.c_void_p]
     L.bsa_forward.restype = ctypes.c_int32
     L.bsa_forward.argtypes = [ctypes.c_void_p] * 6
     L.bsa_plan_destroy.argtypes = [ctypes.c_void_p]
@@ -353,6 +363,26 @@ def forward(p: Plan, q, k, v, o, stream=None) -> None:
     """bsa_forward: enqueue the forward pass on `stream` (torch stream, raw
     hipStream_t as int, or None for the current torch stream)."""
     _check(lib().bsa_forward(p.handle, _dptr(q), _dptr(k), _dptr(v), _dptr(o), _stream_handle(stream)))
+
+
+def route_heads(q, k, v, B: int, H: int, L: int, d: int, T: int, Hg: int, Wg: int, rows, *, anchor_frame: int = 0,
+                radius: int = 2, device: int = 0, stream=None):
+    """bsa_route_heads: per head, the video pattern (PAT_SPATIAL or
+    PAT_TEMPORAL) whose output over the sampled query tokens `rows` is nearer
+    the dense output. Returns (pattern uint8 [H], err float64 [H][2]).
+    Synchronises with `stream`."""
+    r = np.ascontiguousarray(rows, dtype=np.int32)
+    desc = RouteDesc()
+    desc.T, desc.Hg, desc.Wg = T, Hg, Wg
+    desc.anchor_frame, desc.radius = anchor_frame, radius
+    desc.rows = _ptr(r)
+    desc.n_rows = r.size
+    desc.device = device
+    pat = np.zeros(H, np.uint8)
+    err = np.zeros((H, 2), np.float64)
+    _check(lib().bsa_route_heads(_dptr(q), _dptr(k), _dptr(v), B, H, L, d, ctypes.byref(desc),
+                                 _stream_handle(stream), _ptr(pat), _ptr(err)))
+    return pat, err
 
 
 def regimes():

@@ -30,7 +30,7 @@ def build(verbose: bool = False) -> str:
     _embed_lut()
     objs = []
     common = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", os.path.join(ROOT, "include")]
-    for name in ("api.cpp", "attn_fwd.hip", "attn_fwd_f32.hip", "plan_device.hip"):
+    for name in ("api.cpp", "attn_fwd.hip", "attn_fwd_f32.hip", "plan_device.hip", "route_probe.hip"):
         src = os.path.join(CSRC, name)
         obj = os.path.join(CSRC, name + ".o")
         lang = ["-x", "hip"]

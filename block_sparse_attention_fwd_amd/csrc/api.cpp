@@ -42,6 +42,7 @@
 #include "../../include/bsa.h"
 #include "mempool.hpp"
 #include "plan_device.hpp"
+#include "route_probe.hpp"
 #include "plan_format.hpp"
 
 namespace bsa {
@@ -1772,4 +1773,118 @@ extern "C" void bsa_request_destroy(bsa_request_t r)
             if (s.done) (void)hipEventDestroy(s.done);
     }
     delete r;
+}
+
+// ---------------------------------------------------------------------------
+// head routing probe
+// ---------------------------------------------------------------------------
+
+extern "C" int32_t bsa_route_heads(const void *Q, const void *K, const void *V, int32_t B, int32_t H, int64_t L,
+                                   int32_t d, const bsa_route_desc_t *desc, void *stream, uint8_t *head_pattern,
+                                   double *err)
+{
+    if (!Q || !K || !V || !desc || !head_pattern || !desc->rows)
+        return fail(BSA_ERR_INVALID_ARGUMENT, "Q, K, V, desc, desc->rows and head_pattern must be non-NULL");
+    if (((uintptr_t)Q | (uintptr_t)K | (uintptr_t)V) & 15)
+        return fail(BSA_ERR_INVALID_ARGUMENT, "Q, K and V must be 16-byte aligned");
+    const bsa_route_desc_t &r = *desc;
+    if (B < 1 || H < 1 || L < 1 || L >= ((int64_t)1 << 31) || (d != 64 && d != 128))
+        return fail(BSA_ERR_INVALID_ARGUMENT, "routing shape B=%d H=%d L=%lld d=%d", B, H, (long long)L, d);
+    if (r.T < 1 || r.Hg < 1 || r.Wg < 1 || r.Hg >= 32768 || r.Wg >= 32768 || (int64_t)r.T * r.Hg * r.Wg != L)
+        return fail(BSA_ERR_INVALID_ARGUMENT, "geometry T=%d Hg=%d Wg=%d does not give L=%lld", r.T, r.Hg, r.Wg,
+                    (long long)L);
+    if (r.anchor_frame < 0 || r.anchor_frame >= r.T || r.radius < 0 || r.radius > 256)
+        return fail(BSA_ERR_INVALID_ARGUMENT, "anchor frame %d / radius %d out of range", r.anchor_frame, r.radius);
+    if (r.n_rows < 1 || r.n_rows > 4096) return fail(BSA_ERR_INVALID_ARGUMENT, "n_rows %d (1 .. 4096)", r.n_rows);
+    for (int32_t i = 0; i < r.n_rows; ++i)
+        if (r.rows[i] < 0 || r.rows[i] >= L) return fail(BSA_ERR_INVALID_ARGUMENT, "row %d = %d out of range", i, r.rows[i]);
+    if (r.device < 0) return fail(BSA_ERR_INVALID_ARGUMENT, "routing needs a device (desc->device = %d)", r.device);
+    try {
+        const int32_t BH = B * H, S = r.n_rows, nsb = (S + 31) / 32;
+        const int32_t nkt = (int32_t)((L + kTileK - 1) / kTileK);
+        // key chunks: enough waves (three variants each) to fill the chip
+        const int64_t units = (int64_t)BH * nsb * 3;
+        const int32_t nchunk = (int32_t)std::max<int64_t>(1, std::min<int64_t>(nkt, (4096 + units - 1) / units));
+        const int32_t tpc = (nkt + nchunk - 1) / nchunk;
+        const size_t part_floats = (size_t)BH * nsb * nchunk * 3 * (64 + 32 * (size_t)d);
+        const size_t off_rows = 0;
+        const size_t off_err = align_up((size_t)S * sizeof(int32_t));
+        const size_t off_part = off_err + align_up((size_t)BH * S * 2 * sizeof(float));
+        const size_t bytes = off_part + part_floats * sizeof(float);
+        const size_t host_bytes = align_up((size_t)S * sizeof(int32_t)) + (size_t)BH * S * 2 * sizeof(float);
+
+        DeviceScope ds(r.device);
+        std::string e_str;
+        DeviceRt *rt = device_rt(r.device, e_str);
+        if (!rt) return fail(BSA_ERR_HIP, "%s", e_str.c_str());
+        size_t dev_cap = 0, host_cap = 0;
+        uint8_t *dev = (uint8_t *)rt->pool->acquire(bytes, &dev_cap);
+        if (!dev) return fail(BSA_ERR_OUT_OF_MEMORY, "device allocation of %zu bytes failed", bytes);
+        uint8_t *host = (uint8_t *)pinned_pool().acquire(host_bytes, &host_cap);
+        if (!host) {
+            rt->pool->release(dev, dev_cap);
+            return fail(BSA_ERR_OUT_OF_MEMORY, "pinned host allocation of %zu bytes failed", host_bytes);
+        }
+        std::memcpy(host, r.rows, (size_t)S * sizeof(int32_t));
+        float *err_host = (float *)(host + align_up((size_t)S * sizeof(int32_t)));
+
+        RouteArgs a{};
+        a.Q = Q; a.K = K; a.V = V;
+        a.BH = BH;
+        a.L = (int32_t)L;
+        a.HW = r.Hg * r.Wg;
+        a.W = r.Wg;
+        a.anchor = r.anchor_frame;
+        a.radius = r.radius;
+        magic_div((uint32_t)a.HW, &a.magic_HW, &a.shift_HW);
+        magic_div((uint32_t)a.W, &a.magic_W, &a.shift_W);
+        a.rows = (const int32_t *)(dev + off_rows);
+        a.S = S;
+        a.nsb = nsb;
+        a.nkt = nkt;
+        a.nchunk = nchunk;
+        a.tiles_per_chunk = tpc;
+        a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
+        a.part = (float *)(dev + off_part);
+        a.err_rows = (float *)(dev + off_err);
+        const hipStream_t s = (hipStream_t)stream;
+        hipEvent_t done = nullptr;
+        hipError_t e = hipEventCreateWithFlags(&done, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipMemcpyAsync(dev + off_rows, host, (size_t)S * sizeof(int32_t), hipMemcpyHostToDevice, s);
+        if (e == hipSuccess) e = launch_route_probe(a, d, s);
+        if (e == hipSuccess)
+            e = hipMemcpyAsync(err_host, dev + off_err, (size_t)BH * S * 2 * sizeof(float), hipMemcpyDeviceToHost, s);
+        if (e == hipSuccess) e = hipEventRecord(done, s);
+        if (e == hipSuccess) e = hipEventSynchronize(done);
+        else (void)hipStreamSynchronize(s);  // nothing may still use the scratch memory
+        if (done) (void)hipEventDestroy(done);
+        int32_t st = BSA_OK;
+        if (e != hipSuccess) {
+            st = fail(BSA_ERR_HIP, "routing probe: %s", hipGetErrorString(e));
+        } else {
+            // per head: mean over the batch, the sampled rows and the dims
+            for (int h = 0; h < H; ++h) {
+                double es = 0.0, et = 0.0;
+                for (int b = 0; b < B; ++b)
+                    for (int i = 0; i < S; ++i) {
+                        const float *er = err_host + ((size_t)(b * H + h) * S + i) * 2;
+                        es += er[0];
+                        et += er[1];
+                    }
+                const double n = (double)B * S * d;
+                es /= n;
+                et /= n;
+                head_pattern[h] = es <= et ? BSA_PAT_SPATIAL : BSA_PAT_TEMPORAL;
+                if (err) {
+                    err[2 * h] = es;
+                    err[2 * h + 1] = et;
+                }
+            }
+        }
+        pinned_pool().release(host, host_cap);
+        rt->pool->release(dev, dev_cap);
+        return st;
+    } catch (const std::bad_alloc &) {
+        return fail(BSA_ERR_OUT_OF_MEMORY, "host allocation failed");
+    }
 }

@@ -295,6 +295,38 @@ int32_t bsa_request_stats(bsa_request_t req, bsa_request_stats_t *out);
 /* Finish, then free the request (NULL is allowed). */
 void bsa_request_destroy(bsa_request_t req);
 
+/*
+ * Head routing (Sparse VideoGen / Splash Attention summary, "Sparse
+ * VideoGen": each attention head is routed on the fly to a spatial or a
+ * temporal sparse pattern). The pages give no routing rule; this call takes
+ * the plain one: for every head, the pattern whose masked attention output is
+ * nearer the dense output, measured as the mean squared difference over the
+ * batch, the sampled query tokens and the head dimension (ties: spatial). The
+ * patterns are those of BSA_MASK_VIDEO (spatial: key in the query's frame or
+ * the anchor frame; temporal: key pixel within `radius`, any frame).
+ */
+typedef struct {
+    int32_t T, Hg, Wg;          /* token grid, T*Hg*Wg == L; Hg, Wg < 32768 */
+    int32_t anchor_frame;       /* 0 <= anchor_frame < T */
+    int32_t radius;             /* 0 .. 256 */
+    const int32_t *rows;        /* HOST [n_rows]: sampled query tokens (frame-major), each in [0, L) */
+    int32_t n_rows;             /* 1 .. 4096 */
+    int32_t device;             /* device of Q, K, V (>= 0) */
+} bsa_route_desc_t;
+
+/*
+ * Q, K, V: bf16 DEVICE tensors [B][H][L][d] in frame-major token order, d in
+ * {64, 128}. Runs the probe kernels on `stream` (hipStream_t; NULL = the
+ * device's default stream) after the work already enqueued there, WAITS for
+ * them, and writes head_pattern (HOST [H]: BSA_PAT_SPATIAL or
+ * BSA_PAT_TEMPORAL) and, if err is not NULL, err (HOST [H][2]: the spatial and
+ * the temporal mean squared difference). Scratch device memory comes from the
+ * library's pool. Errors: INVALID_ARGUMENT (null pointers, shapes, geometry,
+ * rows out of range), OUT_OF_MEMORY, HIP.
+ */
+int32_t bsa_route_heads(const void *Q, const void *K, const void *V, int32_t B, int32_t H, int64_t L, int32_t d,
+                        const bsa_route_desc_t *desc, void *stream, uint8_t *head_pattern, double *err);
+
 /* Number of execution regimes compiled in, and their shapes. */
 int32_t bsa_regime_count(void);
 int32_t bsa_regime_info(int32_t regime, bsa_regime_desc_t *out);
