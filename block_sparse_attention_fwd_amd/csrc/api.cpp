@@ -1779,6 +1779,13 @@ extern "C" void bsa_request_destroy(bsa_request_t r)
 // head routing probe
 // ---------------------------------------------------------------------------
 
+// probe workgroups per call, read from BSA_PROBE_WGS when set (a tuning knob)
+static int64_t probe_workgroups()
+{
+    const char *e = std::getenv("BSA_PROBE_WGS");
+    return e ? std::max(1, std::atoi(e)) : 256;
+}
+
 extern "C" int32_t bsa_route_heads(const void *Q, const void *K, const void *V, int32_t B, int32_t H, int64_t L,
                                    int32_t d, const bsa_route_desc_t *desc, void *stream, uint8_t *head_pattern,
                                    double *err)
@@ -1802,9 +1809,10 @@ extern "C" int32_t bsa_route_heads(const void *Q, const void *K, const void *V, 
     try {
         const int32_t BH = B * H, S = r.n_rows, nsb = (S + 31) / 32;
         const int32_t nkt = (int32_t)((L + kTileK - 1) / kTileK);
-        // key chunks: enough waves (three variants each) to fill the chip
-        const int64_t units = (int64_t)BH * nsb * 3;
-        const int32_t nchunk = (int32_t)std::max<int64_t>(1, std::min<int64_t>(nkt, (4096 + units - 1) / units));
+        // key chunks: about probe_workgroups() workgroups of six waves (two
+        // blocks of 32 sampled rows x three variants)
+        const int64_t units = (int64_t)BH * ((nsb + 1) / 2);
+        const int32_t nchunk = (int32_t)std::max<int64_t>(1, std::min<int64_t>(nkt, probe_workgroups() / units));
         const int32_t tpc = (nkt + nchunk - 1) / nchunk;
         const size_t part_floats = (size_t)BH * nsb * nchunk * 3 * (64 + 32 * (size_t)d);
         const size_t off_rows = 0;
