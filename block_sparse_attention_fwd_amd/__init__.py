@@ -289,7 +289,8 @@ class Request:
         h = ctypes.c_void_p()
         _check(lib().bsa_request_create(ctypes.byref(desc), ctypes.byref(h)))
         self._h = h.value
-        self._masks = []  # device masks, kept until the request finishes
+        self._depth = depth
+        self._masks = []  # device masks of the plans that may still be in flight
 
     def submit(self, kind: int, block_q: int, block_k: int, q, k, v, o, *, data=None, row_ptr=None, col_idx=None,
                head_pattern=None, anchor_frame: int = 0, radius: int = 2, on_device: bool = False) -> None:
@@ -298,7 +299,11 @@ class Request:
             m = MaskDesc()
             m.kind = kind
             m.data = _dptr(data)
+            # a plan (and the planning that read its mask) is retired once
+            # `depth` newer plans exist: older masks may go
             self._masks.append(data)
+            if len(self._masks) > self._depth + 1:
+                self._masks.pop(0)
         else:
             m = _host_mask(kind, data, row_ptr, col_idx, head_pattern, anchor_frame, radius, keep)
         _check(lib().bsa_request_submit(self._h, ctypes.byref(m), block_q, block_k, int(on_device), _dptr(q), _dptr(k),

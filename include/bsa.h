@@ -252,7 +252,8 @@ int32_t bsa_plan_coverage(bsa_plan_t plan, int32_t b, int32_t h, bsa_cov_sink_t 
  * stream and returns, so the planning of the next mask overlaps the forwards
  * already enqueued. At most `depth` plans are alive: a submit that finds
  * `depth` plans in flight first waits for the oldest one's forward and
- * destroys that plan. The request owns its plans.
+ * destroys that plan. The request owns its plans. A request is used by one
+ * thread at a time.
  */
 typedef struct bsa_request_s *bsa_request_t;
 
