@@ -215,6 +215,7 @@ struct bsa_plan_s {
     void *dev = nullptr;
     size_t dev_cap = 0;
     hipEvent_t uploaded = nullptr;
+    std::atomic<bool> upload_seen{false};  // `uploaded` has completed (forwards need not wait on it)
     // plans built on the device (bsa_plan_device): the image exists only in
     // device memory until a host query reads back its statistics (and, for
     // the coverage, the task and record sections)
@@ -1533,8 +1534,14 @@ extern "C" int32_t bsa_forward(bsa_plan_t p, const void *Q, const void *K, const
     int cur = 0;
     (void)hipGetDevice(&cur);
     if (cur != p->device) (void)hipSetDevice(p->device);
-    // the launch is ordered after the plan's upload (a no-op once it is done)
-    hipError_t e = hipStreamWaitEvent((hipStream_t)stream, p->uploaded, 0);
+    // the launch is ordered after the plan's upload; once the upload is seen
+    // complete, no wait goes into the stream any more
+    hipError_t e = hipSuccess;
+    if (!p->upload_seen.load(std::memory_order_acquire)) {
+        e = hipEventQuery(p->uploaded);
+        if (e == hipSuccess) p->upload_seen.store(true, std::memory_order_release);
+        else if (e == hipErrorNotReady) e = hipStreamWaitEvent((hipStream_t)stream, p->uploaded, 0);
+    }
     if (e == hipSuccess) {
         const Regime &R = kRegimes[p->regime];
         e = p->dtype == BSA_DTYPE_F32 ? launch_forward_f32(a, R.tile_q / 32, p->d, (hipStream_t)stream)
