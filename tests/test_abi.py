@@ -137,6 +137,30 @@ def test_request_argument_errors():
     L.bsa_request_destroy(None)  # NULL-safe
 
 
+def test_route_argument_errors():
+    """bsa_route_heads validates shapes, geometry and sampled rows before it
+    touches the device (the tensor addresses are never read here)."""
+    R = bsa.route_heads
+    rows = np.array([0, 5, 17], np.int32)
+    ok = dict(B=1, H=2, L=330, d=64, T=3, Hg=10, Wg=11)
+
+    def call(rows=rows, **kw):
+        a = dict(ok)
+        a.update(kw)
+        return R(16, 16, 16, a["B"], a["H"], a["L"], a["d"], a["T"], a["Hg"], a["Wg"], rows, stream=0,
+                 **{k: v for k, v in kw.items() if k in ("anchor_frame", "radius", "device")})
+
+    expect(bsa.ERR_INVALID_ARGUMENT, call, d=96, match="shape")
+    expect(bsa.ERR_INVALID_ARGUMENT, call, T=4, match="geometry")
+    expect(bsa.ERR_INVALID_ARGUMENT, call, anchor_frame=3, match="anchor")
+    expect(bsa.ERR_INVALID_ARGUMENT, call, radius=257, match="radius")
+    expect(bsa.ERR_INVALID_ARGUMENT, call, rows=np.array([330], np.int32), match="out of range")
+    expect(bsa.ERR_INVALID_ARGUMENT, call, rows=np.zeros(0, np.int32), match="n_rows")
+    expect(bsa.ERR_INVALID_ARGUMENT, call, device=-1, match="device")
+    L = bsa.lib()
+    assert L.bsa_route_heads(None, None, None, 1, 1, 64, 64, None, None, None, None) == bsa.ERR_INVALID_ARGUMENT
+
+
 def test_simulated_allocation_failure(monkeypatch):
     monkeypatch.setenv("BSA_TEST_FAIL_ALLOC", "1")
     expect(bsa.ERR_OUT_OF_MEMORY, bsa.plan, bsa.MASK_BLOCK_U8, 1, 2, 256, 64, 64, 64, data=_block(), device=-1)
