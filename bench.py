@@ -162,6 +162,119 @@ def cpu_baseline(w, Q, K, V, P_total, rows_per_head):
             "effective_gflops": 4 * w.d * P_sample / dt / 1e9}
 
 
+def kept_pairs(w, oracle) -> int:
+    """Kept (query, key) pairs of a workload's mask: block and slice masks
+    counted from their descriptors, video masks by the oracle per pattern."""
+    import numpy as np
+    import workloads as wl
+    if w.kind == wl.BLOCK:
+        rows = np.minimum(np.arange(1, w.nqb + 1) * w.bq, w.L) - np.arange(w.nqb) * w.bq
+        cols = np.minimum(np.arange(1, w.nkb + 1) * w.bk, w.L) - np.arange(w.nkb) * w.bk
+        m = w.block.reshape(-1, w.nqb, w.nkb).astype(np.int64)
+        return int(np.einsum("bij,i,j->", m, rows.astype(np.int64), cols.astype(np.int64)))
+    if w.kind == wl.SLICE:
+        nqb = -(-w.L // w.bq)
+        rows = np.minimum(np.arange(1, nqb + 1) * w.bq, w.L) - np.arange(nqb) * w.bq
+        lens = np.diff(np.asarray(w.row_ptr, dtype=np.int64)).reshape(-1, nqb)
+        return int((lens * rows[None, :]).sum())
+    per = {}
+    total = 0
+    for b in range(w.B):
+        for h in range(w.H):
+            key = (int(w.head_pattern[h]), int(w.head_layout[h]) if w.head_layout is not None else 0)
+            if key not in per:
+                per[key] = oracle.count_pairs(w, b, h)
+            total += per[key]
+    return total
+
+
+def time_config(torch, w, P, plan_reps=5, warmup=5, reps=30):
+    """Plan time (median of plan_reps host plans) and forward time (warmup
+    calls, then reps calls timed one by one with events) of one workload on
+    device-random bf16 inputs."""
+    import block_sparse_attention_fwd_amd as bsa
+    from bsa_helpers import plan_workload
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(w.cfg)
+    q, k, v = (torch.randn((w.B, w.H, w.L, w.d), generator=g, device="cuda:0").to(torch.bfloat16) for _ in range(3))
+    o = torch.empty_like(q)
+    plan_ms = []
+    p = None
+    for _ in range(plan_reps):
+        if p is not None:
+            p.close()
+        t0 = time.perf_counter()
+        p = plan_workload(w)
+        plan_ms.append((time.perf_counter() - t0) * 1e3)
+    # warmup: at least `warmup` calls and 50 ms of them (clocks settle)
+    n, t_end = 0, time.perf_counter() + 0.05
+    while n < warmup or time.perf_counter() < t_end:
+        bsa.forward(p, q, k, v, o)
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    ev = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        bsa.forward(p, q, k, v, o)
+        e1.record()
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in ev)
+    info = p.info()
+    p.close()
+    med = t[len(t) // 2]
+    flops = 4 * w.d * P
+    return {"config": w.name, "B": w.B, "H": w.H, "L": w.L, "d": w.d, "kind": w.kind, "block": [w.bq, w.bk],
+            "regime": info["regime"], "task_order": info["task_order"], "kept_pairs": P,
+            "computed_pairs": int(info["executed_pairs"]),
+            "plan_ms_median": round(sorted(plan_ms)[len(plan_ms) // 2], 3),
+            "fwd_ms_median": round(med, 4), "fwd_ms_p10": round(t[len(t) // 10], 4),
+            "fwd_ms_p90": round(t[(9 * len(t)) // 10], 4),
+            "effective_tflops": round(flops / (med * 1e-3) / 1e12, 1),
+            "pct_bf16_peak": round(100.0 * flops / (med * 1e-3) / 1e12 / MI355X_BF16_PEAK_TFLOPS, 2)}
+
+
+def all_configs(torch, oracle, wl):
+    """Every configuration at full size, one JSON line each: tiny, SVG runs A
+    and B, FG-Attn slices (M = 64 and 128), the 48 Tessera-style masks (and
+    the request's sum), high-res."""
+    works = [wl.tiny(), wl.svg("A"), wl.svg("B"), wl.fgattn(M=64), wl.fgattn(M=128)]
+    works[3].name, works[4].name = "fgattn_M64", "fgattn_M128"
+    # settle the clocks first (as the headline does): svg run B for 0.3 s
+    time_config(torch, works[2], 1, plan_reps=1, warmup=10, reps=1)
+    import block_sparse_attention_fwd_amd as bsa
+    from bsa_helpers import plan_workload
+    w0 = works[2]
+    q0 = torch.zeros((w0.B, w0.H, w0.L, w0.d), dtype=torch.bfloat16, device="cuda:0")
+    o0 = torch.empty_like(q0)
+    p0 = plan_workload(w0)
+    t_end = time.perf_counter() + 0.3
+    n = 0
+    while time.perf_counter() < t_end or n < 20:
+        bsa.forward(p0, q0, q0, q0, o0)
+        n += 1
+        if n % 20 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    p0.close()
+    for w in works:
+        log(f"[bench] {w.name}")
+        print(json.dumps(time_config(torch, w, kept_pairs(w, oracle))), flush=True)
+    total = 0.0
+    for i in range(48):
+        w = wl.tessera(i)
+        r = time_config(torch, w, kept_pairs(w, oracle), plan_reps=3, warmup=3, reps=10)
+        total += r["fwd_ms_median"]
+        print(json.dumps(r), flush=True)
+    print(json.dumps({"config": "tessera_request", "masks": 48, "sum_fwd_ms_median": round(total, 2)}), flush=True)
+    w = wl.highres()
+    log("[bench] highres")
+    print(json.dumps(time_config(torch, w, kept_pairs(w, oracle), plan_reps=3, warmup=2, reps=10)), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -172,6 +285,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--runs", default="A,B", help="comma list of runs to time (the headline needs B)")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="instead of the headline, time every configuration: one JSON line each")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes 5 times (HBM counter calibration)")
     args = ap.parse_args()
@@ -196,6 +311,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 5}), flush=True)
+        return
+    if args.all_configs:
+        all_configs(torch, oracle, wl)
         return
     wA, wB = wl.svg("A"), wl.svg("B")
     log("[bench] generating inputs")
