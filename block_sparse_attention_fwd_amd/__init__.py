@@ -29,7 +29,7 @@ DTYPE_BF16, DTYPE_F32 = 0, 1
 TILE_FULL, TILE_PARTIAL = 0, 1
 PRED_NONE, PRED_SUBBLOCK, PRED_VIDEO, PRED_LIST = 0, 1, 2, 3
 ORDER_XCD_GROUPED, ORDER_LONGEST_FIRST = 0, 1
-ABI_VERSION = 3  # the structures below mirror this version of bsa.h
+ABI_VERSION = 4  # the structures below mirror this version of bsa.h
 
 EXPORTED = ["bsa_abi_version", "bsa_plan_opts_default", "bsa_plan", "bsa_plan_device", "bsa_forward", "bsa_plan_destroy",
             "bsa_request_create", "bsa_request_submit", "bsa_request_finish", "bsa_request_stats",
@@ -41,7 +41,7 @@ EXPORTED = ["bsa_abi_version", "bsa_plan_opts_default", "bsa_plan", "bsa_plan_de
 class MaskDesc(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("data", ctypes.c_void_p), ("row_ptr", ctypes.c_void_p),
                 ("col_idx", ctypes.c_void_p), ("head_pattern", ctypes.c_void_p), ("anchor_frame", ctypes.c_int32),
-                ("radius", ctypes.c_int32)]
+                ("radius", ctypes.c_int32), ("nnz", ctypes.c_int64)]
 
 
 class PlanOpts(ctypes.Structure):
@@ -342,25 +342,30 @@ def _stream_handle(stream) -> int:
     return stream.cuda_stream
 
 
-def plan_device(kind: int, B: int, H: int, L: int, d: int, block_q: int, block_k: int, data, *, stream=None,
+def plan_device(kind: int, B: int, H: int, L: int, d: int, block_q: int, block_k: int, data=None, *, row_ptr=None,
+                col_idx=None, nnz: int = 0, stream=None,
                 dtype: int = DTYPE_BF16, T: int = 0, Hg: int = 0, Wg: int = 0, head_layout=None,
                 force_regime: int = -1, lut_path: Optional[str] = None, device: int = 0,
                 task_order: int = -1) -> Plan:
-    """bsa_plan_device: build a plan on the device from a BLOCK mask in device
-    memory (a contiguous torch tensor, or a raw device address: bytes for
-    BLOCK_U8, 64-bit rows for BLOCK_BITS), enqueued on `stream`. The returned
-    plan keeps a reference to the mask tensor."""
+    """bsa_plan_device: build a plan on the device from a mask in device memory
+    (contiguous torch tensors or raw device addresses: `data` bytes for
+    BLOCK_U8 or 64-bit rows for BLOCK_BITS; `row_ptr` int64, `col_idx` int32
+    and `nnz` for SLICE_CSR), enqueued on `stream`. The returned plan keeps
+    references to the mask tensors."""
     L_ = lib()
     keep = []
     m = MaskDesc()
     m.kind = kind
-    m.data = _dptr(data)
+    m.data = _dptr(data) if data is not None else None
+    m.row_ptr = _dptr(row_ptr) if row_ptr is not None else None
+    m.col_idx = _dptr(col_idx) if col_idx is not None else None
+    m.nnz = nnz
     o = _opts(dtype, T, Hg, Wg, head_layout, force_regime, lut_path, device, task_order, keep)
     h = ctypes.c_void_p()
     _check(L_.bsa_plan_device(ctypes.byref(m), B, H, L, d, block_q, block_k, ctypes.byref(o), _stream_handle(stream),
                               ctypes.byref(h)))
     pl = Plan(h.value, L, H, B)
-    pl._mask = data
+    pl._mask = (data, row_ptr, col_idx)
     return pl
 
 

@@ -223,6 +223,7 @@ struct bsa_plan_s {
     bool stats_read = false;
     bool host_copy = false;
     size_t off_stats = 0;
+    int64_t mask_errors = 0;   // invalid slice entries the planning kernels found
     uint8_t *small = nullptr;  // pinned upload source of the head flags and cost classes
     size_t small_cap = 0;
 };
@@ -658,8 +659,6 @@ static int32_t validate(const bsa_mask_desc_t *m, int32_t B, int32_t H, int64_t 
     if (!m) return fail(BSA_ERR_INVALID_ARGUMENT, "logical_mask is NULL");
     if (B < 1 || H < 1 || L < 1) return fail(BSA_ERR_INVALID_ARGUMENT, "B, H, L must be >= 1 (got %d, %d, %lld)", B, H, (long long)L);
     if (L > (1ll << 30)) return fail(BSA_ERR_UNSUPPORTED, "L = %lld exceeds 2^30", (long long)L);
-    if ((int64_t)B * H * L * 128 > (1ll << 31) * 64ll)
-        ;  // sizes are addressed with 64-bit arithmetic in the kernel; nothing to check here
     if (d != 64 && d != 128) return fail(BSA_ERR_UNSUPPORTED, "head dim d = %d (supported: 64, 128)", d);
     if (o.dtype != BSA_DTYPE_BF16 && o.dtype != BSA_DTYPE_F32) return fail(BSA_ERR_INVALID_ARGUMENT, "dtype %d", o.dtype);
     const bool has_geo = o.T || o.Hg || o.Wg;
@@ -701,7 +700,12 @@ static int32_t validate(const bsa_mask_desc_t *m, int32_t B, int32_t H, int64_t 
         if (!m->row_ptr || !m->col_idx) return fail(BSA_ERR_INVALID_ARGUMENT, "slice row_ptr/col_idx is NULL");
         if (bk != 1) return fail(BSA_ERR_INVALID_ARGUMENT, "slice masks need block_k = 1 (got %d)", bk);
         if (bq != 64 && bq != 128) return fail(BSA_ERR_UNSUPPORTED, "slice block M = %d (supported: 64, 128)", bq);
+        if (m->nnz < 0 || m->nnz > (1ll << 31) - 1) return fail(BSA_ERR_INVALID_ARGUMENT, "slice nnz = %lld", (long long)m->nnz);
+        // a device mask is checked by the planning kernels (see bsa_plan_device)
+        if (device_mask) return BSA_OK;
         const int64_t nl = (int64_t)B * H * ((L + bq - 1) / bq);
+        if (m->nnz && m->nnz != m->row_ptr[nl])
+            return fail(BSA_ERR_INVALID_MASK, "nnz = %lld but row_ptr ends at %lld", (long long)m->nnz, (long long)m->row_ptr[nl]);
         if (m->row_ptr[0] != 0) return fail(BSA_ERR_INVALID_MASK, "row_ptr[0] = %lld, expected 0", (long long)m->row_ptr[0]);
         for (int64_t i = 0; i < nl; ++i)
             if (m->row_ptr[i + 1] < m->row_ptr[i]) return fail(BSA_ERR_INVALID_MASK, "row_ptr decreases at %lld", (long long)i);
@@ -745,7 +749,7 @@ static double mask_density(const bsa_mask_desc_t &m, int32_t B, int32_t H, int64
 {
     if (m.kind == BSA_MASK_SLICE_CSR) {
         const int64_t nl = (int64_t)B * H * ((L + bq - 1) / bq);
-        return (double)m.row_ptr[nl] / ((double)nl * (double)L);
+        return (double)(m.nnz ? m.nnz : m.row_ptr[nl]) / ((double)nl * (double)L);
     }
     if (m.kind == BSA_MASK_VIDEO) return -1.0;
     const int64_t nqb = (L + bq - 1) / bq, nkb = (L + bk - 1) / bk;
@@ -1306,14 +1310,16 @@ extern "C" int32_t bsa_plan_device(const bsa_mask_desc_t *logical_mask, int32_t 
         bsa_plan_opts_default(&o);
         if (opts) o = *opts;
         if (!logical_mask) return fail(BSA_ERR_INVALID_ARGUMENT, "logical_mask is NULL");
-        if (logical_mask->kind != BSA_MASK_BLOCK_U8 && logical_mask->kind != BSA_MASK_BLOCK_BITS)
-            return fail(BSA_ERR_UNSUPPORTED, "device planning takes BLOCK masks (kind %d)", logical_mask->kind);
+        const bool slice = logical_mask->kind == BSA_MASK_SLICE_CSR;
+        if (logical_mask->kind != BSA_MASK_BLOCK_U8 && logical_mask->kind != BSA_MASK_BLOCK_BITS && !slice)
+            return fail(BSA_ERR_UNSUPPORTED, "device planning takes BLOCK and SLICE masks (kind %d)", logical_mask->kind);
         if (o.device < 0) return fail(BSA_ERR_INVALID_ARGUMENT, "device planning needs a device (opts.device = %d)", o.device);
         int32_t st = validate(logical_mask, B, H, L, d, block_q, block_k, o, true);
         if (st != BSA_OK) return st;
         const bsa_mask_desc_t &m = *logical_mask;
         int regime = 0, order = 0;
-        st = choose_regime(m, B, H, L, block_q, block_k, o, &regime, &order, false);
+        // a slice mask's density is nnz / (lists * L): known without reading it
+        st = choose_regime(m, B, H, L, block_q, block_k, o, &regime, &order, slice);
         if (st != BSA_OK) return st;
         const Regime &R = kRegimes[regime];
 
@@ -1327,12 +1333,15 @@ extern "C" int32_t bsa_plan_device(const bsa_mask_desc_t *logical_mask, int32_t 
         p->head_layout.assign(H, 0);
         if (o.head_layout) p->head_layout.assign(o.head_layout, o.head_layout + H);
         p->head_pattern.assign(H, 0);
-        p->mode = kModeBlock;
-        p->sub_q = std::min(block_q, R.tile_q);
-        p->sub_k = std::min(block_k, kTileK);
-        p->bq_shift = ilog2(p->sub_q);
-        p->bk_shift = ilog2(p->sub_k);
-        p->nsk = kTileK / p->sub_k;
+        p->mode = slice ? kModeGather : kModeBlock;
+        if (!slice) {
+            p->sub_q = std::min(block_q, R.tile_q);
+            p->sub_k = std::min(block_k, kTileK);
+            p->bq_shift = ilog2(p->sub_q);
+            p->bk_shift = ilog2(p->sub_k);
+            p->nsk = kTileK / p->sub_k;
+        }
+        p->gather_rows = p->ngidx = slice ? m.nnz : 0;
         p->device_planned = true;
 
         const int64_t nqt = (L + R.tile_q - 1) / R.tile_q, nkt = (L + kTileK - 1) / kTileK;
@@ -1371,15 +1380,16 @@ extern "C" int32_t bsa_plan_device(const bsa_mask_desc_t *logical_mask, int32_t 
         p->off_tasks = 0;
         p->off_tiles = align_up((size_t)std::max<int64_t>(1, NT) * sizeof(Task));
         p->off_gidx = p->off_tiles + align_up((size_t)std::max<int64_t>(1, cap) * sizeof(TileRec));
-        p->off_flags = p->off_gidx + align_up(sizeof(int32_t));
+        p->off_flags = p->off_gidx + align_up((size_t)std::max<int64_t>(1, p->ngidx) * sizeof(int32_t));
         p->off_coords = p->off_flags + align_up((size_t)H * sizeof(uint32_t));
         const size_t off_cnt = p->off_coords + align_up(sizeof(int32_t));
         const size_t off_full = off_cnt + align_up((size_t)NT * sizeof(int32_t));
-        const size_t off_hist = off_full + align_up((size_t)NT * sizeof(int32_t));
+        const size_t off_errs = off_full + align_up((size_t)NT * sizeof(int32_t));
+        const size_t off_hist = off_errs + align_up((size_t)NT * sizeof(int32_t));
         const size_t off_csum = off_hist + align_up((size_t)(nkeys * nchunks + 1) * sizeof(int32_t));
-        const size_t off_cls = off_csum + align_up((size_t)nchunks * 2 * sizeof(int64_t));
+        const size_t off_cls = off_csum + align_up((size_t)nchunks * 3 * sizeof(int64_t));
         p->off_stats = off_cls + align_up((size_t)(nkt + 1) * sizeof(int32_t));
-        p->img_bytes = p->off_stats + align_up(3 * sizeof(int64_t));
+        p->img_bytes = p->off_stats + align_up(4 * sizeof(int64_t));
 
         int cur = 0;
         (void)hipGetDevice(&cur);
@@ -1400,13 +1410,20 @@ extern "C" int32_t bsa_plan_device(const bsa_mask_desc_t *logical_mask, int32_t 
             DevPlanArgs a{};
             a.u8 = m.kind == BSA_MASK_BLOCK_U8 ? (const uint8_t *)m.data : nullptr;
             a.bits = m.kind == BSA_MASK_BLOCK_BITS ? (const uint64_t *)m.data : nullptr;
+            if (slice) {
+                a.row_ptr = m.row_ptr;
+                a.col_idx = m.col_idx;
+                a.nnz = m.nnz;
+                a.gidx = (int32_t *)(dv + p->off_gidx);
+                a.errs = (int32_t *)(dv + off_errs);
+            }
             a.L = L;
             a.BQ = R.tile_q;
             a.bq = block_q;
             a.bk = block_k;
             a.bqe = p->sub_q;
             a.bke = p->sub_k;
-            a.nsq = R.tile_q / p->sub_q;
+            a.nsq = slice ? 0 : R.tile_q / p->sub_q;
             a.nsk = p->nsk;
             a.lbq = ilog2(block_q);
             a.lbk = ilog2(block_k);
@@ -1460,18 +1477,20 @@ static int32_t read_back_device_plan(bsa_plan_s *p, bool image)
     (void)hipSetDevice(p->device);
     hipError_t e = hipEventSynchronize(p->uploaded);
     if (e == hipSuccess && !p->stats_read) {
-        int64_t stats[3] = {0, 0, 0};
+        int64_t stats[4] = {0, 0, 0, 0};
         e = hipMemcpy(stats, (uint8_t *)p->dev + p->off_stats, sizeof stats, hipMemcpyDeviceToHost);
         if (e == hipSuccess) {
             p->ntiles = stats[0];
             p->tiles_full = stats[1];
             p->tiles_partial = stats[0] - stats[1];
             p->tiles_empty = stats[2];
+            p->mask_errors = stats[3];
             p->stats_read = true;
         }
     }
     if (e == hipSuccess && image && !p->host_copy) {
-        p->img_vec.assign(p->off_gidx, 0);
+        // tasks and records, and the gathered keys of a slice plan
+        p->img_vec.assign(p->mode == kModeGather ? p->off_flags : p->off_gidx, 0);
         e = hipMemcpy(p->img_vec.data(), p->dev, p->img_vec.size(), hipMemcpyDeviceToHost);
         if (e == hipSuccess) {
             p->img = p->img_vec.data();
@@ -1572,6 +1591,9 @@ extern "C" int32_t bsa_plan_info(bsa_plan_t p, bsa_plan_info_t *out)
     out->plan_ns = p->plan_ns;
     for (int i = 0; i < 5; ++i) out->phase_ns[i] = p->phase_ns[i];
     out->task_order = p->task_order;
+    if (p->mask_errors)
+        return fail(BSA_ERR_INVALID_MASK, "the device mask had %lld invalid slice entries or lists (clamped or dropped)",
+                    (long long)p->mask_errors);
     return BSA_OK;
 }
 

@@ -14,6 +14,8 @@
 //
 //   map_tasks     one wave per task: records of the non-empty key tiles,
 //                 compacted in key order; tile counts
+//   slice_map     (SLICE masks, in place of map_tasks) one wave per list:
+//                 gather records and the plan's copy of the keys
 //   chunk_counts  one workgroup per chunk of tasks: tasks per sort key
 //                 (cost class, highest first; tasks without tiles last)
 //   scan_keys     one workgroup: exclusive prefix over (key, chunk), totals
@@ -155,6 +157,43 @@ __global__ __launch_bounds__(kWave) void map_tasks(DevPlanArgs a)
     }
 }
 
+// SLICE masks (FG-Attn, arXiv 2509.16518, abstract: M x 1 slices whose keys
+// are gathered into packed tiles): one wave per list. The list's keys become
+// gather records of kTileK keys (the last one short and PARTIAL), and are
+// copied into the plan clamped into [0, L), counting entries that are out of
+// range or not increasing; a list whose bounds fall outside [0, nnz] or span
+// more than L keys is taken as empty and counted once.
+__global__ __launch_bounds__(kWave) void slice_map(DevPlanArgs a)
+{
+    const int lane = threadIdx.x;
+    const int64_t t = blockIdx.x;
+    int64_t s = a.row_ptr[t], e = a.row_ptr[t + 1];
+    int err = 0;
+    if (s < 0 || e < s || e > a.nnz || e - s > a.L) {
+        err = lane == 0;
+        s = e = 0;
+    }
+    const int64_t n = e - s;
+    const int ntile = (int)((n + kTileK - 1) / kTileK);
+    TileRec *out = a.tiles + t * a.nkt;
+    for (int i = lane; i < ntile; i += kWave) {
+        const int cnt = (int)min((int64_t)kTileK, n - (int64_t)kTileK * i);
+        out[i] = TileRec{(int32_t)(s + (int64_t)kTileK * i), (uint32_t)cnt | (cnt < kTileK ? kPartial : 0u)};
+    }
+    const int32_t last = (int32_t)a.L - 1;
+    for (int64_t j = s + lane; j < e; j += kWave) {
+        const int32_t k = a.col_idx[j];
+        err += k < 0 || k > last || (j > s && k <= a.col_idx[j - 1]);
+        a.gidx[j] = min(max(k, 0), last);
+    }
+    for (int o = 32; o > 0; o >>= 1) err += __shfl_xor(err, o, kWave);
+    if (lane == 0) {
+        a.cnt[t] = ntile;
+        a.full[t] = (int)(n / kTileK);
+        a.errs[t] = err;
+    }
+}
+
 __global__ __launch_bounds__(kChunk) void chunk_counts(DevPlanArgs a)
 {
     __shared__ int h[kDevPlanMaxKeys];
@@ -162,18 +201,21 @@ __global__ __launch_bounds__(kChunk) void chunk_counts(DevPlanArgs a)
     const int64_t chunk = blockIdx.x, i = chunk * kChunk + threadIdx.x;
     for (int k = threadIdx.x; k < a.nkeys; k += kChunk) h[k] = 0;
     __syncthreads();
-    int c = 0, f = 0;
+    int c = 0, f = 0, e = 0;
     if (i < a.ntasks) {
         c = a.cnt[i];
         f = a.full[i];
+        e = a.errs ? a.errs[i] : 0;
         atomicAdd(&h[key_of(a, c)], 1);  // LDS
     }
-    int64_t sc = 0, sf = 0;
+    int64_t sc = 0, sf = 0, se = 0;
     (void)block_exclusive_scan<kChunk>(c, red, &sc);
     (void)block_exclusive_scan<kChunk>(f, red, &sf);
+    (void)block_exclusive_scan<kChunk>(e, red, &se);
     if (threadIdx.x == 0) {
-        a.csum[2 * chunk] = sc;
-        a.csum[2 * chunk + 1] = sf;
+        a.csum[3 * chunk] = sc;
+        a.csum[3 * chunk + 1] = sf;
+        a.csum[3 * chunk + 2] = se;
     }
     __syncthreads();
     for (int k = threadIdx.x; k < a.nkeys; k += kChunk) a.hist[(int64_t)k * a.nchunks + chunk] = h[k];
@@ -194,19 +236,22 @@ __global__ __launch_bounds__(kChunk) void scan_keys(DevPlanArgs a)
         run += v;
     }
     // per-chunk record sums
-    int64_t r = 0, f = 0;
+    int64_t r = 0, f = 0, e = 0;
     for (int64_t ch = threadIdx.x; ch < a.nchunks; ch += kChunk) {
-        r += a.csum[2 * ch];
-        f += a.csum[2 * ch + 1];
+        r += a.csum[3 * ch];
+        f += a.csum[3 * ch + 1];
+        e += a.csum[3 * ch + 2];
     }
-    int64_t rt = 0, ft = 0;
+    int64_t rt = 0, ft = 0, et = 0;
     (void)block_exclusive_scan<kChunk>(r, red, &rt);
     (void)block_exclusive_scan<kChunk>(f, red, &ft);
+    (void)block_exclusive_scan<kChunk>(e, red, &et);
     if (threadIdx.x == 0) {
         a.hist[n] = (int32_t)total;
         a.stats[0] = rt;
         a.stats[1] = ft;
-        a.stats[2] = a.ntasks * a.nkt - rt;
+        a.stats[2] = a.row_ptr ? 0 : a.ntasks * a.nkt - rt;  // gathered lists skip no tile
+        a.stats[3] = et;
     }
 }
 
@@ -262,6 +307,13 @@ __global__ __launch_bounds__(kChunk) void place_tasks(DevPlanArgs a)
 hipError_t launch_device_plan(const DevPlanArgs &a, hipStream_t stream)
 {
     if (a.ntasks <= 0) return hipSuccess;
+    if (a.row_ptr) {
+        hipLaunchKernelGGL(slice_map, dim3((unsigned)a.ntasks), dim3(kWave), 0, stream, a);
+        hipLaunchKernelGGL(chunk_counts, dim3((unsigned)a.nchunks), dim3(kChunk), 0, stream, a);
+        hipLaunchKernelGGL(scan_keys, dim3(1), dim3(kChunk), 0, stream, a);
+        hipLaunchKernelGGL(place_tasks, dim3((unsigned)a.nchunks), dim3(kChunk), 0, stream, a);
+        return hipGetLastError();
+    }
     const int nq = a.BQ / a.bqe, nk = kTileK / a.bke;
     auto map = [&](auto kernel) { hipLaunchKernelGGL(kernel, dim3((unsigned)a.ntasks), dim3(kWave), 0, stream, a); };
 #define BSA_MAP_CASE(Q, K)                                               \

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define BSA_ABI_VERSION 3
+#define BSA_ABI_VERSION 4
 
 typedef struct bsa_plan_s *bsa_plan_t;
 
@@ -108,6 +108,9 @@ typedef struct {
     const uint8_t *head_pattern;   /* VIDEO: [H] BSA_PAT_*                         */
     int32_t anchor_frame;          /* VIDEO spatial anchor frame (0 <= a < T)     */
     int32_t radius;                /* VIDEO temporal Chebyshev radius (>= 0)      */
+    int64_t nnz;                   /* SLICE_CSR: entries of col_idx; 0 = take
+                                      row_ptr's last entry (host masks); required
+                                      for device masks (bsa_plan_device)          */
 } bsa_mask_desc_t;
 
 typedef struct {
@@ -200,22 +203,30 @@ int32_t bsa_plan(const bsa_mask_desc_t *logical_mask, int32_t B, int32_t H, int6
                  int32_t block_q, int32_t block_k, const bsa_plan_opts_t *opts, bsa_plan_t *out_plan);
 
 /*
- * Build a plan on the device for a BLOCK mask (BLOCK_U8 or BLOCK_BITS) whose
- * data is already in DEVICE memory (logical_mask->data is a device pointer
- * of the layout described above): the tile mapping and the task order run as
- * kernels on `stream` (a hipStream_t; NULL = the default stream of
- * opts->device), with no copy of the mask to the host (Tessera, arXiv
- * 2609.25869, abstract: dynamic masks, preparation kept cheap). Returns after
- * enqueueing; a bsa_forward on the same stream runs after the planning, one
- * on another stream waits for it. The mask must stay valid until the planning
- * work has run. The plan equals the one bsa_plan builds from the same mask,
- * except that the regime and order come from the table without the mask
- * density, and bits past the last key block of a BLOCK_BITS row are ignored.
+ * Build a plan on the device for a BLOCK mask (BLOCK_U8 or BLOCK_BITS) or a
+ * SLICE_CSR mask whose arrays are already in DEVICE memory (data, or row_ptr
+ * and col_idx, are device pointers of the layouts described above; a SLICE
+ * mask needs nnz): the tile mapping and the task order run as kernels on
+ * `stream` (a hipStream_t; NULL = the default stream of opts->device), with no
+ * copy of the mask to the host (Tessera, arXiv 2609.25869, abstract: dynamic
+ * masks, preparation kept cheap; FG-Attn, arXiv 2509.16518, abstract: slices
+ * whose keys are gathered). Returns after enqueueing; a bsa_forward on the
+ * same stream runs after the planning, one on another stream waits for it.
+ * The mask must stay valid until the planning work has run (the plan keeps
+ * its own copy of the slice keys). The plan equals the one bsa_plan builds
+ * from the same mask, except that BLOCK regimes and orders come from the
+ * table without the mask density, and bits past the last key block of a
+ * BLOCK_BITS row are ignored. The host cannot validate a device mask: slice
+ * keys outside [0, L) are clamped into it, a list whose row_ptr bounds fall
+ * outside [0, nnz] or span more than L keys is taken as empty, and keys that
+ * are not strictly increasing are used as given; bsa_plan_info then returns
+ * BSA_ERR_INVALID_MASK (after filling its output). Such a plan stays safe to
+ * run.
  * Device memory: every task has room for a record per key tile (8 bytes per
  * (task, key tile) pair). bsa_plan_info waits for the planning work and reads
  * back its statistics; bsa_plan_coverage also reads back the task and record
  * arrays. Errors: INVALID_ARGUMENT (as bsa_plan; host-only device -1),
- * UNSUPPORTED (other mask kinds, 2^31 or more (task, key tile) pairs, 2^24 or
+ * UNSUPPORTED (VIDEO masks, 2^31 or more (task, key tile) pairs, 2^24 or
  * more tasks, the longest-first order with more than 8190 key tiles),
  * OUT_OF_MEMORY, HIP.
  */

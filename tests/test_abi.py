@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     L = bsa.lib()
-    assert L.bsa_abi_version() == bsa.ABI_VERSION == 3
+    assert L.bsa_abi_version() == bsa.ABI_VERSION == 4
     assert L.bsa_status_str(bsa.ERR_INVALID_MASK) == b"BSA_ERR_INVALID_MASK"
     assert L.bsa_status_str(99) == b"BSA_ERR_UNKNOWN"
     assert len(bsa.regimes()) == L.bsa_regime_count() >= 3
@@ -115,7 +115,11 @@ def test_device_planning_argument_errors():
     (the mask address is never read here)."""
     PD = bsa.plan_device
     expect(bsa.ERR_UNSUPPORTED, PD, bsa.MASK_VIDEO, 1, 2, 256, 64, 1, 1, 16, stream=0, match="BLOCK")
-    expect(bsa.ERR_UNSUPPORTED, PD, bsa.MASK_SLICE_CSR, 1, 2, 256, 64, 64, 1, 16, stream=0, match="BLOCK")
+    expect(bsa.ERR_INVALID_ARGUMENT, PD, bsa.MASK_SLICE_CSR, 1, 2, 256, 64, 64, 1, stream=0, match="NULL")
+    expect(bsa.ERR_INVALID_ARGUMENT, PD, bsa.MASK_SLICE_CSR, 1, 2, 256, 64, 64, 1, row_ptr=16, col_idx=16, nnz=-1,
+           stream=0, match="nnz")
+    expect(bsa.ERR_UNSUPPORTED, PD, bsa.MASK_SLICE_CSR, 1, 2, 256, 64, 32, 1, row_ptr=16, col_idx=16, nnz=4,
+           stream=0, match="slice block")
     expect(bsa.ERR_INVALID_ARGUMENT, PD, bsa.MASK_BLOCK_U8, 1, 2, 256, 64, 64, 64, 16, stream=0, device=-1,
            match="device")
     expect(bsa.ERR_INVALID_ARGUMENT, PD, bsa.MASK_BLOCK_U8, 1, 2, 256, 64, 64, 64, 0, stream=0, match="NULL")

@@ -197,3 +197,106 @@ def test_device_planning_time():
         rows.append((i, w.bq, w.bk, th * 1e3, td * 1e3))
         log(f"[plan time] tessera{i} {w.bq}x{w.bk} host {th * 1e3:.3f} ms device {td * 1e3:.3f} ms")
     assert all(r[4] < r[3] + 2.0 for r in rows)
+
+
+# ---- SLICE masks (FG-Attn M x 1 slices) planned on the device
+
+def _slice_case(M, cfg=61, B=2, H=2, T=3, Hg=10, Wg=11):
+    L = T * Hg * Wg
+    w = wl.Workload(f"slice_M{M}", cfg, B, H, L, 64, T, Hg, Wg, wl.SLICE, M, 1)
+    w.row_ptr, w.col_idx = wl.slice_lists(cfg, B, H, L, M)
+    return w
+
+
+def _plan_slice_device(w, **kw):
+    rp = torch.from_numpy(np.ascontiguousarray(w.row_ptr, dtype=np.int64)).to("cuda:0")
+    ci = torch.from_numpy(np.ascontiguousarray(w.col_idx, dtype=np.int32)).to("cuda:0")
+    return bsa.plan_device(bsa.MASK_SLICE_CSR, w.B, w.H, w.L, w.d, w.bq, 1, row_ptr=rp, col_idx=ci,
+                           nnz=int(w.row_ptr[-1]), T=w.T, Hg=w.Hg, Wg=w.Wg, head_layout=w.head_layout, **kw)
+
+
+def _same_slice_plan(w, ph, pd, heads):
+    ih, idv = ph.info(), pd.info()
+    for k in INFO_KEYS:
+        assert ih[k] == idv[k], (k, ih[k], idv[k])
+    for b, h in heads:
+        ch, cd = ph.coverage(b, h), pd.coverage(b, h)
+        assert len(ch) == len(cd)
+        for x, y in zip(ch, cd):
+            xk, yk = x.pop("keys"), y.pop("keys")
+            assert x == y and np.array_equal(xk, yk)
+
+
+@pytest.mark.parametrize("M", [64, 128])
+def test_device_slice_plan_equals_host_plan(M):
+    w = _slice_case(M)
+    w.head_layout = np.array([0, 1], np.uint8)
+    Q, K, V = wl.make_qkv(w)
+    for order in ORDERS:
+        log(f"[case] slice M={M} order={order}")
+        ph = plan_workload(w, task_order=order)
+        pd = _plan_slice_device(w, task_order=order)
+        _same_slice_plan(w, ph, pd, [(b, h) for b in range(w.B) for h in range(w.H)])
+        Od, _ = run_gpu(w, Q, K, V, plan=pd)
+        Oh, _ = run_gpu(w, Q, K, V, plan=ph)
+        assert np.array_equal(Od, Oh)
+        compare(w, Q, K, V, Od, label=f"slice M{M} device plan order {order}")
+
+
+def test_device_slice_plan_full_size_fgattn():
+    """FG-Attn slices at full size (24 heads, 21 x 30x52 tokens, M = 64): the
+    device plan equals the host plan and runs to the same bits; planning time
+    logged."""
+    w = wl.fgattn()
+    ph = plan_workload(w)
+    pd = _plan_slice_device(w)
+    _same_slice_plan(w, ph, pd, [(0, 0), (0, 13), (0, w.H - 1)])
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(3)
+    q, k, v = (torch.randn((w.B, w.H, w.L, w.d), generator=g, device="cuda:0").to(torch.bfloat16) for _ in range(3))
+    oh, od = torch.empty_like(q), torch.empty_like(q)
+    bsa.forward(ph, q, k, v, oh)
+    bsa.forward(pd, q, k, v, od)
+    torch.cuda.synchronize()
+    assert torch.equal(oh, od)
+    rp = torch.from_numpy(np.ascontiguousarray(w.row_ptr, dtype=np.int64)).to("cuda:0")
+    ci = torch.from_numpy(np.ascontiguousarray(w.col_idx, dtype=np.int32)).to("cuda:0")
+    nnz = int(w.row_ptr[-1])
+    for _ in range(2):
+        p = bsa.plan_device(bsa.MASK_SLICE_CSR, w.B, w.H, w.L, w.d, w.bq, 1, row_ptr=rp, col_idx=ci, nnz=nnz)
+    torch.cuda.synchronize()
+    n = 5
+    t0 = time.perf_counter()
+    for _ in range(n):
+        p = bsa.plan_device(bsa.MASK_SLICE_CSR, w.B, w.H, w.L, w.d, w.bq, 1, row_ptr=rp, col_idx=ci, nnz=nnz)
+    torch.cuda.synchronize()
+    td = (time.perf_counter() - t0) / n
+    t0 = time.perf_counter()
+    for _ in range(n):
+        p = plan_workload(w)
+    torch.cuda.synchronize()
+    th = (time.perf_counter() - t0) / n
+    del p
+    log(f"[plan time] fgattn M=64 ({nnz} slice keys): host {th * 1e3:.3f} ms device {td * 1e3:.3f} ms")
+
+
+def test_device_slice_plan_with_invalid_entries_is_reported_and_safe():
+    """Keys out of range are clamped, a decreasing pair is used as given, a
+    list whose bounds leave [0, nnz] is dropped; the plan reports
+    INVALID_MASK and its forward runs (every gathered row inside the head)."""
+    w = _slice_case(64, cfg=62, B=1)
+    rp = np.ascontiguousarray(w.row_ptr, dtype=np.int64).copy()
+    ci = np.ascontiguousarray(w.col_idx, dtype=np.int32).copy()
+    ci[3] = w.L + 50     # out of range
+    ci[7] = -4           # out of range
+    ci[12], ci[13] = ci[13], ci[12]  # not increasing
+    rpd = torch.from_numpy(rp).to("cuda:0")
+    rpd[5] = int(rp[-1]) + 1000  # list 4 ends and list 5 starts past nnz
+    cid = torch.from_numpy(ci).to("cuda:0")
+    p = bsa.plan_device(bsa.MASK_SLICE_CSR, w.B, w.H, w.L, w.d, 64, 1, row_ptr=rpd, col_idx=cid, nnz=int(rp[-1]))
+    with pytest.raises(bsa.BSAError) as e:
+        p.info()
+    assert e.value.status == bsa.ERR_INVALID_MASK
+    Q, K, V = wl.make_qkv(w)
+    O, _ = run_gpu(w, Q, K, V, plan=p)
+    assert np.all(np.isfinite(O))
