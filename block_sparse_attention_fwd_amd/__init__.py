@@ -293,15 +293,19 @@ class Request:
         self._masks = []  # device masks of the plans that may still be in flight
 
     def submit(self, kind: int, block_q: int, block_k: int, q, k, v, o, *, data=None, row_ptr=None, col_idx=None,
-               head_pattern=None, anchor_frame: int = 0, radius: int = 2, on_device: bool = False) -> None:
+               nnz: int = 0, head_pattern=None, anchor_frame: int = 0, radius: int = 2,
+               on_device: bool = False) -> None:
         keep = []
         if on_device:
             m = MaskDesc()
             m.kind = kind
-            m.data = _dptr(data)
+            m.data = _dptr(data) if data is not None else None
+            m.row_ptr = _dptr(row_ptr) if row_ptr is not None else None
+            m.col_idx = _dptr(col_idx) if col_idx is not None else None
+            m.nnz = nnz
             # a plan (and the planning that read its mask) is retired once
             # `depth` newer plans exist: older masks may go
-            self._masks.append(data)
+            self._masks.append((data, row_ptr, col_idx))
             if len(self._masks) > self._depth + 1:
                 self._masks.pop(0)
         else:
