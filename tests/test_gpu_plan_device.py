@@ -300,3 +300,23 @@ def test_device_slice_plan_with_invalid_entries_is_reported_and_safe():
     Q, K, V = wl.make_qkv(w)
     O, _ = run_gpu(w, Q, K, V, plan=p)
     assert np.all(np.isfinite(O))
+
+
+def test_device_plan_edge_shapes():
+    """A sequence shorter than one key tile, and bit rows with stray bits
+    past the last key block (ignored by the device planner): the device plan
+    equals the host plan of the clean mask."""
+    w = wl.Workload("short", 71, 1, 3, 40, 64, 0, 0, 0, wl.BLOCK, 32, 32)
+    w.block = (np.random.default_rng(5).random((1, 3, w.nqb, w.nkb)) < 0.6).astype(np.uint8)
+    for bits in (False, True):
+        _same_plan(w, plan_workload(w, bits=bits), plan_workload_device(w, bits=bits))
+    w = wl.Workload("stray", 72, 1, 2, 330, 64, 0, 0, 0, wl.BLOCK, 32, 32)
+    w.block = (np.random.default_rng(6).random((1, 2, w.nqb, w.nkb)) < 0.3).astype(np.uint8)
+    bits = w.block_bits().copy()
+    bits[..., -1] |= np.uint64(1) << np.uint64(63)  # nkb = 11: bit 63 lies past the last block
+    md = torch.from_numpy(bits.view(np.int64)).to("cuda:0")
+    pd = plan_workload_device(w, bits=True, mask=md)
+    _same_plan(w, plan_workload(w, bits=True), pd)
+    Q, K, V = wl.make_qkv(w)
+    O, _ = run_gpu(w, Q, K, V, plan=pd)
+    compare(w, Q, K, V, O, label="stray bits")
