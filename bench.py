@@ -292,8 +292,8 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}, "
-              f"WORLD_SIZE {world}); heads would be sharded across GPUs with no exchange, see DESIGN.md.",
+        print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE {world}); heads would be sharded across GPUs with no exchange.",
               file=sys.stderr)
         sys.exit(2)
 

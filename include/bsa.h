@@ -53,7 +53,7 @@ enum {
     BSA_OK = 0,
     BSA_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad shape, bad option          */
     BSA_ERR_INVALID_MASK = 2,     /* mask contents out of range / unsorted / dup   */
-    BSA_ERR_UNSUPPORTED = 3,      /* valid request this build does not implement   */
+    BSA_ERR_UNSUPPORTED = 3,      /* valid request the library does not implement  */
     BSA_ERR_OUT_OF_MEMORY = 4,    /* host or device allocation failed              */
     BSA_ERR_HIP = 5,              /* a HIP runtime call failed (message has it)    */
     BSA_ERR_INTERNAL = 6
