@@ -138,6 +138,31 @@ def test_task_orders_write_identical_outputs():
         assert torch.equal(o, ref)
 
 
+def test_one_plan_on_concurrent_streams():
+    """A plan is immutable: forwards of one plan on two streams at once, into
+    different outputs and on different inputs, each write the bits a lone
+    forward writes."""
+    w = wl.svg("B", H=4, T=5, Hg=7, Wg=13)
+    Q, K, V = wl.make_qkv(w)
+    q, k, v = to_device(Q), to_device(K), to_device(V)
+    q2, k2, v2 = to_device(V), to_device(Q), to_device(K)  # a second input set
+    p = plan_workload(w)
+    ref1, ref2 = torch.empty_like(q), torch.empty_like(q)
+    bsa.forward(p, q, k, v, ref1)
+    bsa.forward(p, q2, k2, v2, ref2)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    o1 = [torch.full_like(q, float("nan")) for _ in range(8)]
+    o2 = [torch.full_like(q, float("nan")) for _ in range(8)]
+    torch.cuda.synchronize()
+    for i in range(8):
+        bsa.forward(p, q, k, v, o1[i], stream=s1)
+        bsa.forward(p, q2, k2, v2, o2[i], stream=s2)
+    torch.cuda.synchronize()
+    for a, b in zip(o1, o2):
+        assert torch.equal(a, ref1) and torch.equal(b, ref2)
+
+
 @pytest.mark.parametrize("regime", [-1, 4])
 @pytest.mark.parametrize("run", ["A", "B"])
 def test_svg_full_size_sampled(run, regime):
