@@ -379,7 +379,7 @@ def main():
         "parity": B.get("parity"),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MI355X_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MI355X_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
-                     "kernel": "bsa_fwd_bf16<4,128>", "flops_per_launch": flops},
+                     "kernel": "bsa_fwd_bf16<4,1,128,2>", "flops_per_launch": flops},
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on a row sample")

@@ -100,8 +100,8 @@ struct Regime {
 
 static const Regime kRegimes[] = {
     {0, 128, 4, 1},  // 0: 128 x 64 tiles, 4 waves of 32 rows
-    {0, 64, 2, 1},   // 1: 64 x 64 tiles, 2 waves of 32 rows
-    {1, 64, 2, 1},   // 2: 64-query gather tiles
+    {0, 64, 2, 1},   // 1: 64 x 64 tiles, 2 waves of 32 rows (d = 128: one LDS buffer, four workgroups per CU)
+    {1, 64, 2, 1},   // 2: 64-query gather tiles (as regime 1)
     {1, 128, 4, 1},  // 3: 128-query gather tiles
     {0, 256, 8, 1},  // 4: 256 x 64 tiles, 8 waves of 32 rows
 };

@@ -128,13 +128,16 @@ __device__ __forceinline__ bf16x8 load_bf16x8(const __bf16 *p)
 // Kernel: NW waves per workgroup, each wave owns RB consecutive blocks of 32
 // query rows. Every K operand read from LDS feeds RB score MFMAs and every V
 // operand read feeds RB output MFMAs, so LDS bytes per MFMA fall as 1/RB.
-template <int NW, int RB, int D>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1 && NW >= 4 ? 2 : 1, RB == 1 ? 2 : 1))) void bsa_fwd_bf16(KernelArgs a)
+template <int NW, int RB, int D, int NB = 2>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1 && (NW >= 4 || NB == 1) ? 2 : 1, RB == 1 ? 2 : 1))) void bsa_fwd_bf16(KernelArgs a)
 {
     using C = Cfg<NW, RB, D>;
-    __shared__ __attribute__((aligned(16))) int kcoord[2][C::BK];  // [buffer] video key coordinates
-    __shared__ __attribute__((aligned(1024))) unsigned char ksm[2][C::TILEB];  // [buffer] swizzled K tile
-    __shared__ __attribute__((aligned(1024))) unsigned char vsm[2][C::TILEB];  // [buffer] swizzled V tile
+    // NB = 2: tile j + 1 lands in the other buffer while tile j is computed;
+    // NB = 1: one buffer, filled after each tile (other workgroups on the CU
+    // cover the copy), so that twice as many workgroups fit in LDS
+    __shared__ __attribute__((aligned(16))) int kcoord[NB][C::BK];  // [buffer] video key coordinates
+    __shared__ __attribute__((aligned(1024))) unsigned char ksm[NB][C::TILEB];  // [buffer] swizzled K tile
+    __shared__ __attribute__((aligned(1024))) unsigned char vsm[NB][C::TILEB];  // [buffer] swizzled V tile
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
@@ -299,11 +302,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1
         // below is unrolled by two), so every LDS operand address is a
         // loop-invariant register plus an immediate offset
         auto tile_step = [&](const int j, auto cur_c) {
-            constexpr int cur = decltype(cur_c)::value;
+            constexpr int cur = NB == 1 ? 0 : decltype(cur_c)::value;
             if ((j & 63) == 0 && j > 0) rs.advance();
             const TileRec rec = rs.get(j);
             const bool more = j + 1 < ntile;
-            if (more) {
+            if (NB == 2 && more) {
                 fetch_tile(rs.get(j + 1), idx_nxt, cur ^ 1);
                 if (gather && j + 2 < ntile) load_indices(rs.get(j + 2), idx_nxt);
             }
@@ -401,8 +404,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1
             __builtin_amdgcn_sched_group_barrier(0x008, 2 * RB, 1);
             }
 
-            if (more) finish_tile(cur ^ 1);
-            __syncthreads();
+            if constexpr (NB == 2) {
+                if (more) finish_tile(cur ^ 1);
+                __syncthreads();
+            } else {
+                __syncthreads();  // every wave is done with the buffer
+                if (more) {
+                    fetch_tile(rs.get(j + 1), idx_nxt, 0);
+                    if (gather && j + 2 < ntile) load_indices(rs.get(j + 2), idx_nxt);
+                    finish_tile(0);
+                    __syncthreads();
+                }
+            }
         };
         int j = 0;
         for (; j + 1 < ntile; j += 2) {
@@ -438,10 +451,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1
     }
 }
 
-template <int NW, int RB, int D>
+template <int NW, int RB, int D, int NB = 2>
 static hipError_t launch(const KernelArgs &a, hipStream_t stream)
 {
-    hipLaunchKernelGGL((bsa_fwd_bf16<NW, RB, D>), dim3(a.ntasks), dim3(NW * 64), 0, stream, a);
+    hipLaunchKernelGGL((bsa_fwd_bf16<NW, RB, D, NB>), dim3(a.ntasks), dim3(NW * 64), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -453,7 +466,10 @@ hipError_t launch_forward(const KernelArgs &a, int waves, int rb, int d, int dty
         if (waves == 8 && d == 64) return launch<8, 1, 64>(a, stream);
         if (waves == 4 && d == 128) return launch<4, 1, 128>(a, stream);
         if (waves == 4 && d == 64) return launch<4, 1, 64>(a, stream);
-        if (waves == 2 && d == 128) return launch<2, 1, 128>(a, stream);
+        // two waves, d = 128: single-buffered, so that four workgroups (two
+        // waves per SIMD) fit in LDS; measured faster than double-buffered
+        // with one wave per SIMD (FG-Attn M = 64: 4.42 -> 4.03 ms)
+        if (waves == 2 && d == 128) return launch<2, 1, 128, 1>(a, stream);
         if (waves == 2 && d == 64) return launch<2, 1, 64>(a, stream);
     }
     return hipErrorInvalidValue;
