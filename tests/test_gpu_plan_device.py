@@ -306,17 +306,39 @@ def test_device_plan_edge_shapes():
     """A sequence shorter than one key tile, and bit rows with stray bits
     past the last key block (ignored by the device planner): the device plan
     equals the host plan of the clean mask."""
+    # the device planner chooses its regime without the mask density, so the
+    # host plan is made with the regime and order the device plan took
+    def host_like(w, pd, bits):
+        i = pd.info()
+        return plan_workload(w, bits=bits, force_regime=i["regime"], task_order=i["task_order"])
+
     w = wl.Workload("short", 71, 1, 3, 40, 64, 0, 0, 0, wl.BLOCK, 32, 32)
     w.block = (np.random.default_rng(5).random((1, 3, w.nqb, w.nkb)) < 0.6).astype(np.uint8)
     for bits in (False, True):
-        _same_plan(w, plan_workload(w, bits=bits), plan_workload_device(w, bits=bits))
+        pd = plan_workload_device(w, bits=bits)
+        _same_plan(w, host_like(w, pd, bits), pd)
     w = wl.Workload("stray", 72, 1, 2, 330, 64, 0, 0, 0, wl.BLOCK, 32, 32)
     w.block = (np.random.default_rng(6).random((1, 2, w.nqb, w.nkb)) < 0.3).astype(np.uint8)
     bits = w.block_bits().copy()
     bits[..., -1] |= np.uint64(1) << np.uint64(63)  # nkb = 11: bit 63 lies past the last block
     md = torch.from_numpy(bits.view(np.int64)).to("cuda:0")
     pd = plan_workload_device(w, bits=True, mask=md)
-    _same_plan(w, plan_workload(w, bits=True), pd)
+    _same_plan(w, host_like(w, pd, True), pd)
     Q, K, V = wl.make_qkv(w)
     O, _ = run_gpu(w, Q, K, V, plan=pd)
     compare(w, Q, K, V, O, label="stray bits")
+
+
+def test_device_plan_regime_ignores_density(tmp_path):
+    """With a table whose rules split one block shape by density, the host
+    planner takes the rule of the mask's density and the device planner, which
+    never reads the mask on the host, the first rule of the shape and length."""
+    lut = tmp_path / "split.lut"
+    lut.write_text("block 32 32 0 0.5 0 9999 1 lpt\n"
+                   "block 32 32 0.5 1 0 9999 4 xcd\n")
+    w = wl.Workload("split", 73, 1, 2, 330, 64, 0, 0, 0, wl.BLOCK, 32, 32)
+    w.block = (np.random.default_rng(7).random((1, 2, w.nqb, w.nkb)) < 0.8).astype(np.uint8)
+    ih = plan_workload(w, lut_path=str(lut)).info()
+    idv = plan_workload_device(w, lut_path=str(lut)).info()
+    assert (ih["regime"], ih["task_order"]) == (4, bsa.ORDER_XCD_GROUPED)
+    assert (idv["regime"], idv["task_order"]) == (1, bsa.ORDER_LONGEST_FIRST)
