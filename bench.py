@@ -243,10 +243,13 @@ def time_config(torch, w, P, plan_reps=5, warmup=5, reps=30):
             "pct_bf16_peak": round(100.0 * flops / (med * 1e-3) / 1e12 / MI355X_BF16_PEAK_TFLOPS, 2)}
 
 
-def all_configs(torch, oracle, wl):
+def all_configs(torch, oracle, wl, only=None):
     """Every configuration at full size, one JSON line each: tiny, SVG runs A
     and B, FG-Attn slices (M = 64 and 128), the 48 Tessera-style masks (and
-    the request's sum), high-res."""
+    the request's sum), high-res. ``only``: a set of configuration names to
+    run instead of all (the request's sum then needs all 48 masks)."""
+    def wanted(name):
+        return only is None or name in only
     works = [wl.tiny(), wl.svg("A"), wl.svg("B"), wl.fgattn(M=64), wl.fgattn(M=128)]
     works[3].name, works[4].name = "fgattn_M64", "fgattn_M128"
     # settle the clocks first (as the headline does): svg run B for 0.3 s
@@ -267,15 +270,22 @@ def all_configs(torch, oracle, wl):
     torch.cuda.synchronize()
     p0.close()
     for w in works:
+        if not wanted(w.name):
+            continue
         log(f"[bench] {w.name}")
         print(json.dumps(time_config(torch, w, kept_pairs(w, oracle))), flush=True)
     total = 0.0
     for i in range(48):
+        if not wanted(f"tessera{i}"):
+            continue
         w = wl.tessera(i)
         r = time_config(torch, w, kept_pairs(w, oracle), plan_reps=3, warmup=3, reps=10)
         total += r["fwd_ms_median"]
         print(json.dumps(r), flush=True)
-    print(json.dumps({"config": "tessera_request", "masks": 48, "sum_fwd_ms_median": round(total, 2)}), flush=True)
+    if only is None:
+        print(json.dumps({"config": "tessera_request", "masks": 48, "sum_fwd_ms_median": round(total, 2)}), flush=True)
+    if not wanted("highres"):
+        return
     w = wl.highres()
     log("[bench] highres")
     print(json.dumps(time_config(torch, w, kept_pairs(w, oracle), plan_reps=3, warmup=2, reps=10)), flush=True)
@@ -293,6 +303,9 @@ def main():
     ap.add_argument("--runs", default="A,B", help="comma list of runs to time (the headline needs B)")
     ap.add_argument("--all-configs", action="store_true",
                     help="instead of the headline, time every configuration: one JSON line each")
+    ap.add_argument("--configs", default=None,
+                    help="with --all-configs: comma list of configuration names to run (tiny, svgA, svgB, "
+                         "fgattn_M64, fgattn_M128, tessera0..tessera47, highres)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes 5 times (HBM counter calibration)")
     args = ap.parse_args()
@@ -319,7 +332,7 @@ def main():
         print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 5}), flush=True)
         return
     if args.all_configs:
-        all_configs(torch, oracle, wl)
+        all_configs(torch, oracle, wl, None if args.configs is None else set(args.configs.split(",")))
         return
     wA, wB = wl.svg("A"), wl.svg("B")
     log("[bench] generating inputs")
