@@ -7,7 +7,8 @@ preparation cheap at run time. This script is that offline step: for every
 bin of the table's features -- mask kind, logical block shape, kept-block
 density, sequence length -- it plans and runs synthetic requests of that bin
 with every regime that can run them, times the forward passes on the GPU and
-writes the fastest regime of each bin as one rule of the table.
+writes the fastest regime of each bin as one rule of the table (the default
+unless another wins by more than 2%).
 
 Inputs are seeded and synthetic (workloads module): BLOCK masks in banded,
 local-window and random layouts, video head routing (half spatial heads,
@@ -51,6 +52,19 @@ def log(*a):
 
 def oname(order):
     return dict(ORDERS)[order]
+
+
+# a choice other than the default (the first timed: regime 0, or the slice
+# height's gather regime, with the XCD-grouped order) must win by more than
+# this fraction; within it the timings do not tell the choices apart (three
+# interleaved rounds spread by about 1%)
+MARGIN = 0.02
+
+
+def pick(times):
+    default = next(iter(times))
+    best = min(times, key=times.get)
+    return best if times[best] < (1.0 - MARGIN) * times[default] else default
 
 
 def vname(x):
@@ -115,7 +129,7 @@ def main():
         # video head routing
         wv = wl.svg("B", H=H, T=T, Hg=Hg, Wg=Wg, d=d, cfg=9)
         tv = time_regimes(bsa, torch, wv, TILE_REGIMES, q, k, v, o, args.reps)
-        best = min(tv, key=tv.get)
+        best = pick(tv)
         log(f"[lut] video L={L}: " + ", ".join(f"{vname(x)} {t:.4f} ms" for x, t in tv.items()) + f" -> {vname(best)}")
         notes.append(f"video L={L}: " + " ".join(f"{vname(x)}={t:.4f}ms" for x, t in tv.items()))
         rules.append(f"video   *       *       -1         1          {llo:<4d} {lhi:<10d} {best[0]} {oname(best[1])}")
@@ -126,7 +140,7 @@ def main():
                     w = wl.block_request(f"lut_{bq}x{bk}_{rho}_{lay}", 9, li, bq, bk, rho, lay, H, T, Hg, Wg, d)
                     for x, t in time_regimes(bsa, torch, w, TILE_REGIMES, q, k, v, o, args.reps).items():
                         tot[x] = tot.get(x, 0.0) + t
-                best = min(tot, key=tot.get)
+                best = pick(tot)
                 log(f"[lut] block {bq}x{bk} density {rho} L={L}: "
                     + ", ".join(f"{vname(x)} {t:.4f} ms" for x, t in tot.items()) + f" -> {vname(best)}")
                 notes.append(f"block {bq}x{bk} rho={rho} L={L} (sum over {len(layouts)} layouts): "
@@ -139,7 +153,7 @@ def main():
             for m, r in SLICE_RULES:
                 ws = wl.fgattn(H=H, T=T, Hg=Hg, Wg=Wg, d=d, M=m, cfg=9)
                 ts = time_regimes(bsa, torch, ws, (r,), q, k, v, o, args.reps)
-                best = min(ts, key=ts.get)
+                best = pick(ts)
                 log(f"[lut] slice M={m} L={L}: " + ", ".join(f"{vname(x)} {t:.4f} ms" for x, t in ts.items()) + f" -> {vname(best)}")
                 notes.append(f"slice M={m} L={L}: " + " ".join(f"{vname(x)}={t:.4f}ms" for x, t in ts.items()))
                 slice_rules.append(f"slice   {m:<7d} 1       0          1          0    9999999999 {r} {oname(best[1])}")
