@@ -243,6 +243,9 @@ def time_config(torch, w, P, plan_reps=5, warmup=5, reps=30):
             "pct_bf16_peak": round(100.0 * flops / (med * 1e-3) / 1e12 / MI355X_BF16_PEAK_TFLOPS, 2)}
 
 
+KNOWN_CONFIGS = {"tiny", "svgA", "svgB", "fgattn_M64", "fgattn_M128", "highres"} | {f"tessera{i}" for i in range(48)}
+
+
 def all_configs(torch, oracle, wl, only=None):
     """Every configuration at full size, one JSON line each: tiny, SVG runs A
     and B, FG-Attn slices (M = 64 and 128), the 48 Tessera-style masks (and
@@ -309,6 +312,11 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes 5 times (HBM counter calibration)")
     args = ap.parse_args()
+    if args.configs is not None:
+        unknown = set(args.configs.split(",")) - KNOWN_CONFIGS
+        if unknown or not args.all_configs:
+            ap.error(f"--configs needs --all-configs and names among tiny, svgA, svgB, fgattn_M64, fgattn_M128, "
+                     f"tessera0..tessera47, highres (unknown: {sorted(unknown)})")
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus}, "
