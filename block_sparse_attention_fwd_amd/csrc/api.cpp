@@ -216,6 +216,14 @@ struct bsa_plan_s {
     size_t dev_cap = 0;
     hipEvent_t uploaded = nullptr;
     std::atomic<bool> upload_seen{false};  // `uploaded` has completed (forwards need not wait on it)
+    // Completes after every forward enqueued on this plan so far: bsa_forward
+    // records it after each launch, so that destroying the plan waits for the
+    // kernels that still read its device image before the image goes back to
+    // the recycling pool (where the next plan may upload into it).
+    hipEvent_t last_use = nullptr;
+    hipStream_t last_stream = nullptr;
+    bool used = false;
+    std::mutex use_mu;
     // plans built on the device (bsa_plan_device): the image exists only in
     // device memory until a host query reads back its statistics (and, for
     // the coverage, the task and record sections)
@@ -1073,6 +1081,24 @@ static int32_t organise_tasks(bsa_plan_s &p, const std::vector<HeadOut *> &heads
 // device upload (asynchronous, on the device's upload stream)
 // ---------------------------------------------------------------------------
 
+// The plan's two events: its upload (or device planning) has run; its last
+// enqueued forward has run. On failure neither is left set.
+static hipError_t create_plan_events(bsa_plan_s *p)
+{
+    hipError_t e = hipEventCreateWithFlags(&p->uploaded, hipEventDisableTiming);
+    if (e != hipSuccess) {
+        p->uploaded = nullptr;
+        return e;
+    }
+    e = hipEventCreateWithFlags(&p->last_use, hipEventDisableTiming);
+    if (e != hipSuccess) {
+        p->last_use = nullptr;
+        (void)hipEventDestroy(p->uploaded);
+        p->uploaded = nullptr;
+    }
+    return e;
+}
+
 static int32_t upload(bsa_plan_s &p)
 {
     if (p.device < 0) return BSA_OK;
@@ -1087,8 +1113,7 @@ static int32_t upload(bsa_plan_s &p)
         st = fail(BSA_ERR_HIP, "%s", err.c_str());
     } else if (!(p.dev = rt->pool->acquire(p.img_bytes, &p.dev_cap))) {
         st = fail(BSA_ERR_OUT_OF_MEMORY, "device allocation of %zu bytes failed", p.img_bytes);
-    } else if ((e = hipEventCreateWithFlags(&p.uploaded, hipEventDisableTiming)) != hipSuccess) {
-        p.uploaded = nullptr;
+    } else if ((e = create_plan_events(&p)) != hipSuccess) {
         st = fail(BSA_ERR_HIP, "hipEventCreateWithFlags: %s", hipGetErrorString(e));
     } else if ((e = hipMemcpyAsync(p.dev, p.img, p.img_bytes, hipMemcpyHostToDevice, rt->upload)) != hipSuccess ||
                (e = hipEventRecord(p.uploaded, rt->upload)) != hipSuccess) {
@@ -1101,6 +1126,12 @@ static int32_t upload(bsa_plan_s &p)
 // Give the plan's memory back to the pools (after its upload has completed).
 static void release_plan_memory(bsa_plan_s *p)
 {
+    if (p->last_use) {
+        // the forwards enqueued on this plan have finished reading it
+        if (p->used) (void)hipEventSynchronize(p->last_use);
+        (void)hipEventDestroy(p->last_use);
+        p->last_use = nullptr;
+    }
     if (p->uploaded) {
         (void)hipEventSynchronize(p->uploaded);
         (void)hipEventDestroy(p->uploaded);
@@ -1400,10 +1431,8 @@ extern "C" int32_t bsa_plan_device(const bsa_mask_desc_t *logical_mask, int32_t 
         if (!rt) st = fail(BSA_ERR_HIP, "%s", err.c_str());
         else if (!(p->dev = rt->pool->acquire(p->img_bytes, &p->dev_cap)))
             st = fail(BSA_ERR_OUT_OF_MEMORY, "device allocation of %zu bytes failed", p->img_bytes);
-        else if ((e = hipEventCreateWithFlags(&p->uploaded, hipEventDisableTiming)) != hipSuccess) {
-            p->uploaded = nullptr;
+        else if ((e = create_plan_events(p.get())) != hipSuccess)
             st = fail(BSA_ERR_HIP, "hipEventCreateWithFlags: %s", hipGetErrorString(e));
-        }
         if (st == BSA_OK) {
             uint8_t *dv = (uint8_t *)p->dev;
             const hipStream_t s = (hipStream_t)stream;
@@ -1565,6 +1594,20 @@ extern "C" int32_t bsa_forward(bsa_plan_t p, const void *Q, const void *K, const
         const Regime &R = kRegimes[p->regime];
         e = p->dtype == BSA_DTYPE_F32 ? launch_forward_f32(a, R.tile_q / 32, p->d, (hipStream_t)stream)
                                       : launch_forward(a, R.waves, R.rb, p->d, p->dtype, (hipStream_t)stream);
+    }
+    if (e == hipSuccess) {
+        // last_use completes after this forward and after every earlier one:
+        // a forward on another stream than the previous one first makes the
+        // record wait for the previous record (later work on this stream then
+        // also waits for the other stream's forward of this plan)
+        std::lock_guard<std::mutex> g(p->use_mu);
+        const hipStream_t s = (hipStream_t)stream;
+        if (p->used && s != p->last_stream) e = hipStreamWaitEvent(s, p->last_use, 0);
+        if (e == hipSuccess) e = hipEventRecord(p->last_use, s);
+        if (e == hipSuccess) {
+            p->used = true;
+            p->last_stream = s;
+        }
     }
     if (cur != p->device) (void)hipSetDevice(cur);
     if (e != hipSuccess) return fail(BSA_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));

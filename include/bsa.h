@@ -191,9 +191,10 @@ int32_t bsa_abi_version(void);
 
 /*
  * Build a plan for `logical_mask` over B x H heads of L tokens, head dim d
- * (64 or 128), logical block shape block_q x block_k (BLOCK kinds: powers of
- * two in [16, 512]; SLICE: block_q = M in {32, 64, 128}, block_k = 1; VIDEO:
- * 1 x 1). opts may be NULL (defaults). On success *out_plan receives a new
+ * (64 or 128), logical block shape block_q x block_k (BLOCK kinds: each side a
+ * power of two in [32, 1024], else UNSUPPORTED; SLICE: block_q = M in {64, 128}
+ * (other M: UNSUPPORTED), block_k = 1; VIDEO: 1 x 1). opts may be NULL
+ * (defaults). On success *out_plan receives a new
  * plan; on failure it is set to NULL and nothing is leaked.
  * Errors: INVALID_ARGUMENT (null pointers, shapes, options, geometry),
  * INVALID_MASK (contents), UNSUPPORTED (d, block shape, dtype), OUT_OF_MEMORY,
@@ -237,7 +238,11 @@ int32_t bsa_plan_device(const bsa_mask_desc_t *logical_mask, int32_t B, int32_t 
 /*
  * Enqueue the forward pass of `plan` on `stream` (a hipStream_t; NULL = the
  * default stream of the plan's device). Q, K, V, O as described above. Never
- * synchronises and never allocates; returns after the launch. Launch errors
+ * synchronises and never allocates; returns after the launch. After the
+ * launch it records the plan's last-use event on `stream`; a forward on a
+ * different stream than the plan's previous forward first makes `stream` wait
+ * for that previous forward (so later work on `stream` waits for it too).
+ * Launch errors
  * are reported (BSA_ERR_HIP); faults inside the kernel surface at the
  * caller's next synchronisation of the stream.
  * Errors: INVALID_ARGUMENT (null plan or pointer, misaligned pointer, host-only
@@ -245,7 +250,10 @@ int32_t bsa_plan_device(const bsa_mask_desc_t *logical_mask, int32_t B, int32_t 
  */
 int32_t bsa_forward(bsa_plan_t plan, const void *Q, const void *K, const void *V, void *O, void *stream);
 
-/* Free a plan (NULL is allowed). The caller guarantees no pending forward. */
+/* Free a plan (NULL is allowed). Blocks until every forward enqueued on the
+ * plan has finished (its last-use event), so that no running kernel still
+ * reads the plan's device memory when it is handed to the next plan; a plan
+ * may therefore be destroyed right after an asynchronous forward. */
 void bsa_plan_destroy(bsa_plan_t plan);
 
 /* Statistics of a plan. Errors: INVALID_ARGUMENT. */

@@ -16,7 +16,10 @@ the definition's invariants (masked key == deleted key, block mask == its
 element expansion, key/value permutation invariance, token-permutation
 equivariance of temporal-major heads), closed forms (one kept key, constant V,
 empty row, score shift, query/key rescale) and closed-form pair counts of the
-video patterns. No function of this oracle is "parity unpinned".
+video patterns, and the per-block key unions (``om_block_union``,
+``om_union_total``) against an independent element-mask union and the
+geometry's hand-computed totals. No function of this oracle is "parity
+unpinned".
 """
 from __future__ import annotations
 
@@ -71,6 +74,8 @@ def lib(path: str = _LIB):
                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
     L.om_count_pairs.restype = ctypes.c_int64
     L.om_count_pairs.argtypes = [ctypes.POINTER(OmMask), ctypes.c_int32, ctypes.c_int32]
+    L.om_union_total.restype = ctypes.c_int64
+    L.om_union_total.argtypes = [ctypes.POINTER(OmMask), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
     L.om_block_union.restype = None
     L.om_block_union.argtypes = [ctypes.POINTER(OmMask), ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
                                  ctypes.c_void_p]
@@ -164,6 +169,45 @@ def block_union(w, b, h, blk, M=64, lib_path: str = _LIB):
     used = np.zeros(w.L, np.uint8)
     L_.om_block_union(ctypes.byref(mk.m), b, h, blk, M, _ptr(used))
     return used
+
+
+def union_total(w, b=0, h=0, M=64, lib_path: str = _LIB) -> int:
+    """Sum over the M-row query blocks of head (b, h), in the head's logical
+    order, of the number of distinct keys kept by any query of the block
+    (FG-Attn, abstract: the keys relevant to a block of queries)."""
+    L_ = lib(lib_path)
+    mk = Mask(w)
+    return int(L_.om_union_total(ctypes.byref(mk.m), b, h, M))
+
+
+def gather_bytes(w, M=64, lib_path: str = _LIB) -> int:
+    """Mask-defined gather bytes G of a workload: per head, every M-row query
+    block loads each distinct key it keeps once as a K row and a V row, and the
+    head's Q is read and O written once (d-wide rows of the input dtype; bf16
+    here, 2 bytes). Heads with identical masks are counted once each."""
+    row = 2 * w.d
+    per = {}
+    total = 0
+    for b in range(w.B):
+        for h in range(w.H):
+            key = _head_key(w, b, h)
+            if key is None or key not in per:
+                u = union_total(w, b, h, M, lib_path=lib_path)
+                if key is not None:
+                    per[key] = u
+            else:
+                u = per[key]
+            total += 2 * row * u + 2 * row * w.L
+    return total
+
+
+def _head_key(w, b, h):
+    """A key that two heads share only when their masks are identical (video
+    heads of one pattern and layout); None when heads must be counted alone."""
+    if w.kind == 4:
+        lay = int(w.head_layout[h]) if w.head_layout is not None else 0
+        return (int(w.head_pattern[h]), lay)
+    return None
 
 
 def route_heads(Q, K, V, T: int, Hg: int, Wg: int, rows, anchor: int = 0, radius: int = 2, lib_path: str = _LIB):

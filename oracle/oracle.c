@@ -232,3 +232,59 @@ void om_block_union(const om_mask_t *m, int32_t b, int32_t h, int64_t blk, int32
     }
     free(keys);
 }
+
+/*
+ * Sum over the M-row query blocks of head (b,h), taken in the head's logical
+ * order (block beta = logical positions [beta*M, min((beta+1)*M, L))), of
+ * |K_beta|: the number of distinct keys kept by at least one query of beta.
+ * FG-Attn (arXiv 2509.16518), abstract: a block of queries needs only the keys
+ * relevant to it; |K_beta| is the count of key (and value) rows such a block
+ * must load at least once, the basis of the mask-defined gather bytes.
+ *
+ * BLOCK masks are taken at block granularity: the rows of beta fall in the
+ * logical query blocks i = floor(j / bq), and a key is kept by some row of
+ * beta exactly when its key block is kept by one of those i, so |K_beta| is
+ * the summed (cropped) size of the key blocks kept by any such i. SLICE and
+ * VIDEO masks take the union of the rows' own key lists (om_block_union).
+ */
+int64_t om_union_total(const om_mask_t *m, int32_t b, int32_t h, int32_t M)
+{
+    const int64_t nbeta = nblocks(m->L, M);
+    int64_t total = 0;
+    if (m->kind == OM_BLOCK || m->kind == OM_BLOCK_BITS) {
+        const int64_t nqb = nblocks(m->L, m->bq), nkb = nblocks(m->L, m->bk);
+        const int64_t words = (nkb + 63) / 64;
+        const int64_t bh = (int64_t)b * m->H + h;
+#pragma omp parallel reduction(+ : total)
+        {
+            uint8_t *any = (uint8_t *)malloc((size_t)nkb);
+#pragma omp for schedule(dynamic, 4)
+            for (int64_t beta = 0; beta < nbeta; ++beta) {
+                const int64_t j0 = beta * M, j1 = (beta + 1) * M < m->L ? (beta + 1) * M : m->L;
+                memset(any, 0, (size_t)nkb);
+                for (int64_t i = j0 / m->bq; i <= (j1 - 1) / m->bq; ++i)
+                    for (int64_t kb = 0; kb < nkb; ++kb) {
+                        const int on = m->kind == OM_BLOCK
+                                           ? m->block_u8[(bh * nqb + i) * nkb + kb] != 0
+                                           : (int)((m->block_bits[(bh * nqb + i) * words + kb / 64] >> (kb % 64)) & 1u);
+                        if (on) any[kb] = 1;
+                    }
+                for (int64_t kb = 0; kb < nkb; ++kb)
+                    if (any[kb]) total += (kb + 1) * m->bk < m->L ? m->bk : m->L - kb * m->bk;
+            }
+            free(any);
+        }
+        return total;
+    }
+#pragma omp parallel reduction(+ : total)
+    {
+        uint8_t *used = (uint8_t *)malloc((size_t)m->L);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t beta = 0; beta < nbeta; ++beta) {
+            om_block_union(m, b, h, beta, M, used);
+            for (int64_t k = 0; k < m->L; ++k) total += used[k];
+        }
+        free(used);
+    }
+    return total;
+}

@@ -20,6 +20,12 @@ def plan_workload(w, device=0, force_regime=-1, bits=False, lut_path=None, dtype
     raise ValueError(w.kind)
 
 
+def to_device_bf16(x_u16: np.ndarray, device: str = "cuda:0"):
+    """bf16 bit patterns (uint16 numpy) -> a bfloat16 torch tensor on ``device``."""
+    import torch
+    return torch.from_numpy(x_u16.view(np.int16)).view(torch.bfloat16).to(device)
+
+
 def tok_of_logical(T, HW):
     return np.arange(T * HW).reshape(T, HW).T.reshape(-1)
 

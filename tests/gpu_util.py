@@ -8,7 +8,7 @@ import torch
 import block_sparse_attention_fwd_amd as bsa
 import oracle
 import workloads as wl
-from bsa_helpers import plan_workload
+from bsa_helpers import plan_workload, to_device_bf16
 
 MAX_ABS = 1e-2   # bf16 inputs: max-abs error against the fp64 oracle
 MEAN_ABS = 1e-3  # bf16 inputs: mean-abs error against the fp64 oracle
@@ -18,10 +18,6 @@ ROW_REL_F32 = 1e-5  # fp32 inputs: max over rows of |O - O_ref|_inf / |O_ref|_in
 def log(*a):
     print(*a, flush=True)
     sys.stdout.flush()
-
-
-def to_device_bf16(x_u16: np.ndarray) -> torch.Tensor:
-    return torch.from_numpy(x_u16.view(np.int16)).view(torch.bfloat16).to("cuda:0")
 
 
 def to_device(x: np.ndarray) -> torch.Tensor:

@@ -395,6 +395,49 @@ def pin_counts(lib_path):
     return fails
 
 
+def brute_union_total(w, b, h, M):
+    """Sum over the M-row blocks of head (b, h)'s logical positions of the
+    number of distinct keys kept by any row of the block, from the independent
+    element-level mask (frame-major tokens), and the per-block key sets."""
+    em = element_mask(w, b, h)
+    if w.layout()[h] == wl.TEMPORAL_MAJOR:
+        order = tok_of_logical(w.T, w.Hg * w.Wg)  # token at each logical position
+    else:
+        order = np.arange(w.L)
+    sets = []
+    for j0 in range(0, w.L, M):
+        rows = order[j0:j0 + M]
+        sets.append(em[rows].any(axis=0))
+    return int(sum(int(u.sum()) for u in sets)), sets
+
+
+def pin_block_union(lib_path):
+    """Per-block key unions (om_block_union) and their totals (om_union_total)
+    == the union of the independent element mask's rows, every kind, both
+    layouts, blocks smaller than, equal to and spanning several logical query
+    blocks; BLOCK_BITS == BLOCK_U8."""
+    fails = []
+    for w in tiny_cases(11):
+        for h in range(w.H):
+            for M in (3, 4, 8, 16, 64):
+                want, sets = brute_union_total(w, 0, h, M)
+                got = oracle.union_total(w, 0, h, M, lib_path=lib_path)
+                if got != want:
+                    fails.append(f"union total {w.name} h{h} M{M}: {got} vs {want}")
+                for beta, u in enumerate(sets):
+                    used = oracle.block_union(w, 0, h, beta, M, lib_path=lib_path).astype(bool)
+                    if not np.array_equal(used, u):
+                        fails.append(f"block union {w.name} h{h} M{M} block {beta}")
+                        break
+                if w.kind == wl.BLOCK:
+                    L_ = oracle.lib(lib_path)
+                    mk = oracle.Mask(w, bits=True)
+                    gb = int(L_.om_union_total(oracle.ctypes.byref(mk.m), 0, h, M))
+                    if gb != want:
+                        fails.append(f"union total bits {w.name} h{h} M{M}: {gb} vs {want}")
+    return fails
+
+
 ALL_PINS = [pin_bruteforce, pin_library_sdpa, pin_masked_equals_deleted, pin_block_equals_expansion,
             pin_kv_permutation, pin_tm_equivariance, pin_video_layout_invariance, pin_closed_forms, pin_golden,
-            pin_counts]
+            pin_counts, pin_block_union]

@@ -240,3 +240,26 @@ def test_task_orders(order):
             (h, q0), (h2, q2) = pos[s], pos[s + 8]
             same += h2 == h and q2 > q0
     assert pairs > 0.9 * n and same > 0.95 * pairs, (pairs, same, n)
+
+
+def test_block_shape_range_ends():
+    """The documented ranges, at both ends: BLOCK sides are powers of two in
+    [32, 1024]; SLICE takes M = 64 or 128 (host-only plans)."""
+    P = bsa.plan
+    L = 2048
+    for bq, bk in ((32, 32), (1024, 1024), (32, 1024), (1024, 32)):
+        m = np.ones((1, 1, -(-L // bq), -(-L // bk)), np.uint8)
+        p = P(bsa.MASK_BLOCK_U8, 1, 1, L, 64, bq, bk, data=m, device=-1)
+        assert p.info()["executed_pairs"] == L * L
+        p.close()
+    for bq, bk in ((16, 64), (64, 16), (2048, 64), (64, 2048)):
+        m = np.ones((1, 1, -(-L // bq), -(-L // bk)), np.uint8)
+        expect(bsa.ERR_UNSUPPORTED, P, bsa.MASK_BLOCK_U8, 1, 1, L, 64, bq, bk, data=m, device=-1, match="block shape")
+    for M in (64, 128):
+        nq = -(-L // M)
+        rp = np.arange(nq + 1, dtype=np.int64)
+        ci = np.zeros(nq, np.int32)
+        P(bsa.MASK_SLICE_CSR, 1, 1, L, 64, M, 1, row_ptr=rp, col_idx=ci, device=-1).close()
+    nq = -(-L // 32)
+    expect(bsa.ERR_UNSUPPORTED, P, bsa.MASK_SLICE_CSR, 1, 1, L, 64, 32, 1, row_ptr=np.arange(nq + 1, dtype=np.int64),
+           col_idx=np.zeros(nq, np.int32), device=-1, match="slice block")

@@ -42,6 +42,14 @@ MUTANTS = [
      "uint32_t bits = (uint32_t)((const uint16_t *)p)[idx];"),
     ("count_no_crop", "if (on) total += rq * ((j + 1) * m->bk < m->L ? m->bk : m->L - j * m->bk);",
      "if (on) total += rq * m->bk;"),
+    ("union_last_logical_block", "for (int64_t i = j0 / m->bq; i <= (j1 - 1) / m->bq; ++i)",
+     "for (int64_t i = j0 / m->bq; i < (j1 - 1) / m->bq; ++i)"),
+    ("union_no_crop", "if (any[kb]) total += (kb + 1) * m->bk < m->L ? m->bk : m->L - kb * m->bk;",
+     "if (any[kb]) total += m->bk;"),
+    ("union_rows_not_mapped", "int64_t n = om_row_keys(m, b, h, token_of(m, h, j), keys);",
+     "int64_t n = om_row_keys(m, b, h, j, keys);"),
+    ("union_block_end", "int64_t hi = (blk + 1) * M < m->L ? (blk + 1) * M : m->L;",
+     "int64_t hi = (blk + 1) * M - 1 < m->L ? (blk + 1) * M - 1 : m->L;"),
 ]
 
 
