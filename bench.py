@@ -298,6 +298,8 @@ def main():
     ap.add_argument("--configs", default=None,
                     help="with --all-configs: comma list of configuration names to run (tiny, svgA, svgB, "
                          "fgattn_M64, fgattn_M128, tessera0..tessera47, highres)")
+    ap.add_argument("--units", action="store_true",
+                    help="instead of the headline, run the unit microbenchmarks (MFMA, vector, LDS, HBM rates)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes 5 times (HBM counter calibration)")
     args = ap.parse_args()
@@ -329,6 +331,10 @@ def main():
         return
     if args.all_configs:
         all_configs(torch, wl, None if args.configs is None else set(args.configs.split(",")))
+        return
+    if args.units:
+        for rec in unit_benchmarks():
+            print(json.dumps(rec), flush=True)
         return
 
     from bsa_helpers import to_device_bf16
@@ -435,6 +441,73 @@ def main():
         log("[bench] timing the oracle on a row sample")
         out["cpu_baseline"] = cpu_baseline(w, Q, K, V, P, args.cpu_rows_per_head)
     print(json.dumps(out), flush=True)
+
+
+# ---------------------------------------------------------------------------
+# unit microbenchmarks (--units)
+# ---------------------------------------------------------------------------
+
+UNITS_LIB = os.path.join(ROOT, "block_sparse_attention_fwd_amd", "libbsa_units.so")
+MFMA_FLOP = 2 * 32 * 32 * 16  # one v_mfma_f32_32x32x16_bf16
+
+
+def unit_benchmarks():
+    """The device rates the forward kernel's roofline fractions rest on,
+    measured with the kernels of csrc/units.hip: MFMA throughput (alone and
+    with exponentials or FMAs issued beside it, in the same wave or by a
+    second wave of the SIMD), vector-unit and LDS read rates, HBM streaming
+    rates. Yields one record per measurement."""
+    import ctypes
+    if not os.path.exists(UNITS_LIB):
+        raise SystemExit(f"{UNITS_LIB} is missing: build it first (__graft_entry__.build())")
+    L = ctypes.CDLL(UNITS_LIB)
+    L.bsa_units_run.restype = ctypes.c_int
+    L.bsa_units_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
+    ncu = 256
+
+    def run(which, param, iters, blocks):
+        out = (ctypes.c_double * 3)()
+        rc = L.bsa_units_run(which, param, iters, blocks, out)
+        if rc != 0:
+            raise RuntimeError(f"bsa_units_run({which}, {param}) failed: hipError {rc}")
+        ms, ticks, rt = out[0], out[1], out[2]
+        ghz = ticks / (rt / 100e6) / 1e9 if rt > 0 else float("nan")
+        return ms, ticks, ghz
+
+    iters = 20000
+    base = None
+    for which, name in ((0, "mfma"), (1, "mfma+exp same wave"), (2, "mfma+fma same wave"),
+                        (3, "mfma wave + exp wave per SIMD")):
+        for ne in ((0,) if which == 0 else (1, 2, 3, 4)):
+            ms, ticks, ghz = run(which, ne, iters, ncu)
+            mfma_waves = 4 if which == 3 else 8
+            flops = ncu * mfma_waves * iters * 4 * MFMA_FLOP
+            # one block per CU: two MFMA-issuing waves per SIMD (one for mode 3)
+            per_simd = 2 if which != 3 else 1
+            clk_per_mfma = ticks / (iters * 4 * per_simd)
+            rec = {"unit": name, "per_mfma": ne, "ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                   "clock_ghz": round(ghz, 3), "clk_per_mfma_per_simd": round(clk_per_mfma, 2)}
+            if which == 0:
+                base = clk_per_mfma
+            else:
+                rec["vs_mfma_alone"] = round(clk_per_mfma / base, 3)
+            yield rec
+    for which, name in ((10, "v_exp_f32"), (11, "v_fma_f32")):
+        ms, ticks, ghz = run(which, 0, iters, ncu)
+        yield {"unit": name, "ms": round(ms, 4), "clock_ghz": round(ghz, 3),
+               "clk_per_wave_instruction": round(ticks / (iters * 16), 2), "note": "one wave per SIMD"}
+    for which, name, nbytes in ((20, "ds_read_b128", 1024), (21, "ds_read_b64_tr_b16", 512)):
+        it = 4000
+        ms, ticks, ghz = run(which, 0, it, ncu)
+        per_cu = 8 * it * 8 * nbytes  # 8 waves x iters x 8 reads x bytes per wave read
+        yield {"unit": name, "ms": round(ms, 4), "clock_ghz": round(ghz, 3),
+               "bytes_per_clk_per_cu": round(per_cu / ticks, 1), "tb_per_s_chip": round(ncu * per_cu / (ms * 1e-3) / 1e12, 2)}
+    for which, name in ((30, "hbm read"), (31, "hbm copy")):
+        mib = 2048
+        ms, ticks, ghz = run(which, mib, 0, ncu * 8)
+        moved = mib * (1 << 20) * (2 if which == 31 else 1)
+        yield {"unit": name, "bytes": moved, "ms": round(ms, 4), "gb_per_s": round(moved / (ms * 1e-3) / 1e9, 1),
+               "frac_of_8tbs": round(moved / (ms * 1e-3) / 1e9 / MI355X_HBM_PEAK_GBS, 3)}
 
 
 # ---------------------------------------------------------------------------

@@ -7,6 +7,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libbsa.so")
+UNITS_LIB = os.path.join(HERE, "libbsa_units.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -42,6 +43,13 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp, "-lpthread"], check=True)
     os.replace(tmp, LIB)
+    # unit microbenchmarks (bench.py --units): a library of their own
+    src = os.path.join(CSRC, "units.hip")
+    cmd = [HIPCC, "-x", "hip", *common, *DEVICE_FLAGS, "-shared", src, "-o", UNITS_LIB + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), file=sys.stderr)
+    subprocess.run(cmd, check=True)
+    os.replace(UNITS_LIB + ".tmp", UNITS_LIB)
     return LIB
 
 
