@@ -36,6 +36,7 @@
 #include <string>
 #include <thread>
 
+#include <emmintrin.h>  // SSE2 (x86-64 baseline): byte masks to keep bits
 #include <sched.h>
 #include <vector>
 
@@ -125,13 +126,16 @@ extern "C" int32_t bsa_regime_info(int32_t r, bsa_regime_desc_t *out)
 }
 
 // Lookup-table rule: first matching line wins. Fields:
-//   kind block_q block_k density_lo density_hi L_lo L_hi regime [order]
+//   kind block_q block_k density_lo density_hi fill_lo fill_hi L_lo L_hi regime [order]
 // kind is block|slice|video; block sizes may be '*'; order is xcd (the
-// default) or lpt (BSA_ORDER_*).
+// default) or lpt (BSA_ORDER_*). density and fill are the mask features of
+// mask_features() (-1 where a kind has none; such a feature matches any
+// range).
 struct LutRule {
     int kind;  // BSA_MASK_BLOCK_U8 (both block kinds), SLICE, VIDEO
     int bq, bk;  // 0 = any
     double dlo, dhi;
+    double flo, fhi;
     int64_t Llo, Lhi;
     int regime;
     int order;
@@ -152,7 +156,7 @@ static bool parse_lut(const std::string &text, std::vector<LutRule> &rules, std:
         std::string kind, bq, bk;
         LutRule r{};
         if (!(ls >> kind)) continue;
-        if (!(ls >> bq >> bk >> r.dlo >> r.dhi >> r.Llo >> r.Lhi >> r.regime)) {
+        if (!(ls >> bq >> bk >> r.dlo >> r.dhi >> r.flo >> r.fhi >> r.Llo >> r.Lhi >> r.regime)) {
             err = "lookup table line " + std::to_string(ln) + " malformed";
             return false;
         }
@@ -196,6 +200,7 @@ struct bsa_plan_s {
     int32_t bq_shift = 0, bk_shift = 0, nsk = 1, sub_q = 0, sub_k = 0;
     int32_t mode = 0;
     int32_t task_order = BSA_ORDER_XCD_GROUPED;
+    double mask_density = -1.0, mask_fill = -1.0;  // regime-lookup features (-1: none for the kind)
     std::vector<uint8_t> head_layout, head_pattern;
     // image
     uint8_t *img = nullptr;
@@ -483,60 +488,96 @@ void parallel_for(int64_t n, F &&f)
 // physical mapping per head
 // ---------------------------------------------------------------------------
 
+// Keep bits of one BLOCK_U8 row (nkb bytes, nonzero = kept) as 64-bit words,
+// bit j of word w = block 64 w + j; 16 bytes per SSE2 compare.
+static void u8_row_bits(const uint8_t *row, int64_t nkb, uint64_t *out)
+{
+    const int64_t words = (nkb + 63) / 64;
+    const __m128i zero = _mm_setzero_si128();
+    for (int64_t w = 0; w < words; ++w) {
+        const int64_t base = w * 64, n = std::min<int64_t>(64, nkb - base);
+        uint64_t x = 0;
+        if (n == 64) {
+            for (int c = 0; c < 4; ++c) {
+                const __m128i v = _mm_loadu_si128((const __m128i *)(row + base + 16 * c));
+                const unsigned z = (unsigned)_mm_movemask_epi8(_mm_cmpeq_epi8(v, zero));
+                x |= (uint64_t)(~z & 0xFFFFu) << (16 * c);
+            }
+        } else {
+            for (int64_t j = 0; j < n; ++j) x |= (uint64_t)(row[base + j] != 0) << j;
+        }
+        out[w] = x;
+    }
+}
+
+// Keep-bit row qb of head bh: BLOCK_BITS rows directly, BLOCK_U8 rows
+// converted into `buf` (words entries).
+static const uint64_t *block_row_bits(const bsa_mask_desc_t &m, int64_t bh, int64_t qb, int64_t nqb, int64_t nkb,
+                                      uint64_t *buf)
+{
+    const int64_t words = (nkb + 63) / 64;
+    if (m.kind == BSA_MASK_BLOCK_BITS) return (const uint64_t *)m.data + (bh * nqb + qb) * words;
+    u8_row_bits((const uint8_t *)m.data + (bh * nqb + qb) * nkb, nkb, buf);
+    return buf;
+}
+
 // BLOCK masks: retain (bq = tile_q, bk = tile_k), combine (smaller logical
 // blocks merged into one tile, kept sub-blocks recorded as bits) or subdivide
-// (larger logical blocks split over several tiles).
+// (larger logical blocks split over several tiles). Each logical row is read
+// as keep-bit words and only its kept blocks are visited (ctz); a bitset of
+// the key tiles the query tile touches yields the records in key order, so
+// the work per query tile follows the kept blocks, not the row length.
 static void map_block_head(const bsa_plan_s &p, const bsa_mask_desc_t &m, int b, int h, int BQ, int64_t tq_lo,
                            int64_t tq_hi, HeadOut &out)
 {
     const int64_t L = p.L;
     const int64_t nqb = (L + p.block_q - 1) / p.block_q, nkb = (L + p.block_k - 1) / p.block_k;
-    const int64_t nqt = (L + BQ - 1) / BQ, nkt = (L + kTileK - 1) / kTileK;
+    const int64_t nkt = (L + kTileK - 1) / kTileK;
     const int bqe = std::min(p.block_q, BQ), bke = std::min(p.block_k, kTileK);
     const int nsq = BQ / bqe, nsk = kTileK / bke;
     const int64_t bh = (int64_t)b * p.H + h;
-    const int64_t words = (nkb + 63) / 64;
-    const uint8_t *u8 = m.kind == BSA_MASK_BLOCK_U8 ? (const uint8_t *)m.data + bh * nqb * nkb : nullptr;
-    const uint64_t *bits = m.kind == BSA_MASK_BLOCK_BITS ? (const uint64_t *)m.data + bh * nqb * words : nullptr;
-    std::vector<uint32_t> acc(nkt, 0);
-    (void)nqt;
+    const int64_t words = (nkb + 63) / 64, twords = (nkt + 63) / 64;
+    std::vector<uint64_t> rowbuf((size_t)words);
+    std::vector<uint32_t> acc((size_t)nkt, 0u);
+    std::vector<uint64_t> touched((size_t)twords, 0u);
     out.tasks.reserve((size_t)(tq_hi - tq_lo));
     for (int64_t tq = tq_lo; tq < tq_hi; ++tq) {
         const int64_t q0 = tq * BQ, q1 = std::min<int64_t>(q0 + BQ, L);
         const int64_t qb0 = q0 / p.block_q, qb1 = (q1 - 1) / p.block_q;
-        std::fill(acc.begin(), acc.end(), 0u);
         for (int64_t qb = qb0; qb <= qb1; ++qb) {
-            const int sq = (int)((qb * p.block_q - q0) / bqe) < 0 ? 0 : (int)((qb * p.block_q - q0) / bqe);
-            auto mark = [&](int64_t kb) {
-                const int64_t k_lo = kb * p.block_k, k_hi = std::min<int64_t>(k_lo + p.block_k, L) - 1;
-                for (int64_t tk = k_lo / kTileK; tk <= k_hi / kTileK; ++tk) {
-                    int sk = p.block_k <= kTileK ? (int)((k_lo - tk * kTileK) / bke) : 0;
-                    acc[tk] |= 1u << (sq * nsk + sk);
+            const int sq = qb * p.block_q <= q0 ? 0 : (int)((qb * p.block_q - q0) / bqe);
+            const uint64_t *row = block_row_bits(m, bh, qb, nqb, nkb, rowbuf.data());
+            for (int64_t w = 0; w < words; ++w)
+                for (uint64_t x = row[w]; x; x &= x - 1) {
+                    const int64_t kb = w * 64 + __builtin_ctzll(x);
+                    const int64_t k_lo = kb * p.block_k, k_hi = std::min<int64_t>(k_lo + p.block_k, L) - 1;
+                    for (int64_t tk = k_lo / kTileK; tk <= k_hi / kTileK; ++tk) {
+                        const int sk = p.block_k <= kTileK ? (int)((k_lo - tk * kTileK) / bke) : 0;
+                        acc[tk] |= 1u << (sq * nsk + sk);
+                        touched[tk >> 6] |= 1ull << (tk & 63);
+                    }
                 }
-            };
-            if (u8) {
-                const uint8_t *row = u8 + qb * nkb;
-                for (int64_t kb = 0; kb < nkb; ++kb)
-                    if (row[kb]) mark(kb);
-            } else {
-                const uint64_t *row = bits + qb * words;
-                for (int64_t w = 0; w < words; ++w)
-                    for (uint64_t x = row[w]; x; x &= x - 1) mark(w * 64 + __builtin_ctzll(x));
-            }
         }
         const int nsq_valid = (int)std::min<int64_t>(nsq, (q1 - 1 - q0) / bqe + 1);
         Task t{(int32_t)bh, (int32_t)q0, (int32_t)out.tiles.size(), 0};
-        for (int64_t tk = 0; tk < nkt; ++tk) {
-            if (!acc[tk]) { ++out.empty; continue; }
-            const int64_t k0 = tk * kTileK, k1 = std::min<int64_t>(k0 + kTileK, L);
-            const int nsk_valid = (int)std::min<int64_t>(nsk, (k1 - 1 - k0) / bke + 1);
-            uint32_t want = 0;
-            for (int sq = 0; sq < nsq_valid; ++sq)
-                for (int sk = 0; sk < nsk_valid; ++sk) want |= 1u << (sq * nsk + sk);
-            const bool full = (acc[tk] & want) == want && k0 + kTileK <= L;
-            out.tiles.push_back({(int32_t)k0, acc[tk] | (full ? 0u : kPartial)});
-            if (full) ++out.full; else ++out.part;
+        int64_t n_tiles = 0;
+        for (int64_t tw = 0; tw < twords; ++tw) {
+            for (uint64_t x = touched[tw]; x; x &= x - 1) {
+                const int64_t tk = tw * 64 + __builtin_ctzll(x);
+                const int64_t k0 = tk * kTileK, k1 = std::min<int64_t>(k0 + kTileK, L);
+                const int nsk_valid = (int)std::min<int64_t>(nsk, (k1 - 1 - k0) / bke + 1);
+                uint32_t want = 0;
+                for (int sq = 0; sq < nsq_valid; ++sq)
+                    for (int sk = 0; sk < nsk_valid; ++sk) want |= 1u << (sq * nsk + sk);
+                const bool full = (acc[tk] & want) == want && k0 + kTileK <= L;
+                out.tiles.push_back({(int32_t)k0, acc[tk] | (full ? 0u : kPartial)});
+                if (full) ++out.full; else ++out.part;
+                acc[tk] = 0u;
+                ++n_tiles;
+            }
+            touched[tw] = 0u;
         }
+        out.empty += nkt - n_tiles;
         t.te = (int32_t)out.tiles.size();
         out.tasks.push_back(t);
     }
@@ -757,39 +798,94 @@ static int32_t validate(const bsa_mask_desc_t *m, int32_t B, int32_t H, int64_t 
 // regime selection
 // ---------------------------------------------------------------------------
 
-static double mask_density(const bsa_mask_desc_t &m, int32_t B, int32_t H, int64_t L, int32_t bq, int32_t bk)
+// Mask features for the regime lookup (Tessera, arXiv 2609.25869, abstract:
+// the physical tiles that suit a mask depend on its shape, and the regime is
+// looked up from offline profiling at low cost):
+//  - density: kept logical blocks over all blocks (slices: listed keys over
+//    all (query block, key) pairs);
+//  - fill: kept pairs over the pairs of the non-empty 128 x 64 physical tiles
+//    (regime 0's tiling), i.e. the share of computed pairs that are kept.
+//    Banded and windowed layouts fill their tiles (near 1); a random layout
+//    of blocks smaller than the tile leaves most of each non-empty tile
+//    masked (about density / (1 - (1 - density)^k) for k blocks per tile),
+//    where 64-row tiles waste less.
+// BLOCK features come from a fixed sample: every kFeatureStride-th 128-row
+// query tile of every head (all of them when a head has fewer tiles), read
+// as keep-bit words, so the cost is a fraction of one mapping pass and the
+// result is a deterministic function of the mask.
+struct MaskFeatures {
+    double density = -1.0;
+    double fill = -1.0;
+};
+constexpr int64_t kFeatureStride = 4;
+
+static MaskFeatures mask_features(const bsa_mask_desc_t &m, int32_t B, int32_t H, int64_t L, int32_t bq, int32_t bk)
 {
+    MaskFeatures f;
     if (m.kind == BSA_MASK_SLICE_CSR) {
         const int64_t nl = (int64_t)B * H * ((L + bq - 1) / bq);
-        return (double)(m.nnz ? m.nnz : m.row_ptr[nl]) / ((double)nl * (double)L);
+        f.density = (double)(m.nnz ? m.nnz : m.row_ptr[nl]) / ((double)nl * (double)L);
+        return f;
     }
-    if (m.kind == BSA_MASK_VIDEO) return -1.0;
+    if (m.kind == BSA_MASK_VIDEO) return f;
     const int64_t nqb = (L + bq - 1) / bq, nkb = (L + bk - 1) / bk;
-    const int64_t rows = (int64_t)B * H * nqb;
-    std::vector<int64_t> cnt(rows, 0);
-    if (m.kind == BSA_MASK_BLOCK_U8) {
-        const uint8_t *u = (const uint8_t *)m.data;
-        parallel_for(rows, [&](int64_t r) {
-            int64_t c = 0;
-            for (int64_t j = 0; j < nkb; ++j) c += u[r * nkb + j] != 0;
-            cnt[r] = c;
-        });
-    } else {
-        const int64_t words = (nkb + 63) / 64;
-        const uint64_t *w = (const uint64_t *)m.data;
-        parallel_for(rows, [&](int64_t r) {
-            int64_t c = 0;
-            for (int64_t j = 0; j < words; ++j) c += __builtin_popcountll(w[r * words + j]);
-            cnt[r] = c;
-        });
+    const int64_t nqt = (L + 127) / 128, nkt = (L + kTileK - 1) / kTileK;
+    const int64_t words = (nkb + 63) / 64, twords = (nkt + 63) / 64;
+    const int64_t stride = nqt >= 4 * kFeatureStride ? kFeatureStride : 1;
+    const int64_t heads = (int64_t)B * H;
+    const int64_t last_w = L - (nkb - 1) * bk;  // width of the (cropped) last key block
+    struct Acc {
+        int64_t blocks = 0, kept = 0;
+        double kept_pairs = 0.0, exec_pairs = 0.0;
+    };
+    std::vector<Acc> acc((size_t)heads);
+    parallel_for(heads, [&](int64_t bh) {
+        std::vector<uint64_t> rowbuf((size_t)words), uni((size_t)words), tiles((size_t)twords);
+        Acc a;
+        for (int64_t tq = 0; tq < nqt; tq += stride) {
+            const int64_t q0 = tq * 128, q1 = std::min<int64_t>(q0 + 128, L);
+            std::fill(uni.begin(), uni.end(), 0ull);
+            for (int64_t qb = q0 / bq; qb <= (q1 - 1) / bq; ++qb) {
+                const uint64_t *row = block_row_bits(m, bh, qb, nqb, nkb, rowbuf.data());
+                int64_t k = 0;
+                for (int64_t w = 0; w < words; ++w) {
+                    k += __builtin_popcountll(row[w]);
+                    uni[w] |= row[w];
+                }
+                const bool last = (row[words - 1] >> ((nkb - 1) & 63)) & 1;
+                const int64_t r_in = std::min<int64_t>(q1, (qb + 1) * bq) - std::max<int64_t>(q0, qb * bq);
+                a.kept_pairs += (double)r_in * (double)(k * bk - (last ? bk - last_w : 0));
+                a.kept += k;
+                a.blocks += nkb;
+            }
+            std::fill(tiles.begin(), tiles.end(), 0ull);
+            for (int64_t w = 0; w < words; ++w)
+                for (uint64_t x = uni[w]; x; x &= x - 1) {
+                    const int64_t kb = w * 64 + __builtin_ctzll(x);
+                    const int64_t k_lo = kb * bk, k_hi = std::min<int64_t>(k_lo + bk, L) - 1;
+                    for (int64_t tk = k_lo / kTileK; tk <= k_hi / kTileK; ++tk) tiles[tk >> 6] |= 1ull << (tk & 63);
+                }
+            int64_t nt = 0;
+            for (int64_t w = 0; w < twords; ++w) nt += __builtin_popcountll(tiles[w]);
+            a.exec_pairs += (double)nt * (double)(q1 - q0) * (double)kTileK;
+        }
+        acc[bh] = a;
+    });
+    Acc t;
+    for (const Acc &a : acc) {
+        t.blocks += a.blocks;
+        t.kept += a.kept;
+        t.kept_pairs += a.kept_pairs;
+        t.exec_pairs += a.exec_pairs;
     }
-    int64_t total = 0;
-    for (int64_t c : cnt) total += c;
-    return (double)total / ((double)rows * (double)nkb);
+    f.density = t.blocks ? (double)t.kept / (double)t.blocks : 0.0;
+    f.fill = t.exec_pairs > 0 ? std::min(1.0, t.kept_pairs / t.exec_pairs) : 1.0;
+    return f;
 }
 
 static int32_t choose_regime(const bsa_mask_desc_t &m, int32_t B, int32_t H, int64_t L, int32_t bq, int32_t bk,
-                             const bsa_plan_opts_t &o, int *regime, int *order, bool density_known = true)
+                             const bsa_plan_opts_t &o, int *regime, int *order, bool density_known = true,
+                             MaskFeatures *feat_out = nullptr)
 {
     *order = BSA_ORDER_XCD_GROUPED;
     if (o.force_regime >= 0 && o.task_order >= 0) {
@@ -815,13 +911,16 @@ static int32_t choose_regime(const bsa_mask_desc_t &m, int32_t B, int32_t H, int
         }
         const std::vector<LutRule> &rules = *rules_p;
         const int kind = m.kind == BSA_MASK_BLOCK_BITS ? BSA_MASK_BLOCK_U8 : m.kind;
-        const double dens = density_known ? mask_density(m, B, H, L, bq, bk) : -1.0;
+        const MaskFeatures feat = density_known ? mask_features(m, B, H, L, bq, bk) : MaskFeatures{};
+        if (feat_out) *feat_out = feat;
+        const double dens = feat.density, fill = feat.fill;
         *regime = -1;
         for (const LutRule &r : rules) {
             if (r.kind != kind) continue;
             if (r.bq && r.bq != bq) continue;
             if (r.bk && r.bk != bk) continue;
             if (dens >= 0 && (dens < r.dlo || dens > r.dhi)) continue;
+            if (fill >= 0 && (fill < r.flo || fill > r.fhi)) continue;
             if (L < r.Llo || L > r.Lhi) continue;
             *regime = r.regime;
             *order = r.order;
@@ -1210,11 +1309,14 @@ extern "C" int32_t bsa_plan(const bsa_mask_desc_t *logical_mask, int32_t B, int3
         if (std::getenv("BSA_TEST_FAIL_ALLOC")) return fail(BSA_ERR_OUT_OF_MEMORY, "simulated allocation failure");
         const bsa_mask_desc_t &m = *logical_mask;
         int regime = 0, order = 0;
-        st = choose_regime(m, B, H, L, block_q, block_k, o, &regime, &order);
+        MaskFeatures feat;
+        st = choose_regime(m, B, H, L, block_q, block_k, o, &regime, &order, true, &feat);
         if (st != BSA_OK) return st;
         t_regime = now_ns();
 
         std::unique_ptr<bsa_plan_s> p(new bsa_plan_s);
+        p->mask_density = feat.density;
+        p->mask_fill = feat.fill;
         p->B = B; p->H = H; p->L = L; p->d = d; p->dtype = o.dtype;
         p->kind = m.kind; p->block_q = block_q; p->block_k = block_k;
         p->regime = regime;
@@ -1354,11 +1456,14 @@ extern "C" int32_t bsa_plan_device(const bsa_mask_desc_t *logical_mask, int32_t 
         const bsa_mask_desc_t &m = *logical_mask;
         int regime = 0, order = 0;
         // a slice mask's density is nnz / (lists * L): known without reading it
-        st = choose_regime(m, B, H, L, block_q, block_k, o, &regime, &order, slice);
+        MaskFeatures feat;
+        st = choose_regime(m, B, H, L, block_q, block_k, o, &regime, &order, slice, &feat);
         if (st != BSA_OK) return st;
         const Regime &R = kRegimes[regime];
 
         std::unique_ptr<bsa_plan_s> p(new bsa_plan_s);
+        p->mask_density = feat.density;
+        p->mask_fill = feat.fill;
         p->B = B; p->H = H; p->L = L; p->d = d; p->dtype = o.dtype;
         p->kind = m.kind; p->block_q = block_q; p->block_k = block_k;
         p->regime = regime;
@@ -1638,6 +1743,8 @@ extern "C" int32_t bsa_plan_info(bsa_plan_t p, bsa_plan_info_t *out)
     out->plan_ns = p->plan_ns;
     for (int i = 0; i < 5; ++i) out->phase_ns[i] = p->phase_ns[i];
     out->task_order = p->task_order;
+    out->mask_density = p->mask_density;
+    out->mask_fill = p->mask_fill;
     if (p->mask_errors)
         return fail(BSA_ERR_INVALID_MASK, "the device mask had %lld invalid slice entries or lists (clamped or dropped)",
                     (long long)p->mask_errors);

@@ -470,8 +470,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1
 // ahead of V. Two barriers per tile: M_j between the halves of tile j and E_j
 // after them. After M_j the copy of K(j + 2) is issued (into the buffer K(j)
 // left, last read before M_j); after E_j the copy of V(j + 2) (into the
-// buffer V(j) left). M_j waits for K(j + 1), E_j for V(j + 1); each copy has
-// about one tile of compute to land.
+// buffer V(j) left). M_j waits for K(j + 1), E_j for V(j + 1) (each waits
+// for every copy the wave has in flight), so a copy has half a tile of
+// compute to land.
 template <int NW, int D>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void bsa_fwd_bf16_pipe(KernelArgs a)
 {
@@ -505,10 +506,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int qtok = token(qvalid ? q : L - 1);
     const int ntile = task.te - task.tb;
     const bool video = a.mode == kModeVideo;
-    // outstanding copies a wave may leave in flight at a barrier: one tensor
-    // of one tile (the video coordinate copy of wave 0 travels with K and is
-    // covered: waiting for fewer outstanding copies only waits longer)
-    constexpr int kWaitOne = 0x0F70 | C::INSTS;
 
     bool careful = false;
     f32x16 oacc[D / 32];
@@ -733,8 +730,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             const bool more = j + 1 < ntile;
             // half 0: scores of tile j's half 1 from K(j)
             half_step(&ksm[cb][0], 1, cb, rec_c, true, &vsm[cb][0], 0, ta, tb);
-            // M_j: K(j + 1) has landed; K(j)'s buffer takes K(j + 2)
-            __builtin_amdgcn_s_waitcnt(kWaitOne);
+            // M_j: K(j + 1) has landed; K(j)'s buffer takes K(j + 2). Every
+            // copy is awaited (vmcnt(0)), not just the older tensor's: a count
+            // that leaves the newest copies in flight would rely on the
+            // direct-to-LDS loads, and the loads and spill reloads the compiler
+            // places between them, completing in issue order.
+            wait_copies();
             __syncthreads();
             TileRec rec_2 = rec_n;
             if (j + 2 < ntile) {
@@ -744,7 +745,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             // half 1: scores of tile j + 1's half 0 from K(j + 1)
             half_step(&ksm[nb][0], 0, nb, rec_n, more, &vsm[cb][0], 1, tb, ta);
             // E_j: V(j + 1) has landed; V(j)'s buffer takes V(j + 2)
-            __builtin_amdgcn_s_waitcnt(kWaitOne);
+            wait_copies();
             __syncthreads();
             if (j + 2 < ntile) fetch(rec_2, Vh, &vsm[cb][0], false);
             rec_c = rec_n;

@@ -5,6 +5,11 @@
 // kept in fp32. It exists to check the method's arithmetic at a precision
 // where the remaining error is rounding of fp32 sums: its output agrees with
 // an fp64 evaluation to ~1e-6 relative per row.
+// Sums over tens of thousands of keys would lose that in fp32 alone (the
+// rounding of a running sum grows with the square root of its length, to
+// ~1e-5 at 20,000 keys), so each key tile's products and weights are summed
+// in fp32 (the MFMA accumulates one tile, from zero) and the tile results are
+// added in fp64: the output, the row sum and their rescaling run in double.
 //
 // Operand layout of v_mfma_f32_32x32x2_f32 (wave64): lane l supplies
 // A[l % 32][l / 32] and B[l / 32][l % 32]; the 32x32 result uses the same
@@ -29,7 +34,7 @@ namespace bsa {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <int NW, int D>
-__global__ __launch_bounds__(NW * 64) void bsa_fwd_f32(KernelArgs a)
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 2))) void bsa_fwd_f32(KernelArgs a)
 {
     constexpr int BK = kTileK;
     constexpr int KS = D + 1;  // K row stride in floats
@@ -65,12 +70,13 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_f32(KernelArgs a)
     const int qtok = head_token(qvalid ? q[0] : L - 1, tm, a);
     if (video) video_query_coords(qtok, a, qt[0], qwin[0]);
 
-    f32x16 oacc[D / 32];
+    double oacc[D / 32][16];  // output sums across tiles, fp64
 #pragma unroll
     for (int n = 0; n < D / 32; ++n)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[n][r] = 0.f;
-    float m_ref = -INFINITY, l_run = 0.f;
+        for (int r = 0; r < 16; ++r) oacc[n][r] = 0.0;
+    float m_ref = -INFINITY;
+    double l_run = 0.0;
     const int ntile = task.te - task.tb;
 
     if (ntile > 0) {
@@ -135,7 +141,7 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_f32(KernelArgs a)
             mx = swap_halves_max(mx) * a.scale_log2;
             const bool need = mx > m_ref + kSlack;
             if (__builtin_amdgcn_ballot_w64(need)) {
-                const float alpha = need ? __builtin_amdgcn_exp2f(m_ref - mx) : 1.0f;
+                const double alpha = need ? (double)__builtin_amdgcn_exp2f(m_ref - mx) : 1.0;
                 m_ref = need ? mx : m_ref;
                 l_run *= alpha;
 #pragma unroll
@@ -144,36 +150,57 @@ __global__ __launch_bounds__(NW * 64) void bsa_fwd_f32(KernelArgs a)
                     for (int r = 0; r < 16; ++r) oacc[n][r] *= alpha;
             }
             const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+            float psum[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 s0[0][r] = __builtin_amdgcn_exp2f(fmaf(s0[0][r], a.scale_log2, -m_use));
                 s1[0][r] = __builtin_amdgcn_exp2f(fmaf(s1[0][r], a.scale_log2, -m_use));
-                l_run += s0[0][r] + s1[0][r];
+                psum[r] = s0[0][r] + s1[0][r];
             }
+            // the tile's weights: a pairwise sum, then added in fp64
+#pragma unroll
+            for (int st = 8; st >= 1; st /= 2)
+#pragma unroll
+                for (int r = 0; r < st; ++r) psum[r] += psum[r + st];
+            l_run += (double)psum[0];
 
-            // ---- O^T += V^T P^T
+            // ---- O^T += V^T P^T for this tile (from zero), added to the fp64 sums
+            f32x16 otile[D / 32];
+#pragma unroll
+            for (int n = 0; n < D / 32; ++n) otile[n] = zero16;
 #pragma unroll
             for (int r = 0; r < 32; ++r) {
                 const int key = 32 * (r / 16) + 8 * ((r % 16) / 4) + 4 * hf + r % 4;
                 const float p = r < 16 ? s0[0][r] : s1[0][r - 16];
 #pragma unroll
                 for (int n = 0; n < D / 32; ++n)
-                    oacc[n] = __builtin_amdgcn_mfma_f32_32x32x2f32(vsm[key * VS + 32 * n + l32], p, oacc[n], 0, 0, 0);
+                    otile[n] = __builtin_amdgcn_mfma_f32_32x32x2f32(vsm[key * VS + 32 * n + l32], p, otile[n], 0, 0, 0);
             }
+#pragma unroll
+            for (int n = 0; n < D / 32; ++n)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) oacc[n][r] += (double)otile[n][r];
         }
     }
 
-    // ---- epilogue: O = O / l (0 for rows without a kept key)
-    const float l_tot = swap_halves_sum(l_run);
-    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    // ---- epilogue: O = O / l (0 for rows without a kept key), in fp64
+    const uint64_t lb = (uint64_t)__double_as_longlong(l_run);
+    const auto lo = __builtin_amdgcn_permlane32_swap((unsigned)lb, (unsigned)lb, false, false);
+    const auto hi = __builtin_amdgcn_permlane32_swap((unsigned)(lb >> 32), (unsigned)(lb >> 32), false, false);
+    // each lane holds its own half's sum in one of the swapped pair and the
+    // other half's in the other; their sum is the row's
+    const double l_a = __longlong_as_double((long long)(((uint64_t)hi[0] << 32) | lo[0]));
+    const double l_b = __longlong_as_double((long long)(((uint64_t)hi[1] << 32) | lo[1]));
+    const double l_tot = l_a + l_b;
+    const double inv = l_tot > 0.0 ? 1.0 / l_tot : 0.0;
     if (qvalid) {
         float *orow = Oh + (size_t)qtok * D;
 #pragma unroll
         for (int n = 0; n < D / 32; ++n)
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
-                const f32x4 o4 = {oacc[n][4 * rr] * inv, oacc[n][4 * rr + 1] * inv, oacc[n][4 * rr + 2] * inv,
-                                  oacc[n][4 * rr + 3] * inv};
+                const f32x4 o4 = {(float)(oacc[n][4 * rr] * inv), (float)(oacc[n][4 * rr + 1] * inv),
+                                  (float)(oacc[n][4 * rr + 2] * inv), (float)(oacc[n][4 * rr + 3] * inv)};
                 *(f32x4 *)(orow + 32 * n + 8 * rr + 4 * hf) = o4;
             }
     }

@@ -10,13 +10,21 @@ with every regime that can run them, times the forward passes on the GPU and
 writes the fastest regime of each bin as one rule of the table (the default
 unless another wins by more than 2%).
 
+Besides the kept-block density, block-mask bins are split by the mask's fill
+(kept pairs over the pairs of its non-empty 128 x 64 tiles, the feature the
+planner computes): a random layout of blocks smaller than the tile leaves most
+of each non-empty tile masked, where banded and windowed layouts fill them, and
+the two want different tile heights. Each synthetic request's fill is read
+back from the planner, the requests of a bin are grouped by fill bin, and each
+group's timings (summed over its layouts) give that group's rule.
+
 Inputs are seeded and synthetic (workloads module): BLOCK masks in banded,
 local-window and random layouts, video head routing (half spatial heads,
 half temporal heads in temporal-major order), slice lists, Q/K/V ~ N(0,1) in
 bf16. Each bin's rule names the fastest (regime, task order) pair.
 
 Usage (on the target GPU, from the repository root):
-    python3 block_sparse_attention_fwd_amd/lut/build_lut.py [--out lut/gfx950.lut] [--quick]
+    python3 block_sparse_attention_fwd_amd/lut/build_lut.py [--out lut/gfx950.lut] [--orders all] [--quick]
 Prints one progress line per measurement and writes the table (rules plus the
 measurements as comments). Rebuild the library afterwards: the default table
 is compiled into it.
@@ -34,15 +42,18 @@ import numpy as np  # noqa: E402
 
 TILE_REGIMES = (0, 1, 4)        # contiguous-tile regimes (block and video masks)
 SLICE_RULES = ((64, 2), (128, 3))  # slice masks: the gather regime of the slice height
-ORDERS = ((0, "xcd"), (1, "lpt"))  # task orders (BSA_ORDER_*: XCD-grouped, plain longest first) and table names
-# sequence-length bins: (representative token grid T x Hg x Wg, L range of the rule)
+ORDER_NAMES = ((0, "xcd"), (1, "lpt"))  # task orders (BSA_ORDER_*: XCD-grouped, plain longest first)
+ORDERS = ORDER_NAMES[:1]          # timed orders (--orders all adds lpt)
+# sequence-length bins: (representative token grid T x Hg x Wg, L range of the rule, heads of the requests)
 LENGTH_BINS = (
-    ((4, 32, 32), (0, 8192)),
-    ((13, 30, 52), (8193, 40000)),
-    ((21, 45, 80), (40001, 9999999999)),
+    ((4, 32, 32), (0, 8192), 24),
+    ((13, 30, 52), (8193, 40000), 24),
+    ((21, 45, 80), (40001, 150000), 24),
+    ((21, 90, 160), (150001, 9999999999), 4),
 )
 BLOCK_SHAPES = ((32, 32), (64, 64), (128, 128), (64, 256))
 DENSITY_BINS = ((0.05, (0.0, 0.1)), (0.15, (0.1, 0.275)), (0.4, (0.275, 1.0)))
+FILL_BINS = ((0.0, 0.75), (0.75, 1.0))  # low fill: random layouts of small blocks; high: banded / windowed
 LAYOUTS = ("banded", "local", "random")
 
 
@@ -51,7 +62,7 @@ def log(*a):
 
 
 def oname(order):
-    return dict(ORDERS)[order]
+    return dict(ORDER_NAMES)[order]
 
 
 # a choice other than the default (the first timed: regime 0, or the slice
@@ -77,6 +88,8 @@ def time_regimes(bsa, torch, w, regimes, q, k, v, o, reps, rounds=3):
     and thermal drift during the sweep falls on all of them alike."""
     from bsa_helpers import plan_workload
     plans = {(r, od): plan_workload(w, force_regime=r, task_order=od) for r in regimes for od, _ in ORDERS}
+    for r in regimes:  # warm the code and the clocks of each variant
+        bsa.forward(plans[(r, ORDERS[0][0])], q, k, v, o)
     try:
         times = {v: [] for v in plans}
         for _ in range(rounds):
@@ -99,53 +112,83 @@ def time_regimes(bsa, torch, w, regimes, q, k, v, o, reps, rounds=3):
             p.close()
 
 
+def fill_bin(fill):
+    for lo, hi in FILL_BINS:
+        if lo <= fill <= hi:
+            return (lo, hi)
+    return FILL_BINS[-1]
+
+
+def block_rules(bq, bk, dlo, dhi, llo, lhi, groups):
+    """Table lines of one (block shape, density, length) bin from its fill
+    groups {fill bin: summed timings}; a fill bin no layout fell into takes
+    the choice of the other, so every fill in [0, 1] resolves."""
+    picks = {fb: pick(t) for fb, t in groups.items()}
+    out = []
+    for fb in FILL_BINS:
+        best = picks.get(fb) or next(iter(picks.values()))
+        out.append(f"block   {bq:<7d} {bk:<7d} {dlo:<10g} {dhi:<10g} {fb[0]:<7g} {fb[1]:<7g} {llo:<6d} {lhi:<10d} "
+                   f"{best[0]} {oname(best[1])}")
+    return out
+
+
 def main():
+    global ORDERS
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--out", default=os.path.join(HERE, "gfx950.lut"))
-    ap.add_argument("--heads", type=int, default=24, help="heads per synthetic request")
     ap.add_argument("--reps", type=int, default=5)
+    ap.add_argument("--orders", choices=("xcd", "all"), default="xcd",
+                    help="task orders to time: the XCD-grouped one, or also plain longest first")
     ap.add_argument("--quick", action="store_true", help="one layout per bin, two length bins")
     args = ap.parse_args()
+    if args.orders == "all":
+        ORDERS = ORDER_NAMES
 
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     import torch
 
     import block_sparse_attention_fwd_amd as bsa
     import workloads as wl
-    from gpu_util import to_device_bf16
+    from bsa_helpers import plan_workload, to_device_bf16
 
     assert torch.cuda.is_available(), "the lookup table is built on the GPU it is for"
-    H, d = args.heads, 128
+    d = 128
     length_bins = LENGTH_BINS[:2] if args.quick else LENGTH_BINS
     layouts = LAYOUTS[:1] if args.quick else LAYOUTS
     rules, notes, slice_rules = [], [], []
     t_start = time.time()
-    for (T, Hg, Wg), (llo, lhi) in length_bins:
+    for (T, Hg, Wg), (llo, lhi), H in length_bins:
         L = T * Hg * Wg
         base = wl.Workload("lut", 9, 1, H, L, d, T, Hg, Wg, wl.BLOCK, 64, 64)
         Q, K, V = wl.make_qkv(base)
         q, k, v = to_device_bf16(Q), to_device_bf16(K), to_device_bf16(V)
+        del Q, K, V
         o = torch.empty_like(q)
         # video head routing
         wv = wl.svg("B", H=H, T=T, Hg=Hg, Wg=Wg, d=d, cfg=9)
         tv = time_regimes(bsa, torch, wv, TILE_REGIMES, q, k, v, o, args.reps)
         best = pick(tv)
         log(f"[lut] video L={L}: " + ", ".join(f"{vname(x)} {t:.4f} ms" for x, t in tv.items()) + f" -> {vname(best)}")
-        notes.append(f"video L={L}: " + " ".join(f"{vname(x)}={t:.4f}ms" for x, t in tv.items()))
-        rules.append(f"video   *       *       -1         1          {llo:<4d} {lhi:<10d} {best[0]} {oname(best[1])}")
+        notes.append(f"video L={L} H={H}: " + " ".join(f"{vname(x)}={t:.4f}ms" for x, t in tv.items()))
+        rules.append(f"video   *       *       -1         1          -1      1       {llo:<6d} {lhi:<10d} "
+                     f"{best[0]} {oname(best[1])}")
         for (bq, bk) in BLOCK_SHAPES:
             for rho, (dlo, dhi) in DENSITY_BINS:
-                tot = {}
+                groups = {}
                 for li, lay in enumerate(layouts):
                     w = wl.block_request(f"lut_{bq}x{bk}_{rho}_{lay}", 9, li, bq, bk, rho, lay, H, T, Hg, Wg, d)
-                    for x, t in time_regimes(bsa, torch, w, TILE_REGIMES, q, k, v, o, args.reps).items():
-                        tot[x] = tot.get(x, 0.0) + t
-                best = pick(tot)
-                log(f"[lut] block {bq}x{bk} density {rho} L={L}: "
-                    + ", ".join(f"{vname(x)} {t:.4f} ms" for x, t in tot.items()) + f" -> {vname(best)}")
-                notes.append(f"block {bq}x{bk} rho={rho} L={L} (sum over {len(layouts)} layouts): "
-                             + " ".join(f"{vname(x)}={t:.4f}ms" for x, t in tot.items()))
-                rules.append(f"block   {bq:<7d} {bk:<7d} {dlo:<10g} {dhi:<10g} {llo:<4d} {lhi:<10d} {best[0]} {oname(best[1])}")
+                    hp = plan_workload(w, device=-1)
+                    fill = hp.info()["mask_fill"]
+                    hp.close()
+                    tt = time_regimes(bsa, torch, w, TILE_REGIMES, q, k, v, o, args.reps)
+                    g = groups.setdefault(fill_bin(fill), {})
+                    for x, t in tt.items():
+                        g[x] = g.get(x, 0.0) + t
+                    log(f"[lut] block {bq}x{bk} density {rho} {lay} L={L} fill {fill:.3f}: "
+                        + ", ".join(f"{vname(x)} {t:.4f} ms" for x, t in tt.items()))
+                    notes.append(f"block {bq}x{bk} rho={rho} {lay} L={L} H={H} fill={fill:.3f}: "
+                                 + " ".join(f"{vname(x)}={t:.4f}ms" for x, t in tt.items()))
+                rules += block_rules(bq, bk, dlo, dhi, llo, lhi, groups)
         # slice masks: the gather regime is fixed by the slice height; the task
         # order is timed on the middle length bin (the key lists of the largest
         # one take gigabytes to generate) and applies to every length
@@ -156,20 +199,23 @@ def main():
                 best = pick(ts)
                 log(f"[lut] slice M={m} L={L}: " + ", ".join(f"{vname(x)} {t:.4f} ms" for x, t in ts.items()) + f" -> {vname(best)}")
                 notes.append(f"slice M={m} L={L}: " + " ".join(f"{vname(x)}={t:.4f}ms" for x, t in ts.items()))
-                slice_rules.append(f"slice   {m:<7d} 1       0          1          0    9999999999 {r} {oname(best[1])}")
+                slice_rules.append(f"slice   {m:<7d} 1       0          1          -1      1       0      9999999999 "
+                                   f"{r} {oname(best[1])}")
         del q, k, v, o
         torch.cuda.empty_cache()
-    rules += slice_rules or [f"slice   {m:<7d} 1       0          1          0    9999999999 {r} xcd" for m, r in SLICE_RULES]
+    rules += slice_rules or [f"slice   {m:<7d} 1       0          1          -1      1       0      9999999999 {r} xcd"
+                             for m, r in SLICE_RULES]
     # anything not covered (other block shapes): the default tile regime
-    rules.append("block   *       *       0          1          0    9999999999 0 xcd")
-    rules.append("video   *       *       -1         1          0    9999999999 0 xcd")
+    rules.append("block   *       *       0          1          0       1       0      9999999999 0 xcd")
+    rules.append("video   *       *       -1         1          -1      1       0      9999999999 0 xcd")
     head = [
         "# Regime lookup table for gfx950 (MI355X), built by lut/build_lut.py (offline profiling).",
         "# First matching rule wins. Regimes: 0 = 128x64 tiles (4 waves), 1 = 64x64 tiles (2 waves),",
         "# 2 = 64-query gather, 3 = 128-query gather, 4 = 256x64 tiles (8 waves).",
         "# Task orders: xcd = longest first, grouped so neighbouring query tiles share an XCD; lpt = longest first.",
-        f"# Synthetic requests: {H} heads, d = {d}, bf16; median of 3 interleaved rounds of {args.reps} forwards.",
-        "# kind  block_q block_k density_lo density_hi L_lo L_hi      regime order",
+        "# Features: density = kept blocks / blocks; fill = kept pairs / pairs of the non-empty 128x64 tiles.",
+        f"# Synthetic requests, d = {d}, bf16; median of 3 interleaved rounds of {args.reps} forwards.",
+        "# kind  block_q block_k density_lo density_hi fill_lo fill_hi L_lo   L_hi       regime order",
     ]
     text = "\n".join(head + rules + ["#", "# measurements:"] + ["# " + n for n in notes]) + "\n"
     with open(args.out, "w") as f:

@@ -152,6 +152,13 @@ typedef struct {
     int64_t phase_ns[5];           /* of which: ingest/validation, regime lookup,
                                       physical mapping, task organisation, upload */
     int32_t task_order;            /* BSA_ORDER_* the plan uses                    */
+    double mask_density;           /* regime-lookup features of the mask: kept
+                                      blocks / all blocks (slices: listed keys /
+                                      all pairs), and fill = kept pairs / pairs of
+                                      the non-empty 128 x 64 tiles (block masks,
+                                      from every 4th 128-row query tile); -1 when
+                                      the kind has none (video; fill of slices)  */
+    double mask_fill;
 } bsa_plan_info_t;
 
 typedef struct {

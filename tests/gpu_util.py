@@ -8,7 +8,7 @@ import torch
 import block_sparse_attention_fwd_amd as bsa
 import oracle
 import workloads as wl
-from bsa_helpers import plan_workload, to_device_bf16
+from bsa_helpers import plan_workload, to_device_bf16, tok_of_logical
 
 MAX_ABS = 1e-2   # bf16 inputs: max-abs error against the fp64 oracle
 MEAN_ABS = 1e-3  # bf16 inputs: mean-abs error against the fp64 oracle
@@ -28,9 +28,10 @@ def to_device(x: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(x)).to("cuda:0")
 
 
-def run_gpu(w, Q, K, V, force_regime=-1, plan=None, fill=float("nan"), task_order=-1):
+def run_gpu(w, Q, K, V, force_regime=-1, plan=None, fill=float("nan"), task_order=-1, rows=None):
     """Plan + forward on cuda:0 in the inputs' dtype (bf16 bits or float32);
-    returns (O as float64 numpy [B][H][L][d], plan)."""
+    returns (O as float64 numpy [B][H][L][d], plan), or with ``rows`` (flat
+    row ids) only those rows of O, [len(rows)][d], gathered on the device."""
     f32 = Q.dtype == np.float32
     dtype = bsa.DTYPE_F32 if f32 else bsa.DTYPE_BF16
     p = plan if plan is not None else plan_workload(w, device=0, force_regime=force_regime, dtype=dtype,
@@ -39,15 +40,72 @@ def run_gpu(w, Q, K, V, force_regime=-1, plan=None, fill=float("nan"), task_orde
     o = torch.full(q.shape, fill, dtype=torch.float32 if f32 else torch.bfloat16, device="cuda:0")
     bsa.forward(p, q, k, v, o)
     torch.cuda.synchronize()
+    del q, k, v
+    if rows is not None:
+        idx = torch.from_numpy(np.ascontiguousarray(rows, dtype=np.int64)).to("cuda:0")
+        sub = o.reshape(-1, w.d).index_select(0, idx)
+        return sub.float().cpu().numpy().astype(np.float64), p
     return o.float().cpu().numpy().astype(np.float64), p
 
 
-def compare(w, Q, K, V, O_gpu, rows=None, label="", max_abs=MAX_ABS, mean_abs=MEAN_ABS):
-    """Compare GPU output rows against the oracle. rows: flat row ids or None (all)."""
+def query_tile_rows(w, b, h, q0, tile):
+    """Flat row ids of the logical query positions [q0, q0 + tile) of head
+    (b, h): the rows one task of the kernel computes (temporal-major heads
+    map logical position p*T + t to token t*HW + p)."""
+    lo, hi = q0, min(q0 + tile, w.L)
+    if w.layout()[h] == wl.TEMPORAL_MAJOR:
+        toks = tok_of_logical(w.T, w.Hg * w.Wg)[lo:hi]
+    else:
+        toks = np.arange(lo, hi)
+    return (b * w.H + h) * w.L + toks
+
+
+def heavy_query_tile(w, b, h, tile, plan=None):
+    """First logical position of a demanding query tile of head (b, h): for
+    video masks, the tile with the most PARTIAL records in ``plan`` (exact
+    masking on the device); for block masks, the tile whose logical block
+    rows keep the most key blocks; for slice masks, the longest list."""
+    if w.kind == wl.VIDEO and plan is not None:
+        cnt = {}
+        for r in plan.coverage(b, h):
+            if r["kind"] == bsa.TILE_PARTIAL:
+                key = r["q0"] // tile * tile
+                cnt[key] = cnt.get(key, 0) + 1
+        return max(cnt, key=cnt.get) if cnt else 0
+    if w.kind == wl.BLOCK:
+        per_block = w.block[b, h].astype(np.int64).sum(axis=1)
+        per_tile = np.add.reduceat(per_block, np.arange(0, w.nqb, max(1, tile // w.bq))) if tile >= w.bq else per_block
+        i = int(np.argmax(per_tile))
+        return i * tile if tile >= w.bq else i * w.bq
+    if w.kind == wl.SLICE:
+        lens = np.diff(np.asarray(w.row_ptr, dtype=np.int64)).reshape(w.B, w.H, -1)[b, h]
+        return int(np.argmax(lens)) * w.bq
+    return 0
+
+
+def thick_rows(w, tile, per_head=256, seed=0, plan=None, heads=None):
+    """Per head: every row of one demanding query tile (heavy_query_tile),
+    every row of the last (ragged) tile, ``per_head`` random rows and the
+    first and last rows."""
+    g = np.random.default_rng(seed)
+    rows = []
+    for b in range(w.B):
+        for h in (range(w.H) if heads is None else heads):
+            base = (b * w.H + h) * w.L
+            rows.append(query_tile_rows(w, b, h, heavy_query_tile(w, b, h, tile, plan), tile))
+            rows.append(query_tile_rows(w, b, h, (w.L - 1) // tile * tile, tile))
+            rows.append(base + g.choice(w.L, per_head, replace=False))
+            rows.append(base + np.array([0, w.L - 1]))
+    return np.unique(np.concatenate(rows)).astype(np.int64)
+
+
+def compare(w, Q, K, V, O_gpu, rows=None, label="", max_abs=MAX_ABS, mean_abs=MEAN_ABS, gathered=False):
+    """Compare GPU output rows against the oracle. rows: flat row ids or None
+    (all); gathered: O_gpu already holds just those rows, in that order."""
     if rows is None:
         rows = np.arange(w.B * w.H * w.L, dtype=np.int64)
     ref, cnt = oracle.attend(w, Q, K, V, rows=rows, return_counts=True)
-    got = O_gpu.reshape(-1, w.d)[rows]
+    got = O_gpu.reshape(-1, w.d) if gathered else O_gpu.reshape(-1, w.d)[rows]
     err = np.abs(got - ref)
     mx, mean = float(err.max()), float(err.mean())
     nan = int(np.isnan(got).sum())
@@ -73,14 +131,14 @@ def compare(w, Q, K, V, O_gpu, rows=None, label="", max_abs=MAX_ABS, mean_abs=ME
     return mx, mean
 
 
-def compare_f32(w, Q, K, V, O_gpu, rows=None, label=""):
+def compare_f32(w, Q, K, V, O_gpu, rows=None, label="", gathered=False):
     """fp32 build: per-row normwise relative error against the fp64 oracle
     (max over rows of |O - O_ref|_inf / |O_ref|_inf <= 1e-5); rows without a
     kept key exactly 0; elementwise relative error reported only."""
     if rows is None:
         rows = np.arange(w.B * w.H * w.L, dtype=np.int64)
     ref, cnt = oracle.attend(w, Q, K, V, rows=rows, return_counts=True)
-    got = O_gpu.reshape(-1, w.d)[rows]
+    got = O_gpu.reshape(-1, w.d) if gathered else O_gpu.reshape(-1, w.d)[rows]
     nan = int(np.isnan(got).sum())
     zero_rows = cnt == 0
     zero_ok = bool(np.all(got[zero_rows] == 0.0))

@@ -173,26 +173,30 @@ def test_simulated_allocation_failure(monkeypatch):
 def test_lookup_table_file(tmp_path):
     m = _block()
     f = tmp_path / "lut.txt"
-    f.write_text("# test\nblock * * 0 1 0 99999 0\n")
+    f.write_text("# test\nblock * * 0 1 0 1 0 99999 0\n")
     p = bsa.plan(bsa.MASK_BLOCK_U8, 1, 2, 256, 64, 64, 64, data=m, lut_path=str(f), device=-1)
     assert p.info()["regime"] == 0
-    f.write_text("block 64 64 0 1 0 99999 1\n")
+    f.write_text("block 64 64 0 1 0 1 0 99999 1\n")
     assert bsa.plan(bsa.MASK_BLOCK_U8, 1, 2, 256, 64, 64, 64, data=m, lut_path=str(f), device=-1).info()["regime"] == 1
     f.write_text("block 64 64 0 1\n")
     expect(bsa.ERR_INVALID_ARGUMENT, bsa.plan, bsa.MASK_BLOCK_U8, 1, 2, 256, 64, 64, 64, data=m, lut_path=str(f),
            device=-1, match="malformed")
+    # the fill range: a rule whose fill range excludes the mask's fill is skipped
+    f.write_text("block 64 64 0 1 0 0.5 0 99999 1\nblock 64 64 0 1 0.5 1 0 99999 4\n")
+    info = bsa.plan(bsa.MASK_BLOCK_U8, 1, 2, 256, 64, 64, 64, data=m, lut_path=str(f), device=-1).info()
+    assert info["regime"] == (1 if info["mask_fill"] < 0.5 else 4)
     expect(bsa.ERR_INVALID_ARGUMENT, bsa.plan, bsa.MASK_BLOCK_U8, 1, 2, 256, 64, 64, 64, data=m,
            lut_path=str(tmp_path / "nope"), device=-1)
     # the optional order column; an explicit task_order option overrides it
-    f.write_text("block 64 64 0 1 0 99999 1 lpt\n")
+    f.write_text("block 64 64 0 1 0 1 0 99999 1 lpt\n")
     info = bsa.plan(bsa.MASK_BLOCK_U8, 1, 2, 256, 64, 64, 64, data=m, lut_path=str(f), device=-1).info()
     assert (info["regime"], info["task_order"]) == (1, bsa.ORDER_LONGEST_FIRST)
     info = bsa.plan(bsa.MASK_BLOCK_U8, 1, 2, 256, 64, 64, 64, data=m, lut_path=str(f), device=-1,
                     task_order=bsa.ORDER_XCD_GROUPED).info()
     assert (info["regime"], info["task_order"]) == (1, bsa.ORDER_XCD_GROUPED)
-    f.write_text("block 64 64 0 1 0 99999 1 xcd\n")
+    f.write_text("block 64 64 0 1 0 1 0 99999 1 xcd\n")
     assert bsa.plan(bsa.MASK_BLOCK_U8, 1, 2, 256, 64, 64, 64, data=m, lut_path=str(f), device=-1).info()["task_order"] == 0
-    f.write_text("block 64 64 0 1 0 99999 1 fifo\n")
+    f.write_text("block 64 64 0 1 0 1 0 99999 1 fifo\n")
     expect(bsa.ERR_INVALID_ARGUMENT, bsa.plan, bsa.MASK_BLOCK_U8, 1, 2, 256, 64, 64, 64, data=m, lut_path=str(f),
            device=-1, match="unknown order")
     expect(bsa.ERR_INVALID_ARGUMENT, bsa.plan, bsa.MASK_BLOCK_U8, 1, 2, 256, 64, 64, 64, data=m, device=-1,

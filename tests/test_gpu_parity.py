@@ -22,7 +22,7 @@ def _gpu():
 
 import block_sparse_attention_fwd_amd as bsa  # noqa: E402
 from bsa_helpers import plan_workload  # noqa: E402
-from gpu_util import compare, log, run_gpu, sample_rows, to_device  # noqa: E402
+from gpu_util import compare, log, run_gpu, sample_rows, thick_rows, to_device  # noqa: E402
 
 
 def _small_block_cases():
@@ -172,17 +172,22 @@ def test_svg_full_size_sampled(run, regime):
     Q, K, V = wl.make_qkv(w)
     log(f"[case] svg full run={run} regime={regime}")
     O, p = run_gpu(w, Q, K, V, force_regime=regime)
-    rows = sample_rows(w, per_head=48)
+    # per head: the query tile with the most PARTIAL (exactly masked) tiles,
+    # the ragged last tile and random rows
+    rows = thick_rows(w, p.info()["tile_q"], per_head=256, plan=p)
     compare(w, Q, K, V, O, rows=rows, label=f"svg{run} {p.info()}")
 
 
 def test_fgattn_full_size_sampled():
+    """FG-Attn slices at full size (24 heads, L = 32,760, M = 64): per head
+    every row of the query block with the longest key list and of the ragged
+    last block, plus 256 random rows."""
     w = wl.fgattn()
     Q, K, V = wl.make_qkv(w)
     log("[case] fgattn full")
-    O, p = run_gpu(w, Q, K, V)
-    rows = sample_rows(w, per_head=16, tile=64)
-    compare(w, Q, K, V, O, rows=rows, label=f"fgattn {p.info()}")
+    rows = thick_rows(w, 64)
+    O, p = run_gpu(w, Q, K, V, rows=rows)
+    compare(w, Q, K, V, O, rows=rows, gathered=True, label=f"fgattn {p.info()}")
 
 
 @pytest.fixture(scope="module")
@@ -196,28 +201,31 @@ def tessera_qkv():
 def test_tessera_full_size_sampled(i, tessera_qkv):
     """Tessera-style block masks at full size (24 heads, L = 75,600, d = 128):
     every block shape, density and layout appears among the masks tested;
-    sampled rows of every head, including the ragged last query tile."""
+    per head every row of the query tile whose blocks keep the most keys and
+    of the ragged last tile, plus 256 random rows."""
     w = wl.tessera(i)
     Q, K, V = tessera_qkv
     log(f"[case] tessera mask {i}: {w.bq}x{w.bk} density {float(w.block.mean()):.4f}")
-    O, p = run_gpu(w, Q, K, V)
-    rows = sample_rows(w, per_head=12, tile=256)
-    compare(w, Q, K, V, O, rows=rows, label=f"tessera{i} {p.info()['regime']}")
+    rows = thick_rows(w, 256, seed=i)
+    O, p = run_gpu(w, Q, K, V, rows=rows)
+    compare(w, Q, K, V, O, rows=rows, gathered=True, label=f"tessera{i} {p.info()['regime']}")
 
 
 @pytest.mark.timeout(900)
 def test_highres_full_size_sampled():
     """High-res 128x128 rasterised block mask at full size (24 heads,
     L = 302,400, d = 128; spatial heads frame-major, temporal heads
-    temporal-major); sampled rows of every head."""
+    temporal-major): per head every row of its heaviest query tile (in the
+    head's own token order) and of the ragged last tile, plus 256 random
+    rows."""
     w = wl.highres()
     log("[case] generating high-res Q/K/V (24 x 302400 x 128)")
     Q, K, V = wl.make_qkv(w)
+    rows = thick_rows(w, 128)
     for regime in (-1, 5):
         log(f"[case] highres full regime={regime}")
-        O, p = run_gpu(w, Q, K, V, force_regime=regime)
-        rows = sample_rows(w, per_head=8, tile=128)
-        compare(w, Q, K, V, O, rows=rows, label=f"highres {p.info()}")
+        O, p = run_gpu(w, Q, K, V, force_regime=regime, rows=rows)
+        compare(w, Q, K, V, O, rows=rows, gathered=True, label=f"highres {p.info()}")
 
 
 @pytest.mark.parametrize("regime", [-1, 4, 5, 6])

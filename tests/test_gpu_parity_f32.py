@@ -20,7 +20,7 @@ def _gpu():
     bsa.lib()  # fail loudly if the library is missing
 
 
-from gpu_util import compare_f32, log, run_gpu, sample_rows  # noqa: E402
+from gpu_util import compare_f32, log, run_gpu, sample_rows, thick_rows  # noqa: E402
 
 
 @pytest.mark.parametrize("regime", [-1, 0, 1, 4])
@@ -89,3 +89,44 @@ def test_svg_full_size_sampled_f32():
     O, p = run_gpu(w, Q, K, V)
     rows = sample_rows(w, per_head=32)
     compare_f32(w, Q, K, V, O, rows=rows, label=f"f32 svgB {p.info()['regime']}")
+
+
+def test_fgattn_full_size_sampled_f32():
+    """FG-Attn slices at full size (24 heads, L = 32,760, M = 64), fp32 build;
+    per head the longest list's query block, the ragged last block and 256
+    random rows."""
+    w = wl.fgattn()
+    Q, K, V = wl.make_qkv(w, "f32")
+    rows = thick_rows(w, 64)
+    log("[case] f32 fgattn full")
+    O, p = run_gpu(w, Q, K, V, rows=rows)
+    compare_f32(w, Q, K, V, O, rows=rows, gathered=True, label=f"f32 fgattn {p.info()['regime']}")
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("i", [28, 17, 7])
+def test_tessera_full_size_sampled_f32(i):
+    """Tessera-style masks at full size (24 heads, L = 75,600), fp32 build:
+    32x32 random (mask 28), 64x64 local window (17), 64x256 banded (7), all at
+    density 0.15; per head the heaviest query tile, the ragged last tile and
+    256 random rows."""
+    w = wl.tessera(i)
+    Q, K, V = wl.make_qkv(w, "f32")
+    rows = thick_rows(w, 256, seed=i)
+    log(f"[case] f32 tessera mask {i}: {w.bq}x{w.bk}")
+    O, p = run_gpu(w, Q, K, V, rows=rows)
+    compare_f32(w, Q, K, V, O, rows=rows, gathered=True, label=f"f32 tessera{i} {p.info()['regime']}")
+
+
+@pytest.mark.timeout(900)
+def test_highres_full_size_sampled_f32():
+    """High-res at full size (24 heads, L = 302,400), fp32 build; per head its
+    heaviest query tile (in the head's token order), the ragged last tile and
+    256 random rows."""
+    w = wl.highres()
+    log("[case] f32 generating high-res Q/K/V")
+    Q, K, V = wl.make_qkv(w, "f32")
+    rows = thick_rows(w, 128)
+    log("[case] f32 highres full")
+    O, p = run_gpu(w, Q, K, V, rows=rows)
+    compare_f32(w, Q, K, V, O, rows=rows, gathered=True, label=f"f32 highres {p.info()['regime']}")

@@ -68,3 +68,56 @@ def test_every_dense_bin_resolves_to_a_tile_regime():
         info = bsa.plan(bsa.MASK_VIDEO, w.B, w.H, w.L, 64, 1, 1, head_pattern=w.head_pattern, anchor_frame=0,
                         radius=2, head_layout=w.head_layout, T=w.T, Hg=w.Hg, Wg=w.Wg, device=-1).info()
         assert info["regime"] in (0, 1, 4)
+
+
+def _features_by_definition(block, L, bq, bk, stride):
+    """Density and fill written out from their definitions with numpy:
+    density = kept blocks / blocks of the sampled logical rows; fill = kept
+    pairs / pairs of the non-empty 128 x 64 tiles, over every stride-th
+    128-row query tile of every head."""
+    B, H, nqb, nkb = block.shape
+    kept_blocks = blocks = 0
+    kept_pairs = exec_pairs = 0.0
+    qlen = np.minimum(np.arange(1, nqb + 1) * bq, L) - np.arange(nqb) * bq
+    nqt, nkt = -(-L // 128), -(-L // 64)
+    for bh in range(B * H):
+        m = block.reshape(B * H, nqb, nkb)[bh].astype(bool)
+        el = np.kron(m, np.ones((bq, bk), bool))[:L, :L]  # element mask (logical positions)
+        for tq in range(0, nqt, stride):
+            q0, q1 = tq * 128, min(tq * 128 + 128, L)
+            rows = range(q0 // bq, (q1 - 1) // bq + 1)
+            kept_blocks += int(m[list(rows)].sum())
+            blocks += len(rows) * nkb
+            sub = el[q0:q1]
+            kept_pairs += float(sub.sum())
+            tiles = np.pad(sub.any(axis=0), (0, nkt * 64 - L)).reshape(nkt, 64).any(axis=1)
+            exec_pairs += float(tiles.sum()) * (q1 - q0) * 64
+    return kept_blocks / blocks, kept_pairs / exec_pairs
+
+
+@pytest.mark.parametrize("bq,bk", [(32, 32), (64, 64), (128, 128), (64, 256), (256, 32)])
+@pytest.mark.parametrize("layout", ["random", "banded"])
+def test_mask_features_match_definition(bq, bk, layout):
+    """The planner's regime features (bsa_plan_info mask_density and
+    mask_fill) equal their definitions, on masks short enough that every
+    query tile is sampled and on longer ones where every 4th is; random
+    layouts of small blocks have low fill, banded ones high."""
+    _lib()
+    for L in (1000, 4100):
+        nqb, nkb = -(-L // bq), -(-L // bk)
+        g = np.random.default_rng(bq * 7 + bk)
+        if layout == "random":
+            m = (g.random((1, 2, nqb, nkb)) < 0.2).astype(np.uint8)
+        else:
+            cq = (np.arange(nqb) + 0.5) * bq
+            ck = (np.arange(nkb) + 0.5) * bk
+            m = np.broadcast_to((np.abs(cq[:, None] - ck[None, :]) <= 300)[None, None], (1, 2, nqb, nkb)).astype(np.uint8)
+        info = bsa.plan(bsa.MASK_BLOCK_U8, 1, 2, L, 64, bq, bk, data=np.ascontiguousarray(m), device=-1).info()
+        stride = 4 if -(-L // 128) >= 16 else 1
+        dens, fill = _features_by_definition(m, L, bq, bk, stride)
+        assert abs(info["mask_density"] - dens) < 1e-12, (L, info["mask_density"], dens)
+        assert abs(info["mask_fill"] - fill) < 1e-9, (L, info["mask_fill"], fill)
+    if layout == "banded":
+        assert info["mask_fill"] > 0.75
+    elif bq < 128 or bk < 64:
+        assert info["mask_fill"] < 0.75

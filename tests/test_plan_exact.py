@@ -191,3 +191,137 @@ def test_svg_plan_exact_on_sampled_query_tiles():
                     else:
                         cnt[rows, ks] += em[np.ix_(qs[rows], ks)]
                 assert np.array_equal(cnt, em[qs].astype(np.uint16)), (run, h, q0)
+
+
+# ---------------------------------------------------------------------------
+# full-size plans (host-only): the configurations' own masks
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("regime", [-1, 0, 1, 4])
+def test_tiny_plan_element_exact(regime):
+    """Tiny configuration (2 heads, 1,024 tokens, 64x64 blocks): every pair of
+    every head, element by element, against the oracle's expansion."""
+    w = wl.tiny()
+    p = plan_workload(w, device=-1, force_regime=regime)
+    for h in range(w.H):
+        got = coverage_counts(p, w, 0, h)
+        want = expected(w, 0, h)
+        assert np.array_equal(got, want), (regime, h, int((got != want).sum()))
+
+
+def test_fgattn_plan_lists_exact():
+    """FG-Attn slices at full size (24 heads, L = 32,760, M = 64): for sampled
+    heads, the keys the plan gathers for each 64-query block, in record order,
+    are exactly that block's list, each once; every block is present."""
+    w = wl.fgattn()
+    p = plan_workload(w, device=-1)
+    nqb = w.nqb
+    rp = np.asarray(w.row_ptr, dtype=np.int64)
+    for h in (0, 7, 16, 23):
+        got = {}
+        for r in p.coverage(0, h):
+            assert r["predicate"] == bsa.PRED_LIST and r["q1"] - r["q0"] <= w.bq
+            got.setdefault(r["q0"], []).append(r["keys"])
+        for i in range(nqb):
+            e = h * nqb + i
+            want = w.col_idx[rp[e]:rp[e + 1]]
+            keys = np.concatenate(got.get(i * w.bq, [np.zeros(0, np.int32)]))
+            assert np.array_equal(keys, want), (h, i, keys.size, want.size)
+
+
+def _cell_coverage(p, w, b, h):
+    """Times each logical cell is computed, from the plan's records. A cell is
+    the intersection of a logical block and a physical tile (min(bq, tile_q)
+    x min(bk, 64) positions): FULL records cover every cell of their tile,
+    PARTIAL records the cells whose sub-block keep bit is set."""
+    recs = p.coverage(b, h)
+    tq = p.info()["tile_q"]
+    cq, ck = min(w.bq, tq), min(w.bk, 64)
+    nq, nk = -(-w.L // cq), -(-w.L // ck)
+    cnt = np.zeros((nq, nk), np.uint8)
+    q0 = np.array([r["q0"] for r in recs], np.int64)
+    q1 = np.array([r["q1"] for r in recs], np.int64)
+    k0 = np.array([r["k0"] for r in recs], np.int64)
+    k1 = np.array([r["k1"] for r in recs], np.int64)
+    full = np.array([r["kind"] == bsa.TILE_FULL for r in recs])
+    bits = np.array([r["sub_bits"] for r in recs], np.int64)
+    preds = {r["predicate"] for r in recs if r["kind"] != bsa.TILE_FULL}
+    assert preds <= {bsa.PRED_SUBBLOCK}, preds
+    nsk = 64 // ck
+    for i in range(-(-tq // cq)):
+        for j in range(-(-64 // ck)):
+            rows, cols = q0 + i * cq, k0 + j * ck
+            live = (rows < q1) & (cols < k1)
+            keep = live & (full | (((bits >> (i * nsk + j)) & 1) == 1))
+            np.add.at(cnt, (rows[keep] // cq, cols[keep] // ck), 1)
+    want = np.kron(w.block[b, h].astype(np.uint8), np.ones((w.bq // cq, w.bk // ck), np.uint8))[:nq, :nk]
+    return cnt, want
+
+
+def _tile_elements(w, b, h, q0, q1, k0, k1):
+    """Kept pairs of a rectangle of logical positions from the block mask's
+    definition (every pair of a kept block), for exhaustive tile checks."""
+    qb = np.arange(q0, q1) // w.bq
+    kb = np.arange(k0, k1) // w.bk
+    return w.block[b, h][np.ix_(qb, kb)] != 0
+
+
+def _partial_tiles_exact(p, w, b, h, tiles):
+    """Every PARTIAL record of the query tiles starting at ``tiles``: its
+    computed pairs (sub-block bits; keys past L do not exist) equal the
+    rectangle's kept pairs."""
+    n = 0
+    for r in p.coverage(b, h):
+        if r["kind"] == bsa.TILE_FULL or r["q0"] // p.info()["tile_q"] * p.info()["tile_q"] not in tiles:
+            continue
+        nsk = 64 // r["sub_k"]
+        qi = (np.arange(r["q0"], r["q1"]) - r["q0"]) // r["sub_q"]
+        kj = (np.arange(r["k0"], r["k1"]) - r["k0"]) // r["sub_k"]
+        got = ((r["sub_bits"] >> (qi[:, None] * nsk + kj[None, :])) & 1) == 1
+        want = _tile_elements(w, b, h, r["q0"], r["q1"], r["k0"], r["k1"])
+        assert np.array_equal(got, want), (h, r)
+        n += 1
+    return n
+
+
+@pytest.mark.parametrize("i", [0, 4, 9, 13, 17, 22, 26, 28, 35, 39, 45])
+def test_tessera_plan_cells_exact(i):
+    """Tessera-style masks at full size (L = 75,600): on sampled heads every
+    logical cell is computed exactly once if its block is kept and never
+    otherwise; every PARTIAL tile of sampled query tiles (the last, ragged one
+    included) is exact element by element. The block definition itself is
+    checked against the oracle's expansion on sampled rows."""
+    w = wl.tessera(i)
+    p = plan_workload(w, device=-1)
+    tq = p.info()["tile_q"]
+    last = (w.L - 1) // tq * tq
+    for h in ((0, 23) if w.bq == 32 else (0, 13, 23)):
+        cnt, want = _cell_coverage(p, w, 0, h)
+        assert np.array_equal(cnt, want), (i, h, int((cnt != want).sum()))
+        _partial_tiles_exact(p, w, 0, h, {0, tq * 57, last})
+        for q in (0, 4111, w.L - 1):
+            keys = oracle.row_keys(w, 0, h, q)
+            assert np.array_equal(np.flatnonzero(_tile_elements(w, 0, h, q, q + 1, 0, w.L)[0]), keys)
+
+
+def test_highres_plan_cells_exact():
+    """High-res at full size (L = 302,400, 128x128 blocks; spatial heads
+    frame-major, temporal heads temporal-major): a spatial and a temporal head,
+    every logical cell computed exactly once if kept and never otherwise; the
+    ragged last query tile's PARTIAL tiles exact element by element; the block
+    definition against the oracle's expansion on sampled rows (temporal-major
+    positions mapped to tokens)."""
+    w = wl.highres()
+    p = plan_workload(w, device=-1)
+    tq = p.info()["tile_q"]
+    tok = tok_of_logical(w.T, w.Hg * w.Wg)
+    for h in (0, 12):
+        cnt, want = _cell_coverage(p, w, 0, h)
+        assert np.array_equal(cnt, want), (h, int((cnt != want).sum()))
+        _partial_tiles_exact(p, w, 0, h, {(w.L - 1) // tq * tq})
+        for j in (0, 151234, w.L - 1):
+            qtok = tok[j] if w.layout()[h] else j
+            keys = oracle.row_keys(w, 0, h, qtok)
+            lk = np.flatnonzero(_tile_elements(w, 0, h, j, j + 1, 0, w.L)[0])
+            want_tok = np.sort(tok[lk]) if w.layout()[h] else lk
+            assert np.array_equal(want_tok, keys), (h, j)
