@@ -332,10 +332,11 @@ def test_device_plan_edge_shapes():
 def test_device_plan_regime_ignores_density(tmp_path):
     """With a table whose rules split one block shape by density, the host
     planner takes the rule of the mask's density and the device planner, which
-    never reads the mask on the host, the first rule of the shape and length."""
+    never reads the mask on the host (no density, no fill), the first rule of
+    the shape and length."""
     lut = tmp_path / "split.lut"
-    lut.write_text("block 32 32 0 0.5 0 9999 1 lpt\n"
-                   "block 32 32 0.5 1 0 9999 4 xcd\n")
+    lut.write_text("block 32 32 0 0.5 0 1 0 9999 1 lpt\n"
+                   "block 32 32 0.5 1 0 1 0 9999 4 xcd\n")
     w = wl.Workload("split", 73, 1, 2, 330, 64, 0, 0, 0, wl.BLOCK, 32, 32)
     w.block = (np.random.default_rng(7).random((1, 2, w.nqb, w.nkb)) < 0.8).astype(np.uint8)
     ih = plan_workload(w, lut_path=str(lut)).info()
