@@ -33,7 +33,7 @@ ABI_VERSION = 5  # the structures below mirror this version of bsa.h
 
 EXPORTED = ["bsa_abi_version", "bsa_plan_opts_default", "bsa_plan", "bsa_plan_device", "bsa_forward", "bsa_plan_destroy",
             "bsa_request_create", "bsa_request_submit", "bsa_request_finish", "bsa_request_stats",
-            "bsa_request_destroy", "bsa_route_heads",
+            "bsa_request_destroy", "bsa_route_heads", "bsa_route_heads_noalloc",
             "bsa_plan_info", "bsa_plan_coverage", "bsa_regime_count", "bsa_regime_info", "bsa_status_str",
             "bsa_last_error"]
 
@@ -137,10 +137,11 @@ def lib(path: str = LIB_PATH):
     L.bsa_request_stats.argtypes = [ctypes.c_void_p, ctypes.POINTER(RequestStats)]
     L.bsa_request_destroy.restype = None
     L.bsa_request_destroy.argtypes = [ctypes.c_void_p]
-    L.bsa_route_heads.restype = ctypes.c_int32
-    L.bsa_route_heads.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
-                                  ctypes.c_int64, ctypes.c_int32, ctypes.POINTER(RouteDesc), ctypes.c_void_p,
-                                  ctypes.c_void_p, ctypes.c_void_p]
+    for fn in (L.bsa_route_heads, L.bsa_route_heads_noalloc):
+        fn.restype = ctypes.c_int32
+        fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                       ctypes.c_int64, ctypes.c_int32, ctypes.POINTER(RouteDesc), ctypes.c_void_p,
+                       ctypes.c_void_p, ctypes.c_void_p]
     L.bsa_forward.restype = ctypes.c_int32
     L.bsa_forward.argtypes = [ctypes.c_void_p] * 6
     L.bsa_plan_destroy.argtypes = [ctypes.c_void_p]
@@ -397,6 +398,25 @@ def route_heads(q, k, v, B: int, H: int, L: int, d: int, T: int, Hg: int, Wg: in
     err = np.zeros((H, 2), np.float64)
     _check(lib().bsa_route_heads(_dptr(q), _dptr(k), _dptr(v), B, H, L, d, ctypes.byref(desc),
                                  _stream_handle(stream), _ptr(pat), _ptr(err)))
+    return pat, err
+
+
+def route_heads_noalloc(q, k, v, B: int, H: int, L: int, d: int, T: int, Hg: int, Wg: int, rows, *,
+                        anchor_frame: int = 0, radius: int = 2, device: int = 0, stream=None):
+    """bsa_route_heads_noalloc: route_heads with no memory allocation (a
+    fixed scratch array per device). Returns (pattern uint8 [H], err float64
+    [H][2]); synchronises with `stream`."""
+    r = np.ascontiguousarray(rows, dtype=np.int32)
+    desc = RouteDesc()
+    desc.T, desc.Hg, desc.Wg = T, Hg, Wg
+    desc.anchor_frame, desc.radius = anchor_frame, radius
+    desc.rows = _ptr(r)
+    desc.n_rows = r.size
+    desc.device = device
+    pat = np.zeros(H, np.uint8)
+    err = np.zeros((H, 2), np.float64)
+    _check(lib().bsa_route_heads_noalloc(_dptr(q), _dptr(k), _dptr(v), B, H, L, d, ctypes.byref(desc),
+                                         _stream_handle(stream), _ptr(pat), _ptr(err)))
     return pat, err
 
 

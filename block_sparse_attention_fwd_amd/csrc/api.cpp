@@ -1969,9 +1969,9 @@ static int64_t probe_workgroups()
     return e ? std::max(1, std::atoi(e)) : 256;
 }
 
-extern "C" int32_t bsa_route_heads(const void *Q, const void *K, const void *V, int32_t B, int32_t H, int64_t L,
-                                   int32_t d, const bsa_route_desc_t *desc, void *stream, uint8_t *head_pattern,
-                                   double *err)
+// Argument checks shared by both routing entry points.
+static int32_t check_route_args(const void *Q, const void *K, const void *V, int32_t B, int32_t H, int64_t L,
+                                int32_t d, const bsa_route_desc_t *desc, const uint8_t *head_pattern)
 {
     if (!Q || !K || !V || !desc || !head_pattern || !desc->rows)
         return fail(BSA_ERR_INVALID_ARGUMENT, "Q, K, V, desc, desc->rows and head_pattern must be non-NULL");
@@ -1989,14 +1989,51 @@ extern "C" int32_t bsa_route_heads(const void *Q, const void *K, const void *V, 
     for (int32_t i = 0; i < r.n_rows; ++i)
         if (r.rows[i] < 0 || r.rows[i] >= L) return fail(BSA_ERR_INVALID_ARGUMENT, "row %d = %d out of range", i, r.rows[i]);
     if (r.device < 0) return fail(BSA_ERR_INVALID_ARGUMENT, "routing needs a device (desc->device = %d)", r.device);
+    return BSA_OK;
+}
+
+// The probe's arguments other than its device buffers (rows, part, err_rows).
+static RouteArgs route_args(const void *Q, const void *K, const void *V, int32_t B, int32_t H, int64_t L, int32_t d,
+                            const bsa_route_desc_t &r, int32_t nchunk)
+{
+    RouteArgs a{};
+    a.Q = Q; a.K = K; a.V = V;
+    a.BH = B * H;
+    a.L = (int32_t)L;
+    a.HW = r.Hg * r.Wg;
+    a.W = r.Wg;
+    a.anchor = r.anchor_frame;
+    a.radius = r.radius;
+    magic_div((uint32_t)a.HW, &a.magic_HW, &a.shift_HW);
+    magic_div((uint32_t)a.W, &a.magic_W, &a.shift_W);
+    a.S = r.n_rows;
+    a.nsb = (r.n_rows + 31) / 32;
+    a.nkt = (int32_t)((L + kTileK - 1) / kTileK);
+    a.nchunk = nchunk;
+    a.tiles_per_chunk = (a.nkt + nchunk - 1) / nchunk;
+    a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
+    return a;
+}
+
+// Key chunks of the probe: about probe_workgroups() workgroups of six waves
+// (two blocks of 32 sampled rows x three variants), at most one per key tile.
+static int32_t route_chunks(int32_t BH, int32_t S, int64_t L)
+{
+    const int32_t nsb = (S + 31) / 32;
+    const int64_t nkt = (L + kTileK - 1) / kTileK;
+    const int64_t units = (int64_t)BH * ((nsb + 1) / 2);
+    return (int32_t)std::max<int64_t>(1, std::min<int64_t>(nkt, probe_workgroups() / units));
+}
+
+extern "C" int32_t bsa_route_heads(const void *Q, const void *K, const void *V, int32_t B, int32_t H, int64_t L,
+                                   int32_t d, const bsa_route_desc_t *desc, void *stream, uint8_t *head_pattern,
+                                   double *err)
+{
+    if (int32_t st = check_route_args(Q, K, V, B, H, L, d, desc, head_pattern); st != BSA_OK) return st;
+    const bsa_route_desc_t &r = *desc;
     try {
         const int32_t BH = B * H, S = r.n_rows, nsb = (S + 31) / 32;
-        const int32_t nkt = (int32_t)((L + kTileK - 1) / kTileK);
-        // key chunks: about probe_workgroups() workgroups of six waves (two
-        // blocks of 32 sampled rows x three variants)
-        const int64_t units = (int64_t)BH * ((nsb + 1) / 2);
-        const int32_t nchunk = (int32_t)std::max<int64_t>(1, std::min<int64_t>(nkt, probe_workgroups() / units));
-        const int32_t tpc = (nkt + nchunk - 1) / nchunk;
+        const int32_t nchunk = route_chunks(BH, S, L);
         const size_t part_floats = (size_t)BH * nsb * nchunk * 3 * (64 + 32 * (size_t)d);
         const size_t off_rows = 0;
         const size_t off_err = align_up((size_t)S * sizeof(int32_t));
@@ -2019,23 +2056,8 @@ extern "C" int32_t bsa_route_heads(const void *Q, const void *K, const void *V, 
         std::memcpy(host, r.rows, (size_t)S * sizeof(int32_t));
         float *err_host = (float *)(host + align_up((size_t)S * sizeof(int32_t)));
 
-        RouteArgs a{};
-        a.Q = Q; a.K = K; a.V = V;
-        a.BH = BH;
-        a.L = (int32_t)L;
-        a.HW = r.Hg * r.Wg;
-        a.W = r.Wg;
-        a.anchor = r.anchor_frame;
-        a.radius = r.radius;
-        magic_div((uint32_t)a.HW, &a.magic_HW, &a.shift_HW);
-        magic_div((uint32_t)a.W, &a.magic_W, &a.shift_W);
+        RouteArgs a = route_args(Q, K, V, B, H, L, d, r, nchunk);
         a.rows = (const int32_t *)(dev + off_rows);
-        a.S = S;
-        a.nsb = nsb;
-        a.nkt = nkt;
-        a.nchunk = nchunk;
-        a.tiles_per_chunk = tpc;
-        a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)d));
         a.part = (float *)(dev + off_part);
         a.err_rows = (float *)(dev + off_err);
         const hipStream_t s = (hipStream_t)stream;
@@ -2078,4 +2100,91 @@ extern "C" int32_t bsa_route_heads(const void *Q, const void *K, const void *V, 
     } catch (const std::bad_alloc &) {
         return fail(BSA_ERR_OUT_OF_MEMORY, "host allocation failed");
     }
+}
+
+// ---------------------------------------------------------------------------
+// allocation-free head routing
+// ---------------------------------------------------------------------------
+
+// Scratch of bsa_route_heads_noalloc: a fixed array in each device's memory,
+// held for the life of the process, shared by every call on that device. In
+// host code `scratch` names a host-side stand-in: the array's device address
+// comes from hipGetSymbolAddress (per device) and only that address is used.
+constexpr size_t kRouteScratchBytes = (size_t)32 << 20;  // 32 MiB
+constexpr int32_t kRouteMaxHeads = 1024;                 // B * H
+static __device__ __align__(256) uint8_t scratch[kRouteScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu[kMaxDevices];  // one routing call at a time per device
+void *g_scratch_ptr[kMaxDevices];      // device address of `scratch`, per device (set once)
+
+// The device address of this device's scratch array; called with the device
+// current and g_scratch_mu[device] held.
+hipError_t scratch_address(int device, uint8_t **out)
+{
+    if (!g_scratch_ptr[device]) {
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[device] = ptr;
+    }
+    *out = (uint8_t *)g_scratch_ptr[device];
+    return hipSuccess;
+}
+}  // namespace
+
+extern "C" int32_t bsa_route_heads_noalloc(const void *Q, const void *K, const void *V, int32_t B, int32_t H,
+                                           int64_t L, int32_t d, const bsa_route_desc_t *desc, void *stream,
+                                           uint8_t *head_pattern, double *err)
+{
+    if (int32_t st = check_route_args(Q, K, V, B, H, L, d, desc, head_pattern); st != BSA_OK) return st;
+    const bsa_route_desc_t &r = *desc;
+    if (r.device >= kMaxDevices) return fail(BSA_ERR_INVALID_ARGUMENT, "device %d (at most %d)", r.device, kMaxDevices - 1);
+    if ((int64_t)B * H > kRouteMaxHeads)
+        return fail(BSA_ERR_UNSUPPORTED, "B * H = %lld exceeds the allocation-free limit of %d heads", (long long)B * H,
+                    kRouteMaxHeads);
+    const int32_t BH = B * H, S = r.n_rows, nsb = (S + 31) / 32;
+    // layout of the scratch: rows | per-row errors | per-head sums | partials
+    const size_t off_err = align_up((size_t)S * sizeof(int32_t));
+    const size_t off_sums = off_err + align_up((size_t)BH * S * 2 * sizeof(float));
+    const size_t off_part = off_sums + align_up((size_t)H * 2 * sizeof(double));
+    const size_t chunk_bytes = (size_t)BH * nsb * 3 * (64 + 32 * (size_t)d) * sizeof(float);
+    if (off_part + chunk_bytes > kRouteScratchBytes)
+        return fail(BSA_ERR_UNSUPPORTED, "routing %d heads x %d rows at d = %d needs %zu bytes of scratch, more than the "
+                    "allocation-free limit of %zu", BH, S, d, off_part + chunk_bytes, kRouteScratchBytes);
+    // as many key chunks as the scratch holds (fewer chunks: less parallelism, same result up to rounding)
+    const int32_t nchunk = std::max<int32_t>(
+        1, std::min<int32_t>(route_chunks(BH, S, L), (int32_t)((kRouteScratchBytes - off_part) / chunk_bytes)));
+
+    std::lock_guard<std::mutex> lock(g_scratch_mu[r.device]);
+    DeviceScope ds(r.device);
+    uint8_t *dev = nullptr;
+    hipError_t e = scratch_address(r.device, &dev);
+    if (e != hipSuccess) return fail(BSA_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    RouteArgs a = route_args(Q, K, V, B, H, L, d, r, nchunk);
+    a.rows = (const int32_t *)dev;
+    a.err_rows = (float *)(dev + off_err);
+    a.part = (float *)(dev + off_part);
+    double sums[2 * kRouteMaxHeads];
+    const hipStream_t s = (hipStream_t)stream;
+    // every scratch element the kernels read is written earlier in this call:
+    // nothing needs clearing
+    e = hipMemcpyAsync(dev, r.rows, (size_t)S * sizeof(int32_t), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = launch_route_probe(a, d, s);
+    if (e == hipSuccess) e = launch_route_head_sums(a.err_rows, B, H, S, (double *)(dev + off_sums), s);
+    if (e == hipSuccess) e = hipMemcpyAsync(sums, dev + off_sums, (size_t)H * 2 * sizeof(double), hipMemcpyDeviceToHost, s);
+    const hipError_t es = hipStreamSynchronize(s);  // the scratch and `sums` are free again after this
+    if (e == hipSuccess) e = es;
+    if (e != hipSuccess) return fail(BSA_ERR_HIP, "routing probe: %s", hipGetErrorString(e));
+    const double n = (double)B * S * d;
+    for (int h = 0; h < H; ++h) {
+        const double e_sp = sums[2 * h] / n, e_tp = sums[2 * h + 1] / n;
+        head_pattern[h] = e_sp <= e_tp ? BSA_PAT_SPATIAL : BSA_PAT_TEMPORAL;
+        if (err) {
+            err[2 * h] = e_sp;
+            err[2 * h + 1] = e_tp;
+        }
+    }
+    return BSA_OK;
 }

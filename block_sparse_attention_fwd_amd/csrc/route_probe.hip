@@ -324,7 +324,31 @@ __global__ __launch_bounds__(256) void probe_combine(RouteArgs a)
     }
 }
 
+// One thread per head: the head's squared differences summed over the batch
+// and the sampled rows, sequentially, in fp64.
+__global__ __launch_bounds__(64) void route_head_sums(const float *err_rows, int B, int H, int S, double *sums)
+{
+    const int h = blockIdx.x * 64 + threadIdx.x;
+    if (h >= H) return;
+    double es = 0.0, et = 0.0;
+    for (int b = 0; b < B; ++b)
+        for (int i = 0; i < S; ++i) {
+            const float *er = err_rows + ((size_t)(b * H + h) * S + i) * 2;
+            es += er[0];
+            et += er[1];
+        }
+    sums[2 * h] = es;
+    sums[2 * h + 1] = et;
+}
+
 }  // namespace
+
+hipError_t launch_route_head_sums(const float *err_rows, int32_t B, int32_t H, int32_t S, double *sums,
+                                  hipStream_t stream)
+{
+    hipLaunchKernelGGL(route_head_sums, dim3((unsigned)((H + 63) / 64)), dim3(64), 0, stream, err_rows, B, H, S, sums);
+    return hipGetLastError();
+}
 
 hipError_t launch_route_probe(const RouteArgs &a, int d, hipStream_t stream)
 {

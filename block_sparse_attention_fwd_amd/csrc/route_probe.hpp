@@ -22,4 +22,10 @@ struct RouteArgs {
 
 hipError_t launch_route_probe(const RouteArgs &a, int d, hipStream_t stream);
 
+// Per head h: sums[2 h] and sums[2 h + 1] = the spatial and temporal squared
+// differences of err_rows summed over the batch and the sampled rows, in fp64
+// and in the order b = 0..B-1, i = 0..S-1 (the order the host sums them in).
+hipError_t launch_route_head_sums(const float *err_rows, int32_t B, int32_t H, int32_t S, double *sums,
+                                  hipStream_t stream);
+
 }  // namespace bsa

@@ -357,6 +357,27 @@ typedef struct {
 int32_t bsa_route_heads(const void *Q, const void *K, const void *V, int32_t B, int32_t H, int64_t L, int32_t d,
                         const bsa_route_desc_t *desc, void *stream, uint8_t *head_pattern, double *err);
 
+/*
+ * bsa_route_heads for callers that cannot allocate memory: code under graph
+ * capture, tight serving loops, harnesses that forbid allocation. Same
+ * arguments, checks, errors and results (the per-head sums are formed on the
+ * device in the order bsa_route_heads forms them on the host); it allocates
+ * nothing and creates no event. Its scratch is a fixed 32 MiB array in each
+ * device's memory, held until the process ends and shared by every call on
+ * that device: calls on one device are serialized by a host lock, and work
+ * that touches the array from calls overlapping on one device by any other
+ * means would race. The sampled rows (HOST) are copied to the array and the
+ * per-head sums back with stream-ordered copies; the call waits for `stream`
+ * before it returns. Limits, each an UNSUPPORTED error: B * H <= 1024, and
+ * the rows, the per-row errors (B*H*n_rows*8 bytes) and one key chunk of
+ * partial softmax states (B*H*ceil(n_rows/32)*3*(64 + 32 d)*4 bytes) must fit
+ * the 32 MiB (at d = 128 and 24 heads: up to 832 sampled rows); within the
+ * limit the key range is cut into as many chunks as the array holds.
+ */
+int32_t bsa_route_heads_noalloc(const void *Q, const void *K, const void *V, int32_t B, int32_t H, int64_t L,
+                                int32_t d, const bsa_route_desc_t *desc, void *stream, uint8_t *head_pattern,
+                                double *err);
+
 /* Number of execution regimes compiled in, and their shapes. */
 int32_t bsa_regime_count(void);
 int32_t bsa_regime_info(int32_t regime, bsa_regime_desc_t *out);
