@@ -29,7 +29,7 @@ DTYPE_BF16, DTYPE_F32 = 0, 1
 TILE_FULL, TILE_PARTIAL = 0, 1
 PRED_NONE, PRED_SUBBLOCK, PRED_VIDEO, PRED_LIST = 0, 1, 2, 3
 ORDER_XCD_GROUPED, ORDER_LONGEST_FIRST = 0, 1
-ABI_VERSION = 5  # the structures below mirror this version of bsa.h
+ABI_VERSION = 6  # the structures below mirror this version of bsa.h
 
 EXPORTED = ["bsa_abi_version", "bsa_plan_opts_default", "bsa_plan", "bsa_plan_device", "bsa_forward", "bsa_plan_destroy",
             "bsa_request_create", "bsa_request_submit", "bsa_request_finish", "bsa_request_stats",
@@ -83,7 +83,7 @@ class RouteDesc(ctypes.Structure):
 
 class RegimeDesc(ctypes.Structure):
     _fields_ = [("family", ctypes.c_int32), ("tile_q", ctypes.c_int32), ("tile_k", ctypes.c_int32),
-                ("waves", ctypes.c_int32), ("rows_per_wave", ctypes.c_int32), ("pipelined", ctypes.c_int32)]
+                ("waves", ctypes.c_int32), ("rows_per_wave", ctypes.c_int32)]
 
 
 class TileRecord(ctypes.Structure):
@@ -427,5 +427,5 @@ def regimes():
         d = RegimeDesc()
         _check(L_.bsa_regime_info(r, ctypes.byref(d)))
         out.append({"family": d.family, "tile_q": d.tile_q, "tile_k": d.tile_k, "waves": d.waves,
-                    "rows_per_wave": d.rows_per_wave, "pipelined": d.pipelined})
+                    "rows_per_wave": d.rows_per_wave})
     return out

@@ -47,7 +47,7 @@
 #include "plan_format.hpp"
 
 namespace bsa {
-hipError_t launch_forward(const KernelArgs &a, int waves, int rb, int d, int dtype, hipStream_t stream, bool pipe);
+hipError_t launch_forward(const KernelArgs &a, int waves, int rb, int d, int dtype, hipStream_t stream);
 hipError_t launch_forward_f32(const KernelArgs &a, int waves, int d, hipStream_t stream);
 }
 
@@ -97,17 +97,14 @@ struct Regime {
     int tile_q;  // = 32 * waves * rb
     int waves;   // wavefronts per workgroup
     int rb;      // 32-row query blocks per wave
-    int pipe;    // 1 = software-pipelined tile loop (two key tiles in flight per wave)
 };
 
 static const Regime kRegimes[] = {
-    {0, 128, 4, 1, 0},  // 0: 128 x 64 tiles, 4 waves of 32 rows
-    {0, 64, 2, 1, 0},   // 1: 64 x 64 tiles, 2 waves of 32 rows (d = 128: one LDS buffer, four workgroups per CU)
-    {1, 64, 2, 1, 0},   // 2: 64-query gather tiles (as regime 1)
-    {1, 128, 4, 1, 0},  // 3: 128-query gather tiles
-    {0, 256, 8, 1, 0},  // 4: 256 x 64 tiles, 8 waves of 32 rows
-    {0, 128, 4, 1, 1},  // 5: as regime 0, pipelined tile loop
-    {0, 256, 8, 1, 1},  // 6: as regime 4, pipelined tile loop
+    {0, 128, 4, 1},  // 0: 128 x 64 tiles, 4 waves of 32 rows
+    {0, 64, 2, 1},   // 1: 64 x 64 tiles, 2 waves of 32 rows (d = 128: one LDS buffer, four workgroups per CU)
+    {1, 64, 2, 1},   // 2: 64-query gather tiles (as regime 1)
+    {1, 128, 4, 1},  // 3: 128-query gather tiles
+    {0, 256, 8, 1},  // 4: 256 x 64 tiles, 8 waves of 32 rows
 };
 static const int kNumRegimes = (int)(sizeof kRegimes / sizeof kRegimes[0]);
 
@@ -121,7 +118,6 @@ extern "C" int32_t bsa_regime_info(int32_t r, bsa_regime_desc_t *out)
     out->tile_k = kTileK;
     out->waves = kRegimes[r].waves;
     out->rows_per_wave = 32 * kRegimes[r].rb;
-    out->pipelined = kRegimes[r].pipe;
     return BSA_OK;
 }
 
@@ -1702,7 +1698,7 @@ extern "C" int32_t bsa_forward(bsa_plan_t p, const void *Q, const void *K, const
     if (e == hipSuccess) {
         const Regime &R = kRegimes[p->regime];
         e = p->dtype == BSA_DTYPE_F32 ? launch_forward_f32(a, R.tile_q / 32, p->d, (hipStream_t)stream)
-                                      : launch_forward(a, R.waves, R.rb, p->d, p->dtype, (hipStream_t)stream, R.pipe != 0);
+                                      : launch_forward(a, R.waves, R.rb, p->d, p->dtype, (hipStream_t)stream);
     }
     if (e == hipSuccess) {
         // last_use completes after this forward and after every earlier one:

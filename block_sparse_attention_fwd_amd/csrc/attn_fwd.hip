@@ -119,12 +119,6 @@ __device__ __forceinline__ void copy4_to_lds_s(const void *base, uint32_t off, u
 // stall on the copies).
 __device__ __forceinline__ void wait_copies() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// An empty statement that claims to modify x: computations on x stay after
-// this point in the instruction stream.
-__device__ __forceinline__ void pin(f32x16 &x) { asm volatile("" : "+v"(x)); }
-__device__ __forceinline__ void pin(u32x4 &x) { asm volatile("" : "+v"(x)); }
-__device__ __forceinline__ void pin(float &x) { asm volatile("" : "+v"(x)); }
-
 __device__ __forceinline__ bf16x8 load_bf16x8(const __bf16 *p)
 {
     i32x4 v = *(const i32x4 *)p;
@@ -457,328 +451,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1
     }
 }
 
-// Software-pipelined variant (one 32-row block per wave, contiguous or
-// permuted key tiles, no gather). The pipeline unit is one 32-key half of a
-// 64-key tile, and each wave has two of them in flight: while the matrix
-// cores form the scores of the next half (S = K Q^T), the same wave's vector
-// units exponentiate the current half; while the matrix cores add the current
-// half's P V to the output, the vector units mask, reduce and scale the next
-// half. Neither phase has a data dependence between its matrix and its vector
-// half, so one wave keeps both units busy.
-// LDS: K and V tiles of 64 keys in separate double buffers. Half 1 of tile j
-// reads K(j + 1) (for the scores of tile j + 1's half 0), so K runs one tile
-// ahead of V. Two barriers per tile: M_j between the halves of tile j and E_j
-// after them. After M_j the copy of K(j + 2) is issued (into the buffer K(j)
-// left, last read before M_j); after E_j the copy of V(j + 2) (into the
-// buffer V(j) left). M_j waits for K(j + 1), E_j for V(j + 1) (each waits
-// for every copy the wave has in flight), so a copy has half a tile of
-// compute to land.
-template <int NW, int D>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void bsa_fwd_bf16_pipe(KernelArgs a)
-{
-    using C = Cfg<NW, 1, D>;
-    __shared__ __attribute__((aligned(16))) int kcoord[2][C::BK];                // [K buffer] video key coordinates
-    __shared__ __attribute__((aligned(1024))) unsigned char ksm[2][C::TILEB];   // swizzled K tiles
-    __shared__ __attribute__((aligned(1024))) unsigned char vsm[2][C::TILEB];   // swizzled V tiles
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, hf = lane >> 5, l32 = lane & 31;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const Task tl = a.tasks[blockIdx.x];
-    const Task task{__builtin_amdgcn_readfirstlane(tl.bh), __builtin_amdgcn_readfirstlane(tl.q0),
-                    __builtin_amdgcn_readfirstlane(tl.tb), __builtin_amdgcn_readfirstlane(tl.te)};
-    if (task.bh < 0) return;
-    const int bh = task.bh;
-    const int h = bh % a.H;
-    const uint32_t hflag = (uint32_t)__builtin_amdgcn_readfirstlane((int)a.head_flags[h]);
-    const bool tm = (hflag & kHeadTemporalMajor) != 0;
-    const int pat = (int)((hflag >> kHeadPatShift) & 3u);
-    const int L = a.L;
-    const size_t head_off = (size_t)bh * (size_t)L * D;
-    const __bf16 *Qh = (const __bf16 *)a.Q + head_off;
-    const __bf16 *Kh = (const __bf16 *)a.K + head_off;
-    const __bf16 *Vh = (const __bf16 *)a.V + head_off;
-    __bf16 *Oh = (__bf16 *)a.O + head_off;
-    auto token = [&](int j) __attribute__((always_inline)) -> int { return head_token(j, tm, a); };
-
-    const int q = task.q0 + 32 * w + l32;
-    const bool qvalid = q < L;
-    const int qtok = token(qvalid ? q : L - 1);
-    const int ntile = task.te - task.tb;
-    const bool video = a.mode == kModeVideo;
-
-    bool careful = false;
-    f32x16 oacc[D / 32];
-    float m_ref, l_run;
-    for (;;) {
-#pragma unroll
-    for (int n = 0; n < D / 32; ++n)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[n][r] = 0.f;
-    m_ref = -INFINITY;
-    l_run = 0.f;
-
-    if (ntile > 0) {
-        bf16x8 qreg[D / 16];
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s) qreg[s] = load_bf16x8(Qh + (size_t)qtok * D + 16 * s + 8 * hf);
-        int qt = 0;
-        unsigned qwin = 0;
-        if (video) video_query_coords(qtok, a, qt, qwin);
-
-        const int pos = lane % C::CHUNKS;
-        RecordStream rs;
-        rs.init(a.tiles, task.tb, task.te, lane);
-        const int32_t *ctab = a.coords + (int)((hflag >> kHeadCoordShift) & 3u) * a.coords_stride;
-        uint32_t kgoff[C::INSTS], vgoff[C::INSTS];
-#pragma unroll
-        for (int i = 0; i < C::INSTS; ++i) {
-            const int slot = (w * C::INSTS + i) * C::RPI + lane / C::CHUNKS;
-            kgoff[i] = (uint32_t)(slot * C::ROWB + 16 * (pos ^ swz_k<D>(slot)));
-            vgoff[i] = (uint32_t)(slot * C::ROWB + 16 * (pos ^ swz_v<D>(slot & 3)));
-        }
-        // global -> LDS copies of one tensor of a tile
-        auto fetch = [&](const TileRec r, const __bf16 *X, unsigned char *dst, bool is_k) __attribute__((always_inline)) {
-            const uint32_t xl = (uint32_t)(uintptr_t)dst;
-            if (!tm && r.k0 + C::BK <= L) {
-                const __bf16 *xb = X + (size_t)r.k0 * D;
-#pragma unroll
-                for (int i = 0; i < C::INSTS; ++i)
-                    copy16_to_lds_s(xb, is_k ? kgoff[i] : vgoff[i], __builtin_amdgcn_readfirstlane(xl + (uint32_t)((w * C::INSTS + i) * 1024)));
-            } else {
-                int xtok[C::INSTS];
-#pragma unroll
-                for (int i = 0; i < C::INSTS; ++i) {
-                    const int slot = (w * C::INSTS + i) * C::RPI + lane / C::CHUNKS;
-                    xtok[i] = token(min(r.k0 + slot, L - 1));
-                }
-#pragma unroll
-                for (int i = 0; i < C::INSTS; ++i) {
-                    const int slot = (w * C::INSTS + i) * C::RPI + lane / C::CHUNKS;
-                    const int sw = is_k ? swz_k<D>(slot) : swz_v<D>(slot & 3);
-                    copy16_to_lds(X + (size_t)xtok[i] * D + 8 * (pos ^ sw), __builtin_amdgcn_readfirstlane(xl + (uint32_t)((w * C::INSTS + i) * 1024)));
-                }
-            }
-        };
-        auto fetch_k = [&](const TileRec r, int kb) __attribute__((always_inline)) {
-            fetch(r, Kh, &ksm[kb][0], true);
-            if (video && w == 0)
-                copy4_to_lds_s(ctab + r.k0, 4u * (uint32_t)lane, __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&kcoord[kb][0]));
-        };
-
-        int koff[D / 16];
-#pragma unroll
-        for (int s = 0; s < D / 16; ++s) koff[s] = l32 * C::ROWB + 16 * ((2 * s + hf) ^ swz_k<D>(l32));
-        const int grp = lane >> 4, jl = lane & 15;
-        const int dd_base = 16 * (grp & 1) + 4 * (jl & 3);
-        const int key_sub = jl >> 2;
-        const int sv = swz_v<D>(key_sub);
-        int voff[D / 32];
-#pragma unroll
-        for (int n = 0; n < D / 32; ++n)
-            voff[n] = (4 * hf + key_sub) * C::ROWB + 16 * (((32 * n + dd_base) >> 3) ^ sv) + 2 * (dd_base & 7);
-        const f32x16 zero16 = {};
-        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-
-        // scores of one 32-key half: kt = the K tile + 32 rows for half 1
-        auto scores = [&](const unsigned char *kt, f32x16 &sc) __attribute__((always_inline)) {
-#pragma unroll
-            for (int s = 0; s < D / 16; ++s) {
-                const bf16x8 kv = *LDS_PTR(bf16x8, kt + koff[s]);
-                sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qreg[s], s == 0 ? zero16 : sc, 0, 0, 0);
-            }
-        };
-        // exponentials of a prepared half, rounded to bf16 pairs (two 16-key
-        // operand chunks), and their sum from the same rounded values
-        auto expo = [&](const f32x16 &t, u32x4 (&pk)[2]) {
-#pragma unroll
-            for (int c = 0; c < 2; ++c)
-#pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    const float p0 = __builtin_amdgcn_exp2f(t[8 * c + e]);
-                    const float p1 = __builtin_amdgcn_exp2f(t[8 * c + e + 1]);
-                    const bf16x2 pp = {(__bf16)p0, (__bf16)p1};
-                    l_run = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, l_run, false);
-                    pk[c][e / 2] = __builtin_bit_cast(unsigned, pp);
-                }
-        };
-        // O^T += V^T P^T over one half: vt = the V tile + 32 rows for half 1
-        auto pv = [&](const unsigned char *vt, const u32x4 (&pk)[2]) {
-#pragma unroll
-            for (int c = 0; c < 2; ++c)
-#pragma unroll
-                for (int n = 0; n < D / 32; ++n) {
-                    const unsigned char *pa = vt + voff[n] + 16 * c * C::ROWB;
-                    const unsigned char *pb = pa + 8 * C::ROWB;
-                    const s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, pa));
-                    const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s16x4, pb));
-                    const bf16x4 a4 = __builtin_bit_cast(bf16x4, va), b4 = __builtin_bit_cast(bf16x4, vb);
-                    const bf16x8 vop = {a4[0], a4[1], a4[2], a4[3], b4[0], b4[1], b4[2], b4[3]};
-                    oacc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, __builtin_bit_cast(bf16x8, pk[c]), oacc[n], 0, 0, 0);
-                }
-        };
-        // exact mask of a PARTIAL tile's half (FULL tiles: nothing)
-        auto mask = [&](const TileRec rec, int half, int kb, f32x16 &t) __attribute__((always_inline)) {
-            if (wave_masks_tile(a, rec.aux, w))
-                mask_partial_half(t, half, a, rec.k0, rec.aux, video, pat, LDS_PTR(const int, &kcoord[kb][4 * hf]), qt, qwin, 32 * w, hf);
-        };
-        // reference update from a half's scores (only while some row of the
-        // wave has none, or in careful mode); returns the factor the output
-        // and the row sum take once the previous half's products are in
-        auto reference = [&](const f32x16 &t) __attribute__((always_inline)) -> float {
-            float alpha = 1.0f;
-            if (careful || __builtin_amdgcn_ballot_w64(m_ref == -INFINITY)) {
-                float mx = fmaxf(t[0], t[1]);
-#pragma unroll
-                for (int r = 2; r < 16; r += 2) mx = max3f(mx, t[r], t[r + 1]);
-                mx = swap_halves_max(mx) * a.scale_log2;
-                const bool need = mx > m_ref + kSlack;
-                alpha = need ? __builtin_amdgcn_exp2f(m_ref - mx) : 1.0f;
-                m_ref = need ? mx : m_ref;
-            }
-            return alpha;
-        };
-        // t = s * c - m
-        auto scale = [&](f32x16 &t) __attribute__((always_inline)) {
-            const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) t[r] = fmaf(t[r], a.scale_log2, -m_use);
-        };
-        auto rescale = [&](float alpha) __attribute__((always_inline)) {
-            if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
-                l_run *= alpha;
-#pragma unroll
-                for (int n = 0; n < D / 32; ++n)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) oacc[n][r] *= alpha;
-            }
-        };
-        // one pipeline step: scores of the next half (K tile kn, rows of half
-        // nh; absent when `more` is false) under the exponentials of the
-        // current half (in t_cur); the current half's P V (V tile vc, half ch)
-        // under the mask, reference and scaling of the next half (into t_nxt)
-        auto half_step = [&](const unsigned char *kn, int nh, int kbn, const TileRec rec_nx, bool more,
-                             const unsigned char *vc, int ch, f32x16 &t_cur, f32x16 &t_nxt) __attribute__((always_inline)) {
-            u32x4 pk[2];
-            if (more) {
-                __builtin_amdgcn_sched_barrier(0);
-                pin(t_cur);
-                scores(kn + 32 * nh * C::ROWB, t_nxt);
-                expo(t_cur, pk);
-                // K operand reads run two MFMAs ahead; each MFMA carries its
-                // share of the exponentials and the conversions / sums
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-                for (int i = 0; i < D / 16; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    if (i + 2 < D / 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x400, 16 / (D / 16), 0);
-                    __builtin_amdgcn_sched_group_barrier(0x002, 16 / (D / 16), 0);
-                }
-                pin(pk[0]);
-                pin(pk[1]);
-                pin(l_run);
-                __builtin_amdgcn_sched_barrier(0);
-                mask(rec_nx, nh, kbn, t_nxt);
-                const float alpha = reference(t_nxt);
-                __builtin_amdgcn_sched_barrier(0);
-                pin(t_nxt);
-                pv(vc + 32 * ch * C::ROWB, pk);
-                scale(t_nxt);
-                // V operand reads (two per MFMA) run one MFMA ahead; each MFMA
-                // carries its share of the scaling
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-#pragma unroll
-                for (int i = 0; i < 2 * (D / 32); ++i) {
-                    if (i + 1 < 2 * (D / 32)) __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-                    __builtin_amdgcn_sched_group_barrier(0x002, 16 / (2 * (D / 32)), 1);
-                }
-                pin(t_nxt);
-                __builtin_amdgcn_sched_barrier(0);
-                rescale(alpha);
-            } else {
-                expo(t_cur, pk);
-                pv(vc + 32 * ch * C::ROWB, pk);
-            }
-        };
-
-        // prologue: K(0), V(0) and K(1), V(1) copied; scores of tile 0's half 0
-        // prepared
-        f32x16 ta, tb;  // prepared scores of the current / next half, alternating
-        TileRec rec_c = rs.get(0);
-        TileRec rec_n = rec_c;
-        fetch_k(rec_c, 0);
-        fetch(rec_c, Vh, &vsm[0][0], false);
-        if (ntile > 1) {
-            rec_n = rs.get(1);
-            fetch_k(rec_n, 1);
-            fetch(rec_n, Vh, &vsm[1][0], false);
-        }
-        wait_copies();
-        __syncthreads();
-        scores(&ksm[0][0], ta);
-        mask(rec_c, 0, 0, ta);
-        rescale(reference(ta));
-        scale(ta);
-
-        // tile j (parity cb): half 0 with ta current, half 1 with tb current
-        auto tile = [&](const int j, auto par) __attribute__((always_inline)) {
-            constexpr int cb = decltype(par)::value;  // j & 1
-            constexpr int nb = cb ^ 1;
-            if ((j & 63) == 0 && j > 0) rs.advance();
-            const bool more = j + 1 < ntile;
-            // half 0: scores of tile j's half 1 from K(j)
-            half_step(&ksm[cb][0], 1, cb, rec_c, true, &vsm[cb][0], 0, ta, tb);
-            // M_j: K(j + 1) has landed; K(j)'s buffer takes K(j + 2). Every
-            // copy is awaited (vmcnt(0)), not just the older tensor's: a count
-            // that leaves the newest copies in flight would rely on the
-            // direct-to-LDS loads, and the loads and spill reloads the compiler
-            // places between them, completing in issue order.
-            wait_copies();
-            __syncthreads();
-            TileRec rec_2 = rec_n;
-            if (j + 2 < ntile) {
-                rec_2 = rs.get(j + 2);
-                fetch_k(rec_2, cb);
-            }
-            // half 1: scores of tile j + 1's half 0 from K(j + 1)
-            half_step(&ksm[nb][0], 0, nb, rec_n, more, &vsm[cb][0], 1, tb, ta);
-            // E_j: V(j + 1) has landed; V(j)'s buffer takes V(j + 2)
-            wait_copies();
-            __syncthreads();
-            if (j + 2 < ntile) fetch(rec_2, Vh, &vsm[cb][0], false);
-            rec_c = rec_n;
-            rec_n = rec_2;
-        };
-        int j = 0;
-        for (; j + 1 < ntile; j += 2) {
-            tile(j, IntC<0>{});
-            tile(j + 1, IntC<1>{});
-        }
-        if (j < ntile) tile(j, IntC<0>{});
-        wait_copies();
-    }
-    if (careful || !__syncthreads_or(!(l_run <= 0x1p64f))) break;
-    careful = true;
-    }
-
-    const float l_tot = swap_halves_sum(l_run);
-    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-    if (qvalid) {
-        __bf16 *orow = Oh + (size_t)qtok * D;
-#pragma unroll
-        for (int n = 0; n < D / 32; ++n)
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int dd = 32 * n + 8 * rr + 4 * hf;
-                const bf16x4 o4 = {(__bf16)(oacc[n][4 * rr] * inv), (__bf16)(oacc[n][4 * rr + 1] * inv),
-                                   (__bf16)(oacc[n][4 * rr + 2] * inv), (__bf16)(oacc[n][4 * rr + 3] * inv)};
-                *(bf16x4 *)(orow + dd) = o4;
-            }
-    }
-}
-
 template <int NW, int RB, int D, int NB = 2>
 static hipError_t launch(const KernelArgs &a, hipStream_t stream)
 {
@@ -786,24 +458,9 @@ static hipError_t launch(const KernelArgs &a, hipStream_t stream)
     return hipGetLastError();
 }
 
-template <int NW, int D>
-static hipError_t launch_pipe(const KernelArgs &a, hipStream_t stream)
-{
-    hipLaunchKernelGGL((bsa_fwd_bf16_pipe<NW, D>), dim3(a.ntasks), dim3(NW * 64), 0, stream, a);
-    return hipGetLastError();
-}
-
-hipError_t launch_forward(const KernelArgs &a, int waves, int rb, int d, int dtype, hipStream_t stream, bool pipe)
+hipError_t launch_forward(const KernelArgs &a, int waves, int rb, int d, int dtype, hipStream_t stream)
 {
     if (dtype != 0) return hipErrorInvalidValue;
-    if (pipe) {
-        if (a.mode == kModeGather || rb != 1) return hipErrorInvalidValue;
-        if (waves == 4 && d == 128) return launch_pipe<4, 128>(a, stream);
-        if (waves == 4 && d == 64) return launch_pipe<4, 64>(a, stream);
-        if (waves == 8 && d == 128) return launch_pipe<8, 128>(a, stream);
-        if (waves == 8 && d == 64) return launch_pipe<8, 64>(a, stream);
-        return hipErrorInvalidValue;
-    }
     if (rb == 1) {
         if (waves == 8 && d == 128) return launch<8, 1, 128>(a, stream);
         if (waves == 8 && d == 64) return launch<8, 1, 64>(a, stream);

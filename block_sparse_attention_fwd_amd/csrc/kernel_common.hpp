@@ -252,44 +252,4 @@ __device__ __forceinline__ void mask_partial_tile(f32x16 (&s0)[RB], f32x16 (&s1)
     }
 }
 
-// The same predicate on one 32-key half of a PARTIAL tile (half 0: keys
-// 0..31, half 1: keys 32..63), for a wave with one 32-row block.
-__device__ __forceinline__ void mask_partial_half(f32x16 &s, int half, const KernelArgs &a, int rec_k0, uint32_t rec_aux,
-                                                  bool video, int pat, const __attribute__((address_space(3))) int *kc,
-                                                  int qt, unsigned qwin, int wrow0, int hf)
-{
-    if (video) {
-        const unsigned win2 = 2u * (unsigned)a.radius;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const i32x4 c = *(const __attribute__((address_space(3))) i32x4 *)(kc + 32 * half + 8 * g);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                bool keep;
-                if (pat == 1) {
-                    keep = c[e] == qt || c[e] == a.anchor;
-                } else if (pat == 2) {
-                    const unsigned dd = (unsigned)c[e] - qwin;
-                    keep = max(dd & 0xffffu, dd >> 16) <= win2;
-                } else {
-                    keep = c[e] != kNoKey;
-                }
-                s[4 * g + e] = keep ? s[4 * g + e] : -INFINITY;
-            }
-        }
-        return;
-    }
-    const int kmax = (a.mode == kModeBlock ? a.L - rec_k0 : (int)(rec_aux & kAuxMask)) - 32 * half;
-    uint32_t v = ~0u;  // slots >= kmax: past the sequence / list end
-    if (kmax < 32) v = (1u << max(kmax, 0)) - 1u;
-    if (a.mode == kModeBlock) {
-        const int sq = wrow0 >> a.bq_shift;
-        const uint32_t rowbits = rec_aux >> (sq * a.nsk);
-        v &= ((rowbits >> (half * (a.nsk - 1))) & 1u) ? ~0u : 0u;
-    }
-    v >>= 4 * hf;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = ((v >> (8 * (r / 4) + (r % 4))) & 1u) ? s[r] : -INFINITY;
-}
-
 }  // namespace bsa

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define BSA_ABI_VERSION 5
+#define BSA_ABI_VERSION 6
 
 typedef struct bsa_plan_s *bsa_plan_t;
 
@@ -165,10 +165,7 @@ typedef struct {
     int32_t family;                /* 0 = contiguous/permuted tiles, 1 = gather    */
     int32_t tile_q, tile_k;
     int32_t waves;                 /* wavefronts per workgroup                     */
-    int32_t rows_per_wave;         /* query rows each wavefront owns (32 or 64)    */
-    int32_t pipelined;             /* 1: each wavefront keeps two 32-key halves in
-                                      flight (scores of the next half on the matrix
-                                      cores under the softmax of the current one) */
+    int32_t rows_per_wave;         /* query rows each wavefront owns (32)          */
 } bsa_regime_desc_t;
 
 /* One physical tile of a plan, as computed by the device (test hook for

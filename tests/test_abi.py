@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     L = bsa.lib()
-    assert L.bsa_abi_version() == bsa.ABI_VERSION == 5
+    assert L.bsa_abi_version() == bsa.ABI_VERSION == 6
     assert L.bsa_status_str(bsa.ERR_INVALID_MASK) == b"BSA_ERR_INVALID_MASK"
     assert L.bsa_status_str(99) == b"BSA_ERR_UNKNOWN"
     assert len(bsa.regimes()) == L.bsa_regime_count() >= 3
