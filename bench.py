@@ -286,8 +286,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-rows-per-head", type=int, default=500,
-                    help="oracle rows per head for the CPU baseline (about 10-20 s of CPU work by default)")
+    ap.add_argument("--cpu-rows-per-head", type=int, default=2000,
+                    help="oracle rows per head for the CPU baseline (about 10-15 s on 16 host threads by default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--no-classes", action="store_true", help="skip the per-class records")
