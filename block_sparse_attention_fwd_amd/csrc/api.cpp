@@ -47,7 +47,7 @@
 #include "plan_format.hpp"
 
 namespace bsa {
-hipError_t launch_forward(const KernelArgs &a, int waves, int rb, int d, int dtype, hipStream_t stream);
+hipError_t launch_forward(const KernelArgs &a, int waves, int rb, int d, int dtype, int nbuf, hipStream_t stream);
 hipError_t launch_forward_f32(const KernelArgs &a, int waves, int d, hipStream_t stream);
 }
 
@@ -97,14 +97,15 @@ struct Regime {
     int tile_q;  // = 32 * waves * rb
     int waves;   // wavefronts per workgroup
     int rb;      // 32-row query blocks per wave
+    int nbuf;    // LDS key/value buffers: 3 = two tiles in flight (0 = the kernel's default: 2, or 1 for two waves at d = 128)
 };
 
 static const Regime kRegimes[] = {
-    {0, 128, 4, 1},  // 0: 128 x 64 tiles, 4 waves of 32 rows
-    {0, 64, 2, 1},   // 1: 64 x 64 tiles, 2 waves of 32 rows (d = 128: one LDS buffer, four workgroups per CU)
-    {1, 64, 2, 1},   // 2: 64-query gather tiles (as regime 1)
-    {1, 128, 4, 1},  // 3: 128-query gather tiles
-    {0, 256, 8, 1},  // 4: 256 x 64 tiles, 8 waves of 32 rows
+    {0, 128, 4, 1, 0},  // 0: 128 x 64 tiles, 4 waves of 32 rows
+    {0, 64, 2, 1, 0},   // 1: 64 x 64 tiles, 2 waves of 32 rows (d = 128: one LDS buffer, four workgroups per CU)
+    {1, 64, 2, 1, 0},   // 2: 64-query gather tiles (as regime 1)
+    {1, 128, 4, 1, 0},  // 3: 128-query gather tiles
+    {0, 256, 8, 1, 3},  // 4: 256 x 64 tiles, 8 waves of 32 rows, three LDS buffers (copies two tiles ahead)
 };
 static const int kNumRegimes = (int)(sizeof kRegimes / sizeof kRegimes[0]);
 
@@ -1698,7 +1699,7 @@ extern "C" int32_t bsa_forward(bsa_plan_t p, const void *Q, const void *K, const
     if (e == hipSuccess) {
         const Regime &R = kRegimes[p->regime];
         e = p->dtype == BSA_DTYPE_F32 ? launch_forward_f32(a, R.tile_q / 32, p->d, (hipStream_t)stream)
-                                      : launch_forward(a, R.waves, R.rb, p->d, p->dtype, (hipStream_t)stream);
+                                      : launch_forward(a, R.waves, R.rb, p->d, p->dtype, R.nbuf, (hipStream_t)stream);
     }
     if (e == hipSuccess) {
         // last_use completes after this forward and after every earlier one:

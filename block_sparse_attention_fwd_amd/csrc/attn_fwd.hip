@@ -134,7 +134,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1
     using C = Cfg<NW, RB, D>;
     // NB = 2: tile j + 1 lands in the other buffer while tile j is computed;
     // NB = 1: one buffer, filled after each tile (other workgroups on the CU
-    // cover the copy), so that twice as many workgroups fit in LDS
+    // cover the copy), so that twice as many workgroups fit in LDS;
+    // NB = 3: tile j + 2 is issued while tile j is computed, so a copy has two
+    // tiles of compute to land. The two halves of the workgroup copy
+    // alternate tiles (waves 0..NW/2-1 the even ones), so that each wave only
+    // ever waits for all of its own copies: the half that issued tile j + 1
+    // waits at the end of tile j, while the other half's tile j + 2 stays in
+    // flight.
+    static_assert(NB != 3 || NW >= 4, "three buffers need two copy groups");
+    constexpr int CW = NB == 3 ? NW / 2 : NW;       // waves that copy one tile
+    constexpr int CI = C::BK / C::RPI / CW;          // copies per copying wave per tensor
     __shared__ __attribute__((aligned(16))) int kcoord[NB][C::BK];  // [buffer] video key coordinates
     __shared__ __attribute__((aligned(1024))) unsigned char ksm[NB][C::TILEB];  // [buffer] swizzled K tile
     __shared__ __attribute__((aligned(1024))) unsigned char vsm[NB][C::TILEB];  // [buffer] swizzled V tile
@@ -213,9 +222,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1
             if (video) video_query_coords(qtok[rb], a, qt[rb], qwin[rb]);
         }
 
-        // rows this lane copies for each tile: slot = (w*INSTS + i)*RPI + lane/CHUNKS
+        // rows this lane copies for each tile: slot = (wc*CI + i)*RPI + lane/CHUNKS,
+        // wc = the wave's index among the waves that copy the tile
         const int pos = lane % C::CHUNKS;
-        int idx_nxt[C::INSTS];  // gathered logical key positions of the next tile to fetch
+        const int wc = w % CW;
+        const bool odd_copier = w >= CW;  // NB = 3: this wave copies the odd tiles
+        int idx_nxt[CI];  // gathered logical key positions of the next tile to fetch
 
         RecordStream rs;
         rs.init(a.tiles, task.tb, task.te, lane);
@@ -223,8 +235,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1
         auto load_indices = [&](const TileRec r, int *dst) {
             const int cnt = (int)(r.aux & kAuxMask);
 #pragma unroll
-            for (int i = 0; i < C::INSTS; ++i) {
-                int slot = (w * C::INSTS + i) * C::RPI + lane / C::CHUNKS;
+            for (int i = 0; i < CI; ++i) {
+                int slot = (wc * CI + i) * C::RPI + lane / C::CHUNKS;
                 dst[i] = a.gidx[r.k0 + (slot < cnt ? slot : cnt - 1)];
             }
         };
@@ -233,10 +245,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1
         // computed), the video key coordinates included
         const int32_t *ctab = a.coords + (int)((hflag >> kHeadCoordShift) & 3u) * a.coords_stride;
         // per-lane byte offsets of the copied chunks within a contiguous tile
-        uint32_t kgoff[C::INSTS], vgoff[C::INSTS];
+        uint32_t kgoff[CI], vgoff[CI];
 #pragma unroll
-        for (int i = 0; i < C::INSTS; ++i) {
-            const int slot = (w * C::INSTS + i) * C::RPI + lane / C::CHUNKS;
+        for (int i = 0; i < CI; ++i) {
+            const int slot = (wc * CI + i) * C::RPI + lane / C::CHUNKS;
             kgoff[i] = (uint32_t)(slot * C::ROWB + 16 * (pos ^ swz_k<D>(slot)));
             vgoff[i] = (uint32_t)(slot * C::ROWB + 16 * (pos ^ swz_v<D>(slot & 3)));
         }
@@ -246,29 +258,29 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1
                 // 64 consecutive rows: scalar base + loop-invariant lane offsets
                 const __bf16 *kb = Kh + (size_t)r.k0 * D, *vb = Vh + (size_t)r.k0 * D;
 #pragma unroll
-                for (int i = 0; i < C::INSTS; ++i) {
-                    const uint32_t off = (uint32_t)((w * C::INSTS + i) * 1024);
+                for (int i = 0; i < CI; ++i) {
+                    const uint32_t off = (uint32_t)((wc * CI + i) * 1024);
                     copy16_to_lds_s(kb, kgoff[i], __builtin_amdgcn_readfirstlane(kl + off));
                     copy16_to_lds_s(vb, vgoff[i], __builtin_amdgcn_readfirstlane(vl + off));
                 }
             } else {
                 // listed rows (gather) or rows of a temporal-major head: one
                 // address per lane, all computed before the copies are issued
-                int ktok[C::INSTS];
+                int ktok[CI];
 #pragma unroll
-                for (int i = 0; i < C::INSTS; ++i) {
-                    const int slot = (w * C::INSTS + i) * C::RPI + lane / C::CHUNKS;
+                for (int i = 0; i < CI; ++i) {
+                    const int slot = (wc * CI + i) * C::RPI + lane / C::CHUNKS;
                     ktok[i] = token(gather ? idx[i] : min(r.k0 + slot, L - 1));
                 }
 #pragma unroll
-                for (int i = 0; i < C::INSTS; ++i) {
-                    const int slot = (w * C::INSTS + i) * C::RPI + lane / C::CHUNKS;
-                    const uint32_t off = (uint32_t)((w * C::INSTS + i) * 1024);
+                for (int i = 0; i < CI; ++i) {
+                    const int slot = (wc * CI + i) * C::RPI + lane / C::CHUNKS;
+                    const uint32_t off = (uint32_t)((wc * CI + i) * 1024);
                     copy16_to_lds(Kh + (size_t)ktok[i] * D + 8 * (pos ^ swz_k<D>(slot)), __builtin_amdgcn_readfirstlane(kl + off));
                     copy16_to_lds(Vh + (size_t)ktok[i] * D + 8 * (pos ^ swz_v<D>(slot & 3)), __builtin_amdgcn_readfirstlane(vl + off));
                 }
             }
-            if (video && w == 0) {
+            if (video && wc == 0) {
                 // the tile's 64 key-coordinate words, copied from the head's
                 // table in the plan (frame, or (y << 16) | x; kNoKey past the end)
                 copy4_to_lds_s(ctab + r.k0, 4u * (uint32_t)lane, __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)&kcoord[buf][0]));
@@ -277,11 +289,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1
         // publish a fetched tile: its copies have landed
         auto finish_tile = [&](int) { wait_copies(); };
 
-        // prologue: tile 0 into buffer 0
-        if (gather) load_indices(rs.get(0), idx_nxt);
-        fetch_tile(rs.get(0), idx_nxt, 0);
-        if (gather && ntile > 1) load_indices(rs.get(1), idx_nxt);
-        finish_tile(0);
+        // prologue: tile 0 into buffer 0 (NB = 3: and tile 1 into buffer 1, by
+        // the odd half, which waits for it at the end of tile 0)
+        if constexpr (NB == 3) {
+            if (!odd_copier) {
+                fetch_tile(rs.get(0), idx_nxt, 0);
+                finish_tile(0);
+            } else if (ntile > 1) {
+                fetch_tile(rs.get(1), idx_nxt, 1);
+            }
+        } else {
+            if (gather) load_indices(rs.get(0), idx_nxt);
+            fetch_tile(rs.get(0), idx_nxt, 0);
+            if (gather && ntile > 1) load_indices(rs.get(1), idx_nxt);
+            finish_tile(0);
+        }
         __syncthreads();
 
         // per-lane LDS read offsets (loop-invariant; tile-relative parts are immediates)
@@ -299,7 +321,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1
         const f32x16 zero16 = {};
 
         // one key tile; the LDS buffer index is a compile-time constant (the loop
-        // below is unrolled by two), so every LDS operand address is a
+        // below is unrolled by NB), so every LDS operand address is a
         // loop-invariant register plus an immediate offset
         auto tile_step = [&](const int j, auto cur_c) {
             constexpr int cur = NB == 1 ? 0 : decltype(cur_c)::value;
@@ -310,6 +332,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1
                 fetch_tile(rs.get(j + 1), idx_nxt, cur ^ 1);
                 if (gather && j + 2 < ntile) load_indices(rs.get(j + 2), idx_nxt);
             }
+            // NB = 3: tile j + 2 goes to the buffer tile j - 1 left (its reads
+            // ended before the barrier that closed tile j - 1); the half that
+            // copies it is the one that copied tile j, whose copies have landed
+            if (NB == 3 && j + 2 < ntile && odd_copier == ((j & 1) != 0))
+                fetch_tile(rs.get(j + 2), idx_nxt, (cur + 2) % 3);
 
             // A PARTIAL tile may keep no pair of this wave's rows: the wave
             // skips it (and still takes its part in the copies and barriers)
@@ -407,6 +434,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1
             if constexpr (NB == 2) {
                 if (more) finish_tile(cur ^ 1);
                 __syncthreads();
+            } else if constexpr (NB == 3) {
+                // tile j + 1 has landed: its copying half waits for its copies
+                if (more && odd_copier == (((j + 1) & 1) != 0)) finish_tile(0);
+                __syncthreads();
             } else {
                 __syncthreads();  // every wave is done with the buffer
                 if (more) {
@@ -418,11 +449,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1
             }
         };
         int j = 0;
-        for (; j + 1 < ntile; j += 2) {
-            tile_step(j, IntC<0>{});
-            tile_step(j + 1, IntC<1>{});
+        if constexpr (NB == 3) {
+            for (; j + 2 < ntile; j += 3) {
+                tile_step(j, IntC<0>{});
+                tile_step(j + 1, IntC<1>{});
+                tile_step(j + 2, IntC<2>{});
+            }
+            if (j < ntile) tile_step(j, IntC<0>{});
+            if (j + 1 < ntile) tile_step(j + 1, IntC<1>{});
+        } else {
+            for (; j + 1 < ntile; j += 2) {
+                tile_step(j, IntC<0>{});
+                tile_step(j + 1, IntC<1>{});
+            }
+            if (j < ntile) tile_step(j, IntC<0>{});
         }
-        if (j < ntile) tile_step(j, IntC<0>{});
     }
     bool bad = false;
 #pragma unroll
@@ -458,12 +499,18 @@ static hipError_t launch(const KernelArgs &a, hipStream_t stream)
     return hipGetLastError();
 }
 
-hipError_t launch_forward(const KernelArgs &a, int waves, int rb, int d, int dtype, hipStream_t stream)
+hipError_t launch_forward(const KernelArgs &a, int waves, int rb, int d, int dtype, int nbuf, hipStream_t stream)
 {
     if (dtype != 0) return hipErrorInvalidValue;
+    if (nbuf == 3) {
+        // contiguous / permuted key tiles only (the gather regimes keep their
+        // own buffering)
+        if (a.mode == kModeGather || rb != 1) return hipErrorInvalidValue;
+        if (waves == 8 && d == 128) return launch<8, 1, 128, 3>(a, stream);
+        if (waves == 8 && d == 64) return launch<8, 1, 64, 3>(a, stream);
+        return hipErrorInvalidValue;
+    }
     if (rb == 1) {
-        if (waves == 8 && d == 128) return launch<8, 1, 128>(a, stream);
-        if (waves == 8 && d == 64) return launch<8, 1, 64>(a, stream);
         if (waves == 4 && d == 128) return launch<4, 1, 128>(a, stream);
         if (waves == 4 && d == 64) return launch<4, 1, 64>(a, stream);
         // two waves, d = 128: single-buffered, so that four workgroups (two
