@@ -203,7 +203,8 @@ struct bsa_plan_s {
     uint8_t *img = nullptr;
     size_t img_cap = 0, img_bytes = 0;
     bool img_pinned = false;
-    std::vector<uint8_t> img_vec;
+    std::unique_ptr<uint8_t[]> img_host;  // the image of a host-only plan, or a device plan read back (not zero-filled)
+    size_t img_host_n = 0;
     size_t off_tasks = 0, off_tiles = 0, off_gidx = 0, off_flags = 0, off_coords = 0;
     int64_t coord_stride = 0;                   // words per video key-coordinate table
     std::vector<uint8_t> head_coord_table;      // per head: index of its table
@@ -534,45 +535,88 @@ static void map_block_head(const bsa_plan_s &p, const bsa_mask_desc_t &m, int b,
     const int nsq = BQ / bqe, nsk = kTileK / bke;
     const int64_t bh = (int64_t)b * p.H + h;
     const int64_t words = (nkb + 63) / 64, twords = (nkt + 63) / 64;
-    std::vector<uint64_t> rowbuf((size_t)words);
-    std::vector<uint32_t> acc((size_t)nkt, 0u);
-    std::vector<uint64_t> touched((size_t)twords, 0u);
+    // key blocks of at most one tile (block_k <= 64): the key tiles are read
+    // straight off the rows' bit words, one word (64 or 32 key tiles) at a
+    // time; larger key blocks (split over several tiles) go through a per-tile
+    // accumulator
+    const bool word_path = p.block_k <= kTileK;
+    std::vector<uint64_t> rowbuf((size_t)words * (word_path ? nsq : 1));
+    std::vector<uint32_t> acc(word_path ? 0 : (size_t)nkt, 0u);
+    std::vector<uint64_t> touched(word_path ? 0 : (size_t)twords, 0u);
     out.tasks.reserve((size_t)(tq_hi - tq_lo));
     for (int64_t tq = tq_lo; tq < tq_hi; ++tq) {
         const int64_t q0 = tq * BQ, q1 = std::min<int64_t>(q0 + BQ, L);
         const int64_t qb0 = q0 / p.block_q, qb1 = (q1 - 1) / p.block_q;
-        for (int64_t qb = qb0; qb <= qb1; ++qb) {
-            const int sq = qb * p.block_q <= q0 ? 0 : (int)((qb * p.block_q - q0) / bqe);
-            const uint64_t *row = block_row_bits(m, bh, qb, nqb, nkb, rowbuf.data());
-            for (int64_t w = 0; w < words; ++w)
-                for (uint64_t x = row[w]; x; x &= x - 1) {
-                    const int64_t kb = w * 64 + __builtin_ctzll(x);
-                    const int64_t k_lo = kb * p.block_k, k_hi = std::min<int64_t>(k_lo + p.block_k, L) - 1;
-                    for (int64_t tk = k_lo / kTileK; tk <= k_hi / kTileK; ++tk) {
-                        const int sk = p.block_k <= kTileK ? (int)((k_lo - tk * kTileK) / bke) : 0;
-                        acc[tk] |= 1u << (sq * nsk + sk);
-                        touched[tk >> 6] |= 1ull << (tk & 63);
-                    }
-                }
-        }
         const int nsq_valid = (int)std::min<int64_t>(nsq, (q1 - 1 - q0) / bqe + 1);
         Task t{(int32_t)bh, (int32_t)q0, (int32_t)out.tiles.size(), 0};
         int64_t n_tiles = 0;
-        for (int64_t tw = 0; tw < twords; ++tw) {
-            for (uint64_t x = touched[tw]; x; x &= x - 1) {
-                const int64_t tk = tw * 64 + __builtin_ctzll(x);
-                const int64_t k0 = tk * kTileK, k1 = std::min<int64_t>(k0 + kTileK, L);
-                const int nsk_valid = (int)std::min<int64_t>(nsk, (k1 - 1 - k0) / bke + 1);
-                uint32_t want = 0;
-                for (int sq = 0; sq < nsq_valid; ++sq)
-                    for (int sk = 0; sk < nsk_valid; ++sk) want |= 1u << (sq * nsk + sk);
-                const bool full = (acc[tk] & want) == want && k0 + kTileK <= L;
-                out.tiles.push_back({(int32_t)k0, acc[tk] | (full ? 0u : kPartial)});
-                if (full) ++out.full; else ++out.part;
-                acc[tk] = 0u;
-                ++n_tiles;
+        // a tile whose rows and keys all exist is FULL when every one of its
+        // sub-blocks is kept; a cropped last key tile is always PARTIAL
+        uint32_t want_full = 0;
+        for (int sq = 0; sq < nsq_valid; ++sq)
+            for (int sk = 0; sk < nsk; ++sk) want_full |= 1u << (sq * nsk + sk);
+        auto emit = [&](int64_t tk, uint32_t bits) {
+            const int64_t k0 = tk * kTileK;
+            const bool full = k0 + kTileK <= L && (bits & want_full) == want_full;
+            out.tiles.push_back({(int32_t)k0, bits | (full ? 0u : kPartial)});
+            if (full) ++out.full; else ++out.part;
+            ++n_tiles;
+        };
+        if (word_path) {
+            // the logical rows of the tile (sub-row sq of each) as bit words
+            const uint64_t *rows[32];
+            int sqs[32];
+            int nr = 0;
+            for (int64_t qb = qb0; qb <= qb1; ++qb, ++nr) {
+                sqs[nr] = qb * p.block_q <= q0 ? 0 : (int)((qb * p.block_q - q0) / bqe);
+                rows[nr] = block_row_bits(m, bh, qb, nqb, nkb, rowbuf.data() + (size_t)nr * words);
             }
-            touched[tw] = 0u;
+            for (int64_t w = 0; w < words; ++w) {
+                uint64_t o = 0;
+                for (int r = 0; r < nr; ++r) o |= rows[r][w];
+                if (!o) continue;
+                if (nsk == 1) {
+                    // bit j of word w: key block = key tile 64 w + j
+                    for (uint64_t x = o; x; x &= x - 1) {
+                        const int j = __builtin_ctzll(x);
+                        uint32_t bits = 0;
+                        for (int r = 0; r < nr; ++r) bits |= (uint32_t)((rows[r][w] >> j) & 1u) << sqs[r];
+                        emit(w * 64 + j, bits);
+                    }
+                } else {
+                    // bits j, j + 1 (j even) of word w: the two 32-key blocks of
+                    // key tile 32 w + j / 2
+                    for (uint64_t x = (o | (o >> 1)) & 0x5555555555555555ull; x; x &= x - 1) {
+                        const int j = __builtin_ctzll(x);
+                        uint32_t bits = 0;
+                        for (int r = 0; r < nr; ++r) bits |= (uint32_t)((rows[r][w] >> j) & 3u) << (2 * sqs[r]);
+                        emit(w * 32 + j / 2, bits);
+                    }
+                }
+            }
+        } else {
+            for (int64_t qb = qb0; qb <= qb1; ++qb) {
+                const int sq = qb * p.block_q <= q0 ? 0 : (int)((qb * p.block_q - q0) / bqe);
+                const uint64_t *row = block_row_bits(m, bh, qb, nqb, nkb, rowbuf.data());
+                // a key block spans block_k / 64 tiles (the last one cropped at L)
+                for (int64_t w = 0; w < words; ++w)
+                    for (uint64_t x = row[w]; x; x &= x - 1) {
+                        const int64_t kb = w * 64 + __builtin_ctzll(x);
+                        const int64_t k_lo = kb * p.block_k, k_hi = std::min<int64_t>(k_lo + p.block_k, L) - 1;
+                        for (int64_t tk = k_lo / kTileK; tk <= k_hi / kTileK; ++tk) {
+                            acc[tk] |= 1u << (sq * nsk);
+                            touched[tk >> 6] |= 1ull << (tk & 63);
+                        }
+                    }
+            }
+            for (int64_t tw = 0; tw < twords; ++tw) {
+                for (uint64_t x = touched[tw]; x; x &= x - 1) {
+                    const int64_t tk = tw * 64 + __builtin_ctzll(x);
+                    emit(tk, acc[tk]);
+                    acc[tk] = 0u;
+                }
+                touched[tw] = 0u;
+            }
         }
         out.empty += nkt - n_tiles;
         t.te = (int32_t)out.tiles.size();
@@ -1095,8 +1139,9 @@ static int32_t organise_tasks(bsa_plan_s &p, const std::vector<HeadOut *> &heads
         if (!p.img) return fail(BSA_ERR_OUT_OF_MEMORY, "pinned host allocation of %zu bytes failed", p.img_bytes);
         p.img_pinned = true;
     } else {
-        p.img_vec.resize(p.img_bytes);
-        p.img = p.img_vec.data();
+        p.img_host.reset(new uint8_t[p.img_bytes]);
+        p.img_host_n = p.img_bytes;
+        p.img = p.img_host.get();
         p.img_cap = p.img_bytes;
     }
     // tiles and gather indices, per head in parallel; tasks unsorted into a scratch list
@@ -1348,6 +1393,16 @@ extern "C" int32_t bsa_plan(const bsa_mask_desc_t *logical_mask, int32_t B, int3
         const int64_t nqb_m = (L + block_q - 1) / block_q, nkb_m = (L + block_k - 1) / block_k;
         const size_t head_bytes = m.kind == BSA_MASK_BLOCK_U8 ? (size_t)(nqb_m * nkb_m)
                                   : m.kind == BSA_MASK_BLOCK_BITS ? (size_t)(nqb_m * ((nkb_m + 63) / 64)) * 8 : 0;
+        // BLOCK: each head's mask bytes against the previous head's, in parallel
+        // (a small-block mask holds megabytes per head)
+        std::vector<uint8_t> same_as_prev((size_t)NBH, 0);
+        if (p->mode == kModeBlock && NBH > 1) {
+            const uint8_t *d = (const uint8_t *)m.data;
+            parallel_for(NBH - 1, [&](int64_t i) {
+                const int64_t bh = i + 1;
+                same_as_prev[(size_t)bh] = std::memcmp(d + (size_t)(bh - 1) * head_bytes, d + (size_t)bh * head_bytes, head_bytes) == 0;
+            });
+        }
         for (int64_t bh = 0; bh < NBH; ++bh) {
             src[(size_t)bh] = bh;
             if (p->mode == kModeVideo) {
@@ -1359,10 +1414,8 @@ extern "C" int32_t bsa_plan(const bsa_mask_desc_t *logical_mask, int32_t B, int3
                         break;
                     }
                 }
-            } else if (p->mode == kModeBlock && bh > 0) {
-                const uint8_t *d = (const uint8_t *)m.data;
-                if (std::memcmp(d + (size_t)(bh - 1) * head_bytes, d + (size_t)bh * head_bytes, head_bytes) == 0)
-                    src[(size_t)bh] = src[(size_t)(bh - 1)];
+            } else if (p->mode == kModeBlock && same_as_prev[(size_t)bh]) {
+                src[(size_t)bh] = src[(size_t)(bh - 1)];
             }
         }
         // work items: chunks of kMapChunk query tiles of the heads to map, so
@@ -1625,11 +1678,13 @@ static int32_t read_back_device_plan(bsa_plan_s *p, bool image)
     }
     if (e == hipSuccess && image && !p->host_copy) {
         // tasks and records, and the gathered keys of a slice plan
-        p->img_vec.assign(p->mode == kModeGather ? p->off_flags : p->off_gidx, 0);
-        e = hipMemcpy(p->img_vec.data(), p->dev, p->img_vec.size(), hipMemcpyDeviceToHost);
+        const size_t n = p->mode == kModeGather ? p->off_flags : p->off_gidx;
+        p->img_host.reset(new uint8_t[std::max<size_t>(n, 1)]);
+        p->img_host_n = n;
+        e = hipMemcpy(p->img_host.get(), p->dev, n, hipMemcpyDeviceToHost);
         if (e == hipSuccess) {
-            p->img = p->img_vec.data();
-            p->img_cap = p->img_vec.size();
+            p->img = p->img_host.get();
+            p->img_cap = n;
             p->host_copy = true;
         }
     }
