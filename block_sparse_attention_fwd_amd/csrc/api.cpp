@@ -2041,6 +2041,9 @@ static int32_t check_route_args(const void *Q, const void *K, const void *V, int
     for (int32_t i = 0; i < r.n_rows; ++i)
         if (r.rows[i] < 0 || r.rows[i] >= L) return fail(BSA_ERR_INVALID_ARGUMENT, "row %d = %d out of range", i, r.rows[i]);
     if (r.device < 0) return fail(BSA_ERR_INVALID_ARGUMENT, "routing needs a device (desc->device = %d)", r.device);
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || r.device >= ndev)
+        return fail(BSA_ERR_INVALID_ARGUMENT, "device %d does not exist (%d devices)", r.device, ndev);
     return BSA_OK;
 }
 

@@ -338,7 +338,7 @@ typedef struct {
     int32_t radius;             /* 0 .. 256 */
     const int32_t *rows;        /* HOST [n_rows]: sampled query tokens (frame-major), each in [0, L) */
     int32_t n_rows;             /* 1 .. 4096 */
-    int32_t device;             /* device of Q, K, V (>= 0) */
+    int32_t device;             /* device of Q, K, V: 0 <= device < device count */
 } bsa_route_desc_t;
 
 /*
@@ -349,7 +349,7 @@ typedef struct {
  * BSA_PAT_TEMPORAL) and, if err is not NULL, err (HOST [H][2]: the spatial and
  * the temporal mean squared difference). Scratch device memory comes from the
  * library's pool. Errors: INVALID_ARGUMENT (null pointers, shapes, geometry,
- * rows out of range), OUT_OF_MEMORY, HIP.
+ * rows out of range, no such device), OUT_OF_MEMORY, HIP.
  */
 int32_t bsa_route_heads(const void *Q, const void *K, const void *V, int32_t B, int32_t H, int64_t L, int32_t d,
                         const bsa_route_desc_t *desc, void *stream, uint8_t *head_pattern, double *err);

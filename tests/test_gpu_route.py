@@ -107,3 +107,10 @@ def test_route_argument_errors():
             bsa.route_heads(q, k, v, w.B, w.H, w.L, w.d, args["T"], args["Hg"], args["Wg"], np.array(rows, np.int32),
                             **extra)
         assert e.value.status == bsa.ERR_INVALID_ARGUMENT
+    # a device index past the last device is refused before anything runs,
+    # by both entry points
+    for fn in (bsa.route_heads, bsa.route_heads_noalloc):
+        with pytest.raises(bsa.BSAError) as e:
+            fn(q, k, v, w.B, w.H, w.L, w.d, w.T, w.Hg, w.Wg, np.array([0, 5], np.int32),
+               device=torch.cuda.device_count())
+        assert e.value.status == bsa.ERR_INVALID_ARGUMENT
