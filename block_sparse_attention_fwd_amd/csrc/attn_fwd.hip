@@ -6,7 +6,8 @@
 // and load/compute overlap). Every key tile of 64 keys is staged in LDS once
 // and shared by all waves; the next tile's global loads are in flight while
 // the current tile is computed, and land in the other half of a
-// double-buffered LDS tile. Empty tiles never reach the kernel; FULL tiles
+// double-buffered LDS tile (the 8-wave kernel keeps two tiles in flight in a
+// ring of three buffers). Empty tiles never reach the kernel; FULL tiles
 // run with no mask code; PARTIAL tiles evaluate the exact predicate (Sparse
 // VideoGen / Splash Attention summary, "Splash Attention": empty tiles
 // bypassed, exact coordinate masking only on boundary tiles). Gathered tiles
