@@ -167,25 +167,26 @@ def test_one_plan_on_concurrent_streams():
 @pytest.mark.parametrize("run", ["A", "B"])
 def test_svg_full_size_sampled(run, regime):
     """SVG head routing at full size (24 heads, 13 x 30x52, d=128), in the
-    launch configuration the benchmark times; sampled rows of every head."""
+    launch configuration the benchmark times; per head the query tile with
+    the most PARTIAL tiles, the ragged last tile and 2,048 random rows."""
     w = wl.svg(run)
     Q, K, V = wl.make_qkv(w)
     log(f"[case] svg full run={run} regime={regime}")
     O, p = run_gpu(w, Q, K, V, force_regime=regime)
     # per head: the query tile with the most PARTIAL (exactly masked) tiles,
     # the ragged last tile and random rows
-    rows = thick_rows(w, p.info()["tile_q"], per_head=256, plan=p)
+    rows = thick_rows(w, p.info()["tile_q"], per_head=2048, plan=p)
     compare(w, Q, K, V, O, rows=rows, label=f"svg{run} {p.info()}")
 
 
 def test_fgattn_full_size_sampled():
     """FG-Attn slices at full size (24 heads, L = 32,760, M = 64): per head
     every row of the query block with the longest key list and of the ragged
-    last block, plus 256 random rows."""
+    last block, plus 2,048 random rows."""
     w = wl.fgattn()
     Q, K, V = wl.make_qkv(w)
     log("[case] fgattn full")
-    rows = thick_rows(w, 64)
+    rows = thick_rows(w, 64, per_head=2048)
     O, p = run_gpu(w, Q, K, V, rows=rows)
     compare(w, Q, K, V, O, rows=rows, gathered=True, label=f"fgattn {p.info()}")
 
@@ -216,12 +217,12 @@ def test_highres_full_size_sampled():
     """High-res 128x128 rasterised block mask at full size (24 heads,
     L = 302,400, d = 128; spatial heads frame-major, temporal heads
     temporal-major): per head every row of its heaviest query tile (in the
-    head's own token order) and of the ragged last tile, plus 256 random
+    head's own token order) and of the ragged last tile, plus 2,048 random
     rows."""
     w = wl.highres()
     log("[case] generating high-res Q/K/V (24 x 302400 x 128)")
     Q, K, V = wl.make_qkv(w)
-    rows = thick_rows(w, 128)
+    rows = thick_rows(w, 128, per_head=2048)
     for regime in (-1, 4):
         log(f"[case] highres full regime={regime}")
         O, p = run_gpu(w, Q, K, V, force_regime=regime, rows=rows)
