@@ -960,6 +960,9 @@ static int32_t choose_regime(const bsa_mask_desc_t &m, int32_t B, int32_t H, int
             if (r.kind != kind) continue;
             if (r.bq && r.bq != bq) continue;
             if (r.bk && r.bk != bk) continue;
+            // features not known (a mask in device memory): only a rule that
+            // holds for every density and fill applies, not the first bin's
+            if (!density_known && (r.dlo > 0.0 || r.dhi < 1.0 || r.flo > 0.0 || r.fhi < 1.0)) continue;
             if (dens >= 0 && (dens < r.dlo || dens > r.dhi)) continue;
             if (fill >= 0 && (fill < r.flo || fill > r.fhi)) continue;
             if (L < r.Llo || L > r.Lhi) continue;

@@ -223,8 +223,9 @@ int32_t bsa_plan(const bsa_mask_desc_t *logical_mask, int32_t B, int32_t H, int6
  * The mask must stay valid until the planning work has run (the plan keeps
  * its own copy of the slice keys). The plan equals the one bsa_plan builds
  * from the same mask, except that BLOCK regimes and orders come from the
- * table without the mask density, and bits past the last key block of a
- * BLOCK_BITS row are ignored. The host cannot validate a device mask: slice
+ * table's rules that hold for every mask density and fill (the features need
+ * the mask on the host), and bits past the last key block of a BLOCK_BITS
+ * row are ignored. The host cannot validate a device mask: slice
  * keys outside [0, L) are clamped into it, a list whose row_ptr bounds fall
  * outside [0, nnz] or span more than L keys is taken as empty, and keys that
  * are not strictly increasing are used as given; bsa_plan_info then returns

@@ -132,6 +132,31 @@ def test_tessera_masks_full_size(i):
     compare(w, Q, K, V, O, rows=sample_rows(w, per_head=16, seed=i), label=f"tessera{i} device plan")
 
 
+@pytest.mark.parametrize("i", [1, 5, 9, 25, 29])
+def test_device_plan_regime_without_features(i, tmp_path):
+    """A mask in device memory has no host-side features, so the device
+    planner takes the first lookup-table rule that holds for every density
+    and fill, never a feature-restricted bin: with the compiled-in table the
+    128x64-tile regime for 64x64 masks of every density and layout, and with
+    a table whose first matching rule is restricted, the full-range rule
+    after it."""
+    w = wl.tessera(i)
+    pd = plan_workload_device(w)
+    assert pd.info()["regime"] == 0, (i, pd.info()["regime"])
+    lut = tmp_path / "lut.txt"
+    lut.write_text("block 64 64 0 0.1 0 0.75 0 9999999999 1 xcd\n"
+                   "block 64 64 0 1 0 1 0 9999999999 4 lpt\n")
+    pd = plan_workload_device(w, lut_path=str(lut))
+    info = pd.info()
+    assert (info["regime"], info["task_order"]) == (4, bsa.ORDER_LONGEST_FIRST), info
+    # the host planner, which has the features, takes the restricted rule
+    # where they fall into it
+    ph = plan_workload(w, lut_path=str(lut), device=-1)
+    hi = ph.info()
+    inside = hi["mask_density"] <= 0.1 and hi["mask_fill"] <= 0.75
+    assert hi["regime"] == (1 if inside else 4), hi
+
+
 def test_mask_made_on_device_and_planned_on_a_side_stream():
     """A mask produced by device work (a threshold of device-random scores),
     planned on a second stream while the forward is enqueued on the current
@@ -331,9 +356,11 @@ def test_device_plan_edge_shapes():
 
 def test_device_plan_regime_ignores_density(tmp_path):
     """With a table whose rules split one block shape by density, the host
-    planner takes the rule of the mask's density and the device planner, which
-    never reads the mask on the host (no density, no fill), the first rule of
-    the shape and length."""
+    planner takes the rule of the mask's density; the device planner, which
+    never reads the mask on the host (no density, no fill), takes no
+    feature-restricted rule and, with no rule for every density and fill in
+    this table, falls back to the 128x64-tile regime and the XCD-grouped
+    order."""
     lut = tmp_path / "split.lut"
     lut.write_text("block 32 32 0 0.5 0 1 0 9999 1 lpt\n"
                    "block 32 32 0.5 1 0 1 0 9999 4 xcd\n")
@@ -342,4 +369,4 @@ def test_device_plan_regime_ignores_density(tmp_path):
     ih = plan_workload(w, lut_path=str(lut)).info()
     idv = plan_workload_device(w, lut_path=str(lut)).info()
     assert (ih["regime"], ih["task_order"]) == (4, bsa.ORDER_XCD_GROUPED)
-    assert (idv["regime"], idv["task_order"]) == (1, bsa.ORDER_LONGEST_FIRST)
+    assert (idv["regime"], idv["task_order"]) == (0, bsa.ORDER_XCD_GROUPED)
