@@ -78,6 +78,29 @@ def test_small_video(run, d):
             compare(w, Q, K, V, O, label=f"video{run} d{d} r{regime} order {order}")
 
 
+@pytest.mark.parametrize("regime", [0, 1, 4])
+def test_batch_of_two(regime):
+    """B = 2 with different inputs and masks per batch: a video mask (both
+    layouts, spatial / temporal / dense heads) and a block mask with a
+    batch-dependent pattern (an empty block row in one batch, a dense head in
+    the other), against the oracle."""
+    wv = wl.svg("B", H=3, T=5, Hg=7, Wg=13, d=128)
+    wv.B, wv.name = 2, "video_b2"
+    wv.head_pattern = np.array([wl.SPATIAL, wl.TEMPORAL, wl.DENSE], np.uint8)
+    wv.head_layout = np.array([0, 1, 1], np.uint8)
+    T, Hg, Wg = 3, 10, 11
+    wb = wl.Workload("block_b2", 78, 2, 2, T * Hg * Wg, 128, T, Hg, Wg, wl.BLOCK, 64, 32)
+    wb.block = (np.random.default_rng(78).random((2, 2, wb.nqb, wb.nkb)) < 0.4).astype(np.uint8)
+    wb.block[0, 1, 2, :] = 0
+    wb.block[1, 0] = 1
+    wb.head_layout = np.array([0, 1], np.uint8)
+    for w in (wv, wb):
+        Q, K, V = wl.make_qkv(w)
+        log(f"[case] {w.name} regime={regime}")
+        O, _ = run_gpu(w, Q, K, V, force_regime=regime)
+        compare(w, Q, K, V, O, label=f"{w.name} r{regime}")
+
+
 @pytest.mark.parametrize("M", [64, 128])
 @pytest.mark.parametrize("d", [64, 128])
 def test_small_slices(M, d):
