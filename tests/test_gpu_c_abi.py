@@ -49,6 +49,8 @@ def test_c_consumer_forward_matches_oracle(w, tmp_path):
     torch = pytest.importorskip("torch")
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
+    if not os.path.exists(EXE):
+        pytest.skip("tests/c_abi_forward is not built (build() compiles it)")
     from gpu_util import compare, log
     Q, K, V = wl.make_qkv(w)
     _write_inputs(str(tmp_path), w, Q, K, V)
