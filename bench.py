@@ -103,6 +103,33 @@ def time_forwards(bsa, p, q, k, v, o, stream, reps):
     return [a.elapsed_time(b) for a, b in ev]
 
 
+MFMA_TFLOPS_PER_GHZ = 256 * 4 * 1024 / 1e3  # dense bf16: 256 CUs x 4 SIMDs x 1,024 flop per clock
+
+
+def shader_clock(bsa, w, q, k, v, o, warm=4):
+    """The shader clock the headline kernel runs at: `warm` forwards back to
+    back, then one bsa_forward_stamped in the same stream; every task's
+    shader-clock ticks over its 100 MHz ticks (their totals, and the 10th and
+    90th percentiles of the per-task clocks). Not a step, not timed."""
+    import numpy as np
+    import torch
+    from bsa_helpers import plan_workload
+    p = plan_workload(w)
+    stamps = torch.zeros(4 * p.info()["workgroups"], dtype=torch.int64, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    for _ in range(warm):
+        bsa.forward(p, q, k, v, o, stream)
+    bsa.forward_stamped(p, q, k, v, o, stamps, stream)
+    torch.cuda.synchronize()
+    p.close()
+    s = stamps.cpu().numpy().reshape(-1, 4).astype(np.float64)
+    s = s[(s[:, 2] > s[:, 0]) & (s[:, 3] > s[:, 1])]
+    clk, real = s[:, 2] - s[:, 0], s[:, 3] - s[:, 1]
+    per = clk / real * 0.1
+    return {"ghz": round(float(clk.sum() / real.sum() * 0.1), 4), "p10": round(float(np.percentile(per, 10)), 4),
+            "p90": round(float(np.percentile(per, 90)), 4), "tasks": int(s.shape[0])}
+
+
 def time_steps(w, q, k, v, o, steps, warmup):
     """Whole-path steps for the headline: plan + forward for a fresh mask each
     step. A plan is retired (its memory back to the library's pools) once an
@@ -358,6 +385,10 @@ def main():
     r = time_steps(w, q, k, v, o, args.steps, args.warmup)
     log(f"[bench] high-res: {json.dumps({a: b for a, b in r.items() if a != 'plan_info'})}")
 
+    import block_sparse_attention_fwd_amd as bsa
+    clock = shader_clock(bsa, w, q, k, v, o)
+    log(f"[bench] shader clock over a stamped forward: {json.dumps(clock)}")
+
     classes = {}
     if not args.no_classes:
         for cw, bound, desc in class_workloads():
@@ -432,6 +463,8 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MI355X_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MI355X_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
                      "kernel": "bsa_fwd_bf16<4,1,128,2>", "flops_per_launch": flops},
+        "clock": dict(clock, mfma_peak_at_clock_tflops=round(MFMA_TFLOPS_PER_GHZ * clock["ghz"], 1),
+                      frac_of_mfma_peak_at_clock=round(achieved / (MFMA_TFLOPS_PER_GHZ * clock["ghz"]), 4)),
         "classes": class_out,
     }
     if not args.no_parity:

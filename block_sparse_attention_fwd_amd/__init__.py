@@ -29,9 +29,10 @@ DTYPE_BF16, DTYPE_F32 = 0, 1
 TILE_FULL, TILE_PARTIAL = 0, 1
 PRED_NONE, PRED_SUBBLOCK, PRED_VIDEO, PRED_LIST = 0, 1, 2, 3
 ORDER_XCD_GROUPED, ORDER_LONGEST_FIRST = 0, 1
-ABI_VERSION = 6  # the structures below mirror this version of bsa.h
+ABI_VERSION = 7  # the structures below mirror this version of bsa.h
 
-EXPORTED = ["bsa_abi_version", "bsa_plan_opts_default", "bsa_plan", "bsa_plan_device", "bsa_forward", "bsa_plan_destroy",
+EXPORTED = ["bsa_abi_version", "bsa_plan_opts_default", "bsa_plan", "bsa_plan_device", "bsa_forward", "bsa_forward_stamped",
+            "bsa_plan_destroy",
             "bsa_request_create", "bsa_request_submit", "bsa_request_finish", "bsa_request_stats",
             "bsa_request_destroy", "bsa_route_heads", "bsa_route_heads_noalloc",
             "bsa_plan_info", "bsa_plan_coverage", "bsa_regime_count", "bsa_regime_info", "bsa_status_str",
@@ -144,6 +145,8 @@ def lib(path: str = LIB_PATH):
                        ctypes.c_void_p, ctypes.c_void_p]
     L.bsa_forward.restype = ctypes.c_int32
     L.bsa_forward.argtypes = [ctypes.c_void_p] * 6
+    L.bsa_forward_stamped.restype = ctypes.c_int32
+    L.bsa_forward_stamped.argtypes = [ctypes.c_void_p] * 7
     L.bsa_plan_destroy.argtypes = [ctypes.c_void_p]
     L.bsa_plan_info.restype = ctypes.c_int32
     L.bsa_plan_info.argtypes = [ctypes.c_void_p, ctypes.POINTER(PlanInfo)]
@@ -379,6 +382,14 @@ def forward(p: Plan, q, k, v, o, stream=None) -> None:
     """bsa_forward: enqueue the forward pass on `stream` (torch stream, raw
     hipStream_t as int, or None for the current torch stream)."""
     _check(lib().bsa_forward(p.handle, _dptr(q), _dptr(k), _dptr(v), _dptr(o), _stream_handle(stream)))
+
+
+def forward_stamped(p: Plan, q, k, v, o, stamps, stream=None) -> None:
+    """bsa_forward_stamped: bsa_forward that also writes per-workgroup clock
+    stamps into `stamps` (a device int64 tensor of 4 * workgroups entries)."""
+    _check(lib().bsa_forward_stamped(p.handle, _dptr(q), _dptr(k), _dptr(v), _dptr(o), _dptr(stamps),
+                                     _stream_handle(stream)))
+
 
 
 def route_heads(q, k, v, B: int, H: int, L: int, d: int, T: int, Hg: int, Wg: int, rows, *, anchor_frame: int = 0,

@@ -1715,7 +1715,8 @@ static void magic_div(uint32_t d, uint32_t *m, int32_t *s)
     *s = l;
 }
 
-extern "C" int32_t bsa_forward(bsa_plan_t p, const void *Q, const void *K, const void *V, void *O, void *stream)
+static int32_t forward_impl(bsa_plan_t p, const void *Q, const void *K, const void *V, void *O, uint64_t *stamps,
+                            void *stream)
 {
     if (!p) return fail(BSA_ERR_INVALID_ARGUMENT, "plan is NULL");
     if (p->device < 0 || !p->dev) return fail(BSA_ERR_INVALID_ARGUMENT, "plan was built host-only (device = -1)");
@@ -1743,6 +1744,7 @@ extern "C" int32_t bsa_forward(bsa_plan_t p, const void *Q, const void *K, const
     a.mode = p->mode;
     a.bq_shift = p->bq_shift; a.bk_shift = p->bk_shift; a.nsk = p->nsk;
     a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)p->d));
+    a.stamps = stamps;
     int cur = 0;
     (void)hipGetDevice(&cur);
     if (cur != p->device) (void)hipSetDevice(p->device);
@@ -1776,6 +1778,19 @@ extern "C" int32_t bsa_forward(bsa_plan_t p, const void *Q, const void *K, const
     if (cur != p->device) (void)hipSetDevice(cur);
     if (e != hipSuccess) return fail(BSA_ERR_HIP, "kernel launch: %s", hipGetErrorString(e));
     return BSA_OK;
+}
+
+extern "C" int32_t bsa_forward(bsa_plan_t p, const void *Q, const void *K, const void *V, void *O, void *stream)
+{
+    return forward_impl(p, Q, K, V, O, nullptr, stream);
+}
+
+extern "C" int32_t bsa_forward_stamped(bsa_plan_t p, const void *Q, const void *K, const void *V, void *O,
+                                       uint64_t *stamps, void *stream)
+{
+    if (!stamps || ((uintptr_t)stamps & 7)) return fail(BSA_ERR_INVALID_ARGUMENT, "stamps must be an 8-byte aligned device pointer");
+    if (p && p->dtype != BSA_DTYPE_BF16) return fail(BSA_ERR_UNSUPPORTED, "clock stamps are written by the bf16 kernel only");
+    return forward_impl(p, Q, K, V, O, stamps, stream);
 }
 
 extern "C" int32_t bsa_plan_info(bsa_plan_t p, bsa_plan_info_t *out)

@@ -157,6 +157,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1
     const Task task{__builtin_amdgcn_readfirstlane(tl.bh), __builtin_amdgcn_readfirstlane(tl.q0),
                     __builtin_amdgcn_readfirstlane(tl.tb), __builtin_amdgcn_readfirstlane(tl.te)};
     if (task.bh < 0) return;  // padding task of an XCD segment
+    // instrumented launches: thread 0 stamps the task's start and end with the
+    // shader clock counter and the constant 100 MHz counter
+    if (a.stamps && tid == 0) {
+        a.stamps[4 * blockIdx.x] = __builtin_amdgcn_s_memtime();
+        a.stamps[4 * blockIdx.x + 1] = __builtin_amdgcn_s_memrealtime();
+    }
     const int bh = task.bh;
     const int h = bh % a.H;
     const uint32_t hflag = (uint32_t)__builtin_amdgcn_readfirstlane((int)a.head_flags[h]);
@@ -490,6 +496,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1
                     *(bf16x4 *)(orow + dd) = o4;
                 }
         }
+    }
+    if (a.stamps && tid == 0) {
+        a.stamps[4 * blockIdx.x + 2] = __builtin_amdgcn_s_memtime();
+        a.stamps[4 * blockIdx.x + 3] = __builtin_amdgcn_s_memrealtime();
     }
 }
 

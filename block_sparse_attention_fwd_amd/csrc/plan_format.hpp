@@ -65,6 +65,7 @@ struct KernelArgs {
     int32_t mode;              // MaskMode
     int32_t bq_shift, bk_shift, nsk;  // block sub-block geometry (log2 sizes, sub-blocks per key tile)
     float scale_log2;          // log2(e) / sqrt(d)
+    uint64_t *stamps;          // per-task clock stamps (instrumented launches), else null
 };
 
 }  // namespace bsa

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define BSA_ABI_VERSION 6
+#define BSA_ABI_VERSION 7
 
 typedef struct bsa_plan_s *bsa_plan_t;
 
@@ -257,6 +257,20 @@ int32_t bsa_plan_device(const bsa_mask_desc_t *logical_mask, int32_t B, int32_t 
  * plan), HIP.
  */
 int32_t bsa_forward(bsa_plan_t plan, const void *Q, const void *K, const void *V, void *O, void *stream);
+
+/* bsa_forward with clock stamps, for measuring the shader clock the kernel
+ * runs at (the rooflines' per-clock rates; it is no step of the method). The
+ * output is the same as bsa_forward's. `stamps` is a caller-owned device
+ * buffer of 4 * workgroups uint64 (bsa_plan_info: workgroups): thread 0 of
+ * workgroup i writes [4i] the shader-clock counter (s_memtime) and [4i+1] the
+ * constant 100 MHz counter (s_memrealtime) when its task starts, [4i+2] and
+ * [4i+3] the same when it ends; workgroups that run no task (padding of an XCD
+ * segment) write nothing. A task's shader clock is 100 MHz x (delta [4i+2] -
+ * [4i]) / (delta [4i+3] - [4i+1]). bf16 plans only.
+ * Errors: those of bsa_forward; INVALID_ARGUMENT (stamps NULL or not 8-byte
+ * aligned), UNSUPPORTED (fp32 plan). */
+int32_t bsa_forward_stamped(bsa_plan_t plan, const void *Q, const void *K, const void *V, void *O, uint64_t *stamps,
+                            void *stream);
 
 /* Free a plan (NULL is allowed). Blocks until every forward enqueued on the
  * plan has finished (its last-use event), so that no running kernel still

@@ -31,7 +31,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_status_strings():
     L = bsa.lib()
-    assert L.bsa_abi_version() == bsa.ABI_VERSION == 6
+    assert L.bsa_abi_version() == bsa.ABI_VERSION == 7
     assert L.bsa_status_str(bsa.ERR_INVALID_MASK) == b"BSA_ERR_INVALID_MASK"
     assert L.bsa_status_str(99) == b"BSA_ERR_UNKNOWN"
     assert len(bsa.regimes()) == L.bsa_regime_count() >= 3
@@ -107,6 +107,10 @@ def test_forward_rejects_host_only_plan_and_null_pointers():
     expect(bsa.ERR_INVALID_ARGUMENT, bsa.forward, p, 16, 16, 16, 16, stream=0, match="host-only")
     L = bsa.lib()
     assert L.bsa_forward(None, None, None, None, None, None) == bsa.ERR_INVALID_ARGUMENT
+    # the stamped forward: stamps must be an aligned pointer; then bsa_forward's checks
+    expect(bsa.ERR_INVALID_ARGUMENT, bsa.forward_stamped, p, 16, 16, 16, 16, 0, stream=0, match="stamps")
+    expect(bsa.ERR_INVALID_ARGUMENT, bsa.forward_stamped, p, 16, 16, 16, 16, 12, stream=0, match="stamps")
+    expect(bsa.ERR_INVALID_ARGUMENT, bsa.forward_stamped, p, 16, 16, 16, 16, 16, stream=0, match="host-only")
     L.bsa_plan_destroy(None)  # NULL-safe
 
 
