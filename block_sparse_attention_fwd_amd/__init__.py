@@ -58,7 +58,7 @@ class PlanInfo(ctypes.Structure):
                 ("tiles_partial", ctypes.c_int64), ("tiles_empty", ctypes.c_int64), ("gather_rows", ctypes.c_int64),
                 ("executed_pairs", ctypes.c_double), ("device_bytes", ctypes.c_int64), ("plan_ns", ctypes.c_int64),
                 ("phase_ns", ctypes.c_int64 * 5), ("task_order", ctypes.c_int32), ("mask_density", ctypes.c_double),
-                ("mask_fill", ctypes.c_double)]
+                ("mask_fill", ctypes.c_double), ("mask_fill2", ctypes.c_double)]
 
     def as_dict(self):
         d = {k: getattr(self, k) for k, _ in self._fields_}

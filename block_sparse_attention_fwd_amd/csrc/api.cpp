@@ -33,6 +33,7 @@
 #include <memory>
 #include <new>
 #include <sstream>
+#include <stdexcept>
 #include <string>
 #include <thread>
 
@@ -123,16 +124,17 @@ extern "C" int32_t bsa_regime_info(int32_t r, bsa_regime_desc_t *out)
 }
 
 // Lookup-table rule: first matching line wins. Fields:
-//   kind block_q block_k density_lo density_hi fill_lo fill_hi L_lo L_hi regime [order]
+//   kind block_q block_k density_lo density_hi fill_lo fill_hi [fill2_lo fill2_hi] L_lo L_hi regime [order]
 // kind is block|slice|video; block sizes may be '*'; order is xcd (the
-// default) or lpt (BSA_ORDER_*). density and fill are the mask features of
-// mask_features() (-1 where a kind has none; such a feature matches any
-// range).
+// default) or lpt (BSA_ORDER_*); a line without the fill2 range matches any
+// fill2. density, fill and fill2 are the mask features of mask_features()
+// (-1 where a kind has none; such a feature matches any range).
 struct LutRule {
     int kind;  // BSA_MASK_BLOCK_U8 (both block kinds), SLICE, VIDEO
     int bq, bk;  // 0 = any
     double dlo, dhi;
     double flo, fhi;
+    double f2lo, f2hi;  // fill of 256-row tiles ([0, 1] when the line omits it)
     int64_t Llo, Lhi;
     int regime;
     int order;
@@ -149,23 +151,57 @@ static bool parse_lut(const std::string &text, std::vector<LutRule> &rules, std:
         ++ln;
         auto hash = line.find('#');
         if (hash != std::string::npos) line.resize(hash);
+        // kind bq bk density_lo density_hi fill_lo fill_hi [fill2_lo fill2_hi] L_lo L_hi regime [order]
         std::istringstream ls(line);
-        std::string kind, bq, bk;
+        std::vector<std::string> tok;
+        for (std::string t; ls >> t;) tok.push_back(t);
+        if (tok.empty()) continue;
         LutRule r{};
-        if (!(ls >> kind)) continue;
-        if (!(ls >> bq >> bk >> r.dlo >> r.dhi >> r.flo >> r.fhi >> r.Llo >> r.Lhi >> r.regime)) {
-            err = "lookup table line " + std::to_string(ln) + " malformed";
-            return false;
+        r.order = BSA_ORDER_XCD_GROUPED;
+        if (tok.back() == "lpt" || tok.back() == "xcd") {
+            if (tok.back() == "lpt") r.order = BSA_ORDER_LONGEST_FIRST;
+            tok.pop_back();
         }
+        const std::string &kind = tok[0];
         if (kind == "block") r.kind = BSA_MASK_BLOCK_U8;
         else if (kind == "slice") r.kind = BSA_MASK_SLICE_CSR;
         else if (kind == "video") r.kind = BSA_MASK_VIDEO;
         else { err = "lookup table line " + std::to_string(ln) + ": unknown kind " + kind; return false; }
-        std::string order;
-        r.order = BSA_ORDER_XCD_GROUPED;
-        if (ls >> order) {
-            if (order == "lpt") r.order = BSA_ORDER_LONGEST_FIRST;
-            else if (order != "xcd") { err = "lookup table line " + std::to_string(ln) + ": unknown order " + order; return false; }
+        if (tok.size() == 11 || tok.size() == 13) {
+            // one field more than a rule: an order name that is neither xcd nor lpt
+            char *end = nullptr;
+            (void)std::strtod(tok.back().c_str(), &end);
+            if (end && *end != '\0') {
+                err = "lookup table line " + std::to_string(ln) + ": unknown order " + tok.back();
+                return false;
+            }
+        }
+        if (tok.size() != 10 && tok.size() != 12) {
+            err = "lookup table line " + std::to_string(ln) + " malformed";
+            return false;
+        }
+        const bool has_f2 = tok.size() == 12;
+        const std::string &bq = tok[1], &bk = tok[2];
+        r.f2lo = 0.0;
+        r.f2hi = 1.0;
+        try {
+            size_t i = 3;
+            r.dlo = std::stod(tok[i++]);
+            r.dhi = std::stod(tok[i++]);
+            r.flo = std::stod(tok[i++]);
+            r.fhi = std::stod(tok[i++]);
+            if (has_f2) {
+                r.f2lo = std::stod(tok[i++]);
+                r.f2hi = std::stod(tok[i++]);
+            }
+            r.Llo = std::stoll(tok[i++]);
+            r.Lhi = std::stoll(tok[i++]);
+            size_t used = 0;
+            r.regime = std::stoi(tok[i], &used);
+            if (used != tok[i].size()) throw std::invalid_argument("regime");
+        } catch (const std::exception &) {
+            err = "lookup table line " + std::to_string(ln) + " malformed";
+            return false;
         }
         r.bq = bq == "*" ? 0 : std::atoi(bq.c_str());
         r.bk = bk == "*" ? 0 : std::atoi(bk.c_str());
@@ -197,7 +233,7 @@ struct bsa_plan_s {
     int32_t bq_shift = 0, bk_shift = 0, nsk = 1, sub_q = 0, sub_k = 0;
     int32_t mode = 0;
     int32_t task_order = BSA_ORDER_XCD_GROUPED;
-    double mask_density = -1.0, mask_fill = -1.0;  // regime-lookup features (-1: none for the kind)
+    double mask_density = -1.0, mask_fill = -1.0, mask_fill2 = -1.0;  // regime-lookup features (-1: none for the kind)
     std::vector<uint8_t> head_layout, head_pattern;
     // image
     uint8_t *img = nullptr;
@@ -849,14 +885,21 @@ static int32_t validate(const bsa_mask_desc_t *m, int32_t B, int32_t H, int64_t 
 //    Banded and windowed layouts fill their tiles (near 1); a random layout
 //    of blocks smaller than the tile leaves most of each non-empty tile
 //    masked (about density / (1 - (1 - density)^k) for k blocks per tile),
-//    where 64-row tiles waste less.
+//    where 64-row tiles waste less;
+//  - fill2: the same over 256 x 64 tiles (the 8-wave regime's tiling). It is
+//    at most fill, and near it where the two 128-row halves of a 256-row tile
+//    keep the same key tiles (banded, windowed and frame-aligned video
+//    layouts); a random layout of 128-row blocks fills 128-row tiles and
+//    leaves half of each 256-row tile masked.
 // BLOCK features come from a fixed sample: every kFeatureStride-th 128-row
-// query tile of every head (all of them when a head has fewer tiles), read
-// as keep-bit words, so the cost is a fraction of one mapping pass and the
-// result is a deterministic function of the mask.
+// query tile of every head (all of them when a head has fewer tiles) for
+// density and fill, and the 256-row tiles that start at those rows for fill2,
+// read as keep-bit words, so the cost is a fraction of one mapping pass and
+// the result is a deterministic function of the mask.
 struct MaskFeatures {
     double density = -1.0;
     double fill = -1.0;
+    double fill2 = -1.0;
 };
 constexpr int64_t kFeatureStride = 4;
 
@@ -873,42 +916,60 @@ static MaskFeatures mask_features(const bsa_mask_desc_t &m, int32_t B, int32_t H
     const int64_t nqt = (L + 127) / 128, nkt = (L + kTileK - 1) / kTileK;
     const int64_t words = (nkb + 63) / 64, twords = (nkt + 63) / 64;
     const int64_t stride = nqt >= 4 * kFeatureStride ? kFeatureStride : 1;
+    const int64_t nqt2 = (L + 255) / 256, stride2 = stride == 1 ? 1 : stride / 2;
     const int64_t heads = (int64_t)B * H;
     const int64_t last_w = L - (nkb - 1) * bk;  // width of the (cropped) last key block
     struct Acc {
         int64_t blocks = 0, kept = 0;
-        double kept_pairs = 0.0, exec_pairs = 0.0;
+        double kept_pairs = 0.0, exec_pairs = 0.0, kept_pairs2 = 0.0, exec_pairs2 = 0.0;
     };
     std::vector<Acc> acc((size_t)heads);
     parallel_for(heads, [&](int64_t bh) {
-        std::vector<uint64_t> rowbuf((size_t)words), uni((size_t)words), tiles((size_t)twords);
+        std::vector<uint64_t> rowbuf((size_t)words), uni((size_t)words), uni2((size_t)words), tiles((size_t)twords);
         Acc a;
-        for (int64_t tq = 0; tq < nqt; tq += stride) {
-            const int64_t q0 = tq * 128, q1 = std::min<int64_t>(q0 + 128, L);
-            std::fill(uni.begin(), uni.end(), 0ull);
-            for (int64_t qb = q0 / bq; qb <= (q1 - 1) / bq; ++qb) {
-                const uint64_t *row = block_row_bits(m, bh, qb, nqb, nkb, rowbuf.data());
-                int64_t k = 0;
-                for (int64_t w = 0; w < words; ++w) {
-                    k += __builtin_popcountll(row[w]);
-                    uni[w] |= row[w];
-                }
-                const bool last = (row[words - 1] >> ((nkb - 1) & 63)) & 1;
-                const int64_t r_in = std::min<int64_t>(q1, (qb + 1) * bq) - std::max<int64_t>(q0, qb * bq);
-                a.kept_pairs += (double)r_in * (double)(k * bk - (last ? bk - last_w : 0));
-                a.kept += k;
-                a.blocks += nkb;
-            }
+        // the non-empty 64-key tiles of a union of keep-bit rows
+        auto count_tiles = [&](const std::vector<uint64_t> &u) {
             std::fill(tiles.begin(), tiles.end(), 0ull);
             for (int64_t w = 0; w < words; ++w)
-                for (uint64_t x = uni[w]; x; x &= x - 1) {
+                for (uint64_t x = u[w]; x; x &= x - 1) {
                     const int64_t kb = w * 64 + __builtin_ctzll(x);
                     const int64_t k_lo = kb * bk, k_hi = std::min<int64_t>(k_lo + bk, L) - 1;
                     for (int64_t tk = k_lo / kTileK; tk <= k_hi / kTileK; ++tk) tiles[tk >> 6] |= 1ull << (tk & 63);
                 }
             int64_t nt = 0;
             for (int64_t w = 0; w < twords; ++w) nt += __builtin_popcountll(tiles[w]);
-            a.exec_pairs += (double)nt * (double)(q1 - q0) * (double)kTileK;
+            return nt;
+        };
+        // 256-row tile t2 = 128-row tiles 2 t2 and 2 t2 + 1; the first (both
+        // when every 128-row tile is sampled) is also a density / fill sample
+        for (int64_t t2 = 0; t2 < nqt2; t2 += stride2) {
+            std::fill(uni2.begin(), uni2.end(), 0ull);
+            for (int64_t tq = 2 * t2; tq < std::min<int64_t>(2 * t2 + 2, nqt); ++tq) {
+                const bool sampled = tq == 2 * t2 || stride == 1;
+                const int64_t q0 = tq * 128, q1 = std::min<int64_t>(q0 + 128, L);
+                std::fill(uni.begin(), uni.end(), 0ull);
+                for (int64_t qb = q0 / bq; qb <= (q1 - 1) / bq; ++qb) {
+                    const uint64_t *row = block_row_bits(m, bh, qb, nqb, nkb, rowbuf.data());
+                    int64_t k = 0;
+                    for (int64_t w = 0; w < words; ++w) {
+                        k += __builtin_popcountll(row[w]);
+                        uni[w] |= row[w];
+                    }
+                    const bool last = (row[words - 1] >> ((nkb - 1) & 63)) & 1;
+                    const int64_t r_in = std::min<int64_t>(q1, (qb + 1) * bq) - std::max<int64_t>(q0, qb * bq);
+                    const double kp = (double)r_in * (double)(k * bk - (last ? bk - last_w : 0));
+                    a.kept_pairs2 += kp;
+                    if (sampled) {
+                        a.kept_pairs += kp;
+                        a.kept += k;
+                        a.blocks += nkb;
+                    }
+                }
+                for (int64_t w = 0; w < words; ++w) uni2[w] |= uni[w];
+                if (sampled) a.exec_pairs += (double)count_tiles(uni) * (double)(q1 - q0) * (double)kTileK;
+            }
+            const int64_t r2 = std::min<int64_t>(256 * t2 + 256, L) - 256 * t2;
+            a.exec_pairs2 += (double)count_tiles(uni2) * (double)r2 * (double)kTileK;
         }
         acc[bh] = a;
     });
@@ -918,9 +979,12 @@ static MaskFeatures mask_features(const bsa_mask_desc_t &m, int32_t B, int32_t H
         t.kept += a.kept;
         t.kept_pairs += a.kept_pairs;
         t.exec_pairs += a.exec_pairs;
+        t.kept_pairs2 += a.kept_pairs2;
+        t.exec_pairs2 += a.exec_pairs2;
     }
     f.density = t.blocks ? (double)t.kept / (double)t.blocks : 0.0;
     f.fill = t.exec_pairs > 0 ? std::min(1.0, t.kept_pairs / t.exec_pairs) : 1.0;
+    f.fill2 = t.exec_pairs2 > 0 ? std::min(1.0, t.kept_pairs2 / t.exec_pairs2) : 1.0;
     return f;
 }
 
@@ -954,7 +1018,7 @@ static int32_t choose_regime(const bsa_mask_desc_t &m, int32_t B, int32_t H, int
         const int kind = m.kind == BSA_MASK_BLOCK_BITS ? BSA_MASK_BLOCK_U8 : m.kind;
         const MaskFeatures feat = density_known ? mask_features(m, B, H, L, bq, bk) : MaskFeatures{};
         if (feat_out) *feat_out = feat;
-        const double dens = feat.density, fill = feat.fill;
+        const double dens = feat.density, fill = feat.fill, fill2 = feat.fill2;
         *regime = -1;
         for (const LutRule &r : rules) {
             if (r.kind != kind) continue;
@@ -962,9 +1026,12 @@ static int32_t choose_regime(const bsa_mask_desc_t &m, int32_t B, int32_t H, int
             if (r.bk && r.bk != bk) continue;
             // features not known (a mask in device memory): only a rule that
             // holds for every density and fill applies, not the first bin's
-            if (!density_known && (r.dlo > 0.0 || r.dhi < 1.0 || r.flo > 0.0 || r.fhi < 1.0)) continue;
+            if (!density_known &&
+                (r.dlo > 0.0 || r.dhi < 1.0 || r.flo > 0.0 || r.fhi < 1.0 || r.f2lo > 0.0 || r.f2hi < 1.0))
+                continue;
             if (dens >= 0 && (dens < r.dlo || dens > r.dhi)) continue;
             if (fill >= 0 && (fill < r.flo || fill > r.fhi)) continue;
+            if (fill2 >= 0 && (fill2 < r.f2lo || fill2 > r.f2hi)) continue;
             if (L < r.Llo || L > r.Lhi) continue;
             *regime = r.regime;
             *order = r.order;
@@ -1362,6 +1429,7 @@ extern "C" int32_t bsa_plan(const bsa_mask_desc_t *logical_mask, int32_t B, int3
         std::unique_ptr<bsa_plan_s> p(new bsa_plan_s);
         p->mask_density = feat.density;
         p->mask_fill = feat.fill;
+        p->mask_fill2 = feat.fill2;
         p->B = B; p->H = H; p->L = L; p->d = d; p->dtype = o.dtype;
         p->kind = m.kind; p->block_q = block_q; p->block_k = block_k;
         p->regime = regime;
@@ -1517,6 +1585,7 @@ extern "C" int32_t bsa_plan_device(const bsa_mask_desc_t *logical_mask, int32_t 
         std::unique_ptr<bsa_plan_s> p(new bsa_plan_s);
         p->mask_density = feat.density;
         p->mask_fill = feat.fill;
+        p->mask_fill2 = feat.fill2;
         p->B = B; p->H = H; p->L = L; p->d = d; p->dtype = o.dtype;
         p->kind = m.kind; p->block_q = block_q; p->block_k = block_k;
         p->regime = regime;
@@ -1815,6 +1884,7 @@ extern "C" int32_t bsa_plan_info(bsa_plan_t p, bsa_plan_info_t *out)
     out->task_order = p->task_order;
     out->mask_density = p->mask_density;
     out->mask_fill = p->mask_fill;
+    out->mask_fill2 = p->mask_fill2;
     if (p->mask_errors)
         return fail(BSA_ERR_INVALID_MASK, "the device mask had %lld invalid slice entries or lists (clamped or dropped)",
                     (long long)p->mask_errors);

@@ -11,17 +11,24 @@ writes the fastest regime of each bin as one rule of the table (the default
 unless another wins by more than 2%).
 
 Besides the kept-block density, block-mask bins are split by the mask's fill
-(kept pairs over the pairs of its non-empty 128 x 64 tiles, the feature the
-planner computes): a random layout of blocks smaller than the tile leaves most
-of each non-empty tile masked, where banded and windowed layouts fill them, and
-the two want different tile heights. Each synthetic request's fill is read
-back from the planner, the requests of a bin are grouped by fill bin, and each
-group's timings (summed over its layouts) give that group's rule.
+(kept pairs over the pairs of its non-empty 128 x 64 tiles) and its fill2
+(the same over 256 x 64 tiles), the features the planner computes: a random
+layout of blocks smaller than a tile leaves most of each non-empty tile
+masked, where banded, windowed and frame-aligned layouts fill them, and the
+two want different tile heights. Each synthetic request's fill and fill2 are
+read back from the planner, the requests of a bin are grouped by (fill bin,
+fill2 bin), and each group's timings (summed over its layouts) give that
+group's rule.
 
 Inputs are seeded and synthetic (workloads module): BLOCK masks in banded,
-local-window and random layouts, video head routing (half spatial heads,
-half temporal heads in temporal-major order), slice lists, Q/K/V ~ N(0,1) in
-bf16. Each bin's rule names the fastest (regime, task order) pair.
+local-window and random layouts at three densities, plus the Sparse VideoGen
+head patterns rasterised at the block shape (half the heads spatial in
+frame-major order, half temporal in temporal-major order, as the high-res
+workload; it joins the density bin its own density falls in); video head
+routing (VIDEO masks, the same head split); slice lists; Q/K/V ~ N(0,1) in
+bf16, drawn on the device. The largest length bin runs 24 heads where the
+mask stays under MASK_CAP bytes (4 heads for 32 x 32 blocks). Each bin's rule
+names the fastest (regime, task order) pair.
 
 Usage (on the target GPU, from the repository root):
     python3 block_sparse_attention_fwd_amd/lut/build_lut.py [--out lut/gfx950.lut] [--orders all] [--quick]
@@ -49,12 +56,15 @@ LENGTH_BINS = (
     ((4, 32, 32), (0, 8192), 24),
     ((13, 30, 52), (8193, 40000), 24),
     ((21, 45, 80), (40001, 150000), 24),
-    ((21, 90, 160), (150001, 9999999999), 4),
+    ((21, 90, 160), (150001, 9999999999), 24),
 )
+MASK_CAP = 600_000_000  # bytes of a request's uint8 block mask; past it the request runs 4 heads
 BLOCK_SHAPES = ((32, 32), (64, 64), (128, 128), (64, 256))
 DENSITY_BINS = ((0.05, (0.0, 0.1)), (0.15, (0.1, 0.275)), (0.4, (0.275, 1.0)))
 FILL_BINS = ((0.0, 0.75), (0.75, 1.0))  # low fill: random layouts of small blocks; high: banded / windowed
+FILL2_BINS = ((0.0, 0.75), (0.75, 1.0))  # the same over 256-row tiles: low also for random 128-row blocks
 LAYOUTS = ("banded", "local", "random")
+VIDEO_LAYOUT = "video"  # the video head patterns rasterised at the block shape
 
 
 def log(*a):
@@ -112,23 +122,26 @@ def time_regimes(bsa, torch, w, regimes, q, k, v, o, reps, rounds=3):
             p.close()
 
 
-def fill_bin(fill):
-    for lo, hi in FILL_BINS:
-        if lo <= fill <= hi:
+def in_bin(x, bins):
+    for lo, hi in bins:
+        if lo <= x <= hi:
             return (lo, hi)
-    return FILL_BINS[-1]
+    return bins[-1]
 
 
 def block_rules(bq, bk, dlo, dhi, llo, lhi, groups):
-    """Table lines of one (block shape, density, length) bin from its fill
-    groups {fill bin: summed timings}; a fill bin no layout fell into takes
-    the choice of the other, so every fill in [0, 1] resolves."""
-    picks = {fb: pick(t) for fb, t in groups.items()}
+    """Table lines of one (block shape, density, length) bin from its groups
+    {(fill bin, fill2 bin): summed timings}. A group no layout fell into takes
+    the choice of the group with the same fill bin, else of one with the same
+    fill2 bin, else of any, so every (fill, fill2) in [0, 1]^2 resolves."""
+    picks = {g: pick(t) for g, t in groups.items()}
     out = []
     for fb in FILL_BINS:
-        best = picks.get(fb) or next(iter(picks.values()))
-        out.append(f"block   {bq:<7d} {bk:<7d} {dlo:<10g} {dhi:<10g} {fb[0]:<7g} {fb[1]:<7g} {llo:<6d} {lhi:<10d} "
-                   f"{best[0]} {oname(best[1])}")
+        for f2 in FILL2_BINS:
+            best = (picks.get((fb, f2)) or next((v for (a, _), v in picks.items() if a == fb), None)
+                    or next((v for (_, b), v in picks.items() if b == f2), None) or next(iter(picks.values())))
+            out.append(f"block   {bq:<7d} {bk:<7d} {dlo:<10g} {dhi:<10g} {fb[0]:<7g} {fb[1]:<7g} {f2[0]:<7g} "
+                       f"{f2[1]:<7g} {llo:<6d} {lhi:<10d} {best[0]} {oname(best[1])}")
     return out
 
 
@@ -149,7 +162,7 @@ def main():
 
     import block_sparse_attention_fwd_amd as bsa
     import workloads as wl
-    from bsa_helpers import plan_workload, to_device_bf16
+    from bsa_helpers import plan_workload
 
     assert torch.cuda.is_available(), "the lookup table is built on the GPU it is for"
     d = 128
@@ -159,10 +172,11 @@ def main():
     t_start = time.time()
     for (T, Hg, Wg), (llo, lhi), H in length_bins:
         L = T * Hg * Wg
-        base = wl.Workload("lut", 9, 1, H, L, d, T, Hg, Wg, wl.BLOCK, 64, 64)
-        Q, K, V = wl.make_qkv(base)
-        q, k, v = to_device_bf16(Q), to_device_bf16(K), to_device_bf16(V)
-        del Q, K, V
+        # Q/K/V ~ N(0,1) in bf16, drawn on the device (the timings do not
+        # depend on the values); requests with fewer heads use the first ones
+        gen = torch.Generator(device="cuda:0")
+        gen.manual_seed(9)
+        q, k, v = (torch.randn((1, H, L, d), generator=gen, device="cuda:0").to(torch.bfloat16) for _ in range(3))
         o = torch.empty_like(q)
         # video head routing
         wv = wl.svg("B", H=H, T=T, Hg=Hg, Wg=Wg, d=d, cfg=9)
@@ -173,22 +187,33 @@ def main():
         rules.append(f"video   *       *       -1         1          -1      1       {llo:<6d} {lhi:<10d} "
                      f"{best[0]} {oname(best[1])}")
         for (bq, bk) in BLOCK_SHAPES:
+            Hs = H if -(-L // bq) * -(-L // bk) * H <= MASK_CAP else 4
+            groups = {rb: {} for rb in DENSITY_BINS}  # density bin -> {(fill bin, fill2 bin): summed timings}
+            requests = [(rho, li, lay) for rho, _ in DENSITY_BINS for li, lay in enumerate(layouts)]
+            if not args.quick:
+                requests.append((None, len(layouts), VIDEO_LAYOUT))
+            for rho, li, lay in requests:
+                if lay == VIDEO_LAYOUT:
+                    w = wl.video_block_request(f"lut_{bq}x{bk}_video", 9, bq, bk, Hs, T, Hg, Wg, d)
+                else:
+                    w = wl.block_request(f"lut_{bq}x{bk}_{rho}_{lay}", 9, li, bq, bk, rho, lay, Hs, T, Hg, Wg, d)
+                hp = plan_workload(w, device=-1)
+                info = hp.info()
+                hp.close()
+                dens, fill, fill2 = info["mask_density"], info["mask_fill"], info["mask_fill2"]
+                tt = time_regimes(bsa, torch, w, TILE_REGIMES, q, k, v, o, args.reps)
+                rb = next(b for b in DENSITY_BINS if b[1][0] <= dens <= b[1][1]) if rho is None else \
+                    next(b for b in DENSITY_BINS if b[0] == rho)
+                g = groups[rb].setdefault((in_bin(fill, FILL_BINS), in_bin(fill2, FILL2_BINS)), {})
+                for x, t in tt.items():
+                    g[x] = g.get(x, 0.0) + t
+                tag = f"density {dens:.3f} (bin {rb[0]})" if rho is None else f"density {rho}"
+                log(f"[lut] block {bq}x{bk} {tag} {lay} L={L} H={Hs} fill {fill:.3f} fill2 {fill2:.3f}: "
+                    + ", ".join(f"{vname(x)} {t:.4f} ms" for x, t in tt.items()))
+                notes.append(f"block {bq}x{bk} rho={rho if rho is not None else round(dens, 3)} {lay} L={L} H={Hs} "
+                             f"fill={fill:.3f} fill2={fill2:.3f}: " + " ".join(f"{vname(x)}={t:.4f}ms" for x, t in tt.items()))
             for rho, (dlo, dhi) in DENSITY_BINS:
-                groups = {}
-                for li, lay in enumerate(layouts):
-                    w = wl.block_request(f"lut_{bq}x{bk}_{rho}_{lay}", 9, li, bq, bk, rho, lay, H, T, Hg, Wg, d)
-                    hp = plan_workload(w, device=-1)
-                    fill = hp.info()["mask_fill"]
-                    hp.close()
-                    tt = time_regimes(bsa, torch, w, TILE_REGIMES, q, k, v, o, args.reps)
-                    g = groups.setdefault(fill_bin(fill), {})
-                    for x, t in tt.items():
-                        g[x] = g.get(x, 0.0) + t
-                    log(f"[lut] block {bq}x{bk} density {rho} {lay} L={L} fill {fill:.3f}: "
-                        + ", ".join(f"{vname(x)} {t:.4f} ms" for x, t in tt.items()))
-                    notes.append(f"block {bq}x{bk} rho={rho} {lay} L={L} H={H} fill={fill:.3f}: "
-                                 + " ".join(f"{vname(x)}={t:.4f}ms" for x, t in tt.items()))
-                rules += block_rules(bq, bk, dlo, dhi, llo, lhi, groups)
+                rules += block_rules(bq, bk, dlo, dhi, llo, lhi, groups[(rho, (dlo, dhi))])
         # slice masks: the gather regime is fixed by the slice height; the task
         # order is timed on the middle length bin (the key lists of the largest
         # one take gigabytes to generate) and applies to every length
@@ -206,16 +231,17 @@ def main():
     rules += slice_rules or [f"slice   {m:<7d} 1       0          1          -1      1       0      9999999999 {r} xcd"
                              for m, r in SLICE_RULES]
     # anything not covered (other block shapes): the default tile regime
-    rules.append("block   *       *       0          1          0       1       0      9999999999 0 xcd")
+    rules.append("block   *       *       0          1          0       1       0       1       0      9999999999 0 xcd")
     rules.append("video   *       *       -1         1          -1      1       0      9999999999 0 xcd")
     head = [
         "# Regime lookup table for gfx950 (MI355X), built by lut/build_lut.py (offline profiling).",
         "# First matching rule wins. Regimes: 0 = 128x64 tiles (4 waves), 1 = 64x64 tiles (2 waves),",
         "# 2 = 64-query gather, 3 = 128-query gather, 4 = 256x64 tiles (8 waves).",
         "# Task orders: xcd = longest first, grouped so neighbouring query tiles share an XCD; lpt = longest first.",
-        "# Features: density = kept blocks / blocks; fill = kept pairs / pairs of the non-empty 128x64 tiles.",
+        "# Features: density = kept blocks / blocks; fill = kept pairs / pairs of the non-empty 128x64 tiles;",
+        "# fill2 = the same over 256x64 tiles. Block lines carry the fill2 range; other lines match any fill2.",
         f"# Synthetic requests, d = {d}, bf16; median of 3 interleaved rounds of {args.reps} forwards.",
-        "# kind  block_q block_k density_lo density_hi fill_lo fill_hi L_lo   L_hi       regime order",
+        "# kind  block_q block_k density_lo density_hi fill_lo fill_hi [fill2_lo fill2_hi] L_lo   L_hi       regime order",
     ]
     text = "\n".join(head + rules + ["#", "# measurements:"] + ["# " + n for n in notes]) + "\n"
     with open(args.out, "w") as f:

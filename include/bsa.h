@@ -159,6 +159,9 @@ typedef struct {
                                       from every 4th 128-row query tile); -1 when
                                       the kind has none (video; fill of slices)  */
     double mask_fill;
+    double mask_fill2;             /* fill over the non-empty 256 x 64 tiles (the
+                                      256-row tiles that start at the sampled
+                                      128-row tiles); -1 as mask_fill          */
 } bsa_plan_info_t;
 
 typedef struct {

@@ -189,6 +189,14 @@ def test_lookup_table_file(tmp_path):
     f.write_text("block 64 64 0 1 0 0.5 0 99999 1\nblock 64 64 0 1 0.5 1 0 99999 4\n")
     info = bsa.plan(bsa.MASK_BLOCK_U8, 1, 2, 256, 64, 64, 64, data=m, lut_path=str(f), device=-1).info()
     assert info["regime"] == (1 if info["mask_fill"] < 0.5 else 4)
+    # a line with a fill2 range (fill over 256-row tiles) between fill and length
+    f.write_text("block 64 64 0 1 0 1 0 0.5 0 99999 1\nblock 64 64 0 1 0 1 0.5 1 0 99999 4\n")
+    info = bsa.plan(bsa.MASK_BLOCK_U8, 1, 2, 256, 64, 64, 64, data=m, lut_path=str(f), device=-1).info()
+    assert 0 <= info["mask_fill2"] <= 1
+    assert info["regime"] == (1 if info["mask_fill2"] < 0.5 else 4)
+    f.write_text("block 64 64 0 1 0 1 0 1 0 99999\n")
+    expect(bsa.ERR_INVALID_ARGUMENT, bsa.plan, bsa.MASK_BLOCK_U8, 1, 2, 256, 64, 64, 64, data=m, lut_path=str(f),
+           device=-1, match="malformed")
     expect(bsa.ERR_INVALID_ARGUMENT, bsa.plan, bsa.MASK_BLOCK_U8, 1, 2, 256, 64, 64, 64, data=m,
            lut_path=str(tmp_path / "nope"), device=-1)
     # the optional order column; an explicit task_order option overrides it

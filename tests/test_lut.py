@@ -71,13 +71,14 @@ def test_every_dense_bin_resolves_to_a_tile_regime():
 
 
 def _features_by_definition(block, L, bq, bk, stride):
-    """Density and fill written out from their definitions with numpy:
+    """Density and fills written out from their definitions with numpy:
     density = kept blocks / blocks of the sampled logical rows; fill = kept
     pairs / pairs of the non-empty 128 x 64 tiles, over every stride-th
-    128-row query tile of every head."""
+    128-row query tile of every head; fill2 = the same over the 256 x 64
+    tiles that start at those rows (every 256-row tile when stride is 1)."""
     B, H, nqb, nkb = block.shape
     kept_blocks = blocks = 0
-    kept_pairs = exec_pairs = 0.0
+    kept_pairs = exec_pairs = kept2 = exec2 = 0.0
     qlen = np.minimum(np.arange(1, nqb + 1) * bq, L) - np.arange(nqb) * bq
     nqt, nkt = -(-L // 128), -(-L // 64)
     for bh in range(B * H):
@@ -92,14 +93,19 @@ def _features_by_definition(block, L, bq, bk, stride):
             kept_pairs += float(sub.sum())
             tiles = np.pad(sub.any(axis=0), (0, nkt * 64 - L)).reshape(nkt, 64).any(axis=1)
             exec_pairs += float(tiles.sum()) * (q1 - q0) * 64
-    return kept_blocks / blocks, kept_pairs / exec_pairs
+        for q0 in range(0, L, 256 * (1 if stride == 1 else stride // 2)):
+            sub = el[q0:q0 + 256]
+            kept2 += float(sub.sum())
+            tiles = np.pad(sub.any(axis=0), (0, nkt * 64 - L)).reshape(nkt, 64).any(axis=1)
+            exec2 += float(tiles.sum()) * sub.shape[0] * 64
+    return kept_blocks / blocks, kept_pairs / exec_pairs, kept2 / exec2
 
 
 @pytest.mark.parametrize("bq,bk", [(32, 32), (64, 64), (128, 128), (64, 256), (256, 32)])
 @pytest.mark.parametrize("layout", ["random", "banded"])
 def test_mask_features_match_definition(bq, bk, layout):
-    """The planner's regime features (bsa_plan_info mask_density and
-    mask_fill) equal their definitions, on masks short enough that every
+    """The planner's regime features (bsa_plan_info mask_density, mask_fill
+    and mask_fill2) equal their definitions, on masks short enough that every
     query tile is sampled and on longer ones where every 4th is; random
     layouts of small blocks have low fill, banded ones high."""
     _lib()
@@ -114,9 +120,12 @@ def test_mask_features_match_definition(bq, bk, layout):
             m = np.broadcast_to((np.abs(cq[:, None] - ck[None, :]) <= 300)[None, None], (1, 2, nqb, nkb)).astype(np.uint8)
         info = bsa.plan(bsa.MASK_BLOCK_U8, 1, 2, L, 64, bq, bk, data=np.ascontiguousarray(m), device=-1).info()
         stride = 4 if -(-L // 128) >= 16 else 1
-        dens, fill = _features_by_definition(m, L, bq, bk, stride)
+        dens, fill, fill2 = _features_by_definition(m, L, bq, bk, stride)
         assert abs(info["mask_density"] - dens) < 1e-12, (L, info["mask_density"], dens)
         assert abs(info["mask_fill"] - fill) < 1e-9, (L, info["mask_fill"], fill)
+        assert abs(info["mask_fill2"] - fill2) < 1e-9, (L, info["mask_fill2"], fill2)
+        if stride == 1:  # same rows: a 256-row tile computes at least its halves' pairs
+            assert info["mask_fill2"] <= info["mask_fill"] + 1e-12
     if layout == "banded":
         assert info["mask_fill"] > 0.75
     elif bq < 128 or bk < 64:

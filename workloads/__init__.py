@@ -385,17 +385,24 @@ def tessera(i: int, H=24, T=21, Hg=45, Wg=80, d=128, cfg=4) -> Workload:
     return block_request(f"tessera{i}", cfg, i, bq, bk, rho, lay, H, T, Hg, Wg, d)
 
 
-def highres(H=24, T=21, Hg=90, Wg=160, d=128, blk=128, cfg=5) -> Workload:
-    """High-res: half the heads spatial (frame-major), half temporal
-    (temporal-major); 128x128 logical blocks rasterised from the patterns."""
+def video_block_request(name, cfg, bq, bk, H, T, Hg, Wg, d) -> Workload:
+    """A BLOCK-mask request whose blocks are the video head patterns
+    rasterised at bq x bk: heads 0..H/2-1 spatial in frame-major order, the
+    rest temporal in temporal-major order."""
     L = T * Hg * Wg
-    w = Workload("highres", cfg, 1, H, L, d, T, Hg, Wg, BLOCK, blk, blk)
+    w = Workload(name, cfg, 1, H, L, d, T, Hg, Wg, BLOCK, bq, bk)
     ns = H // 2
-    sp = rasterize_video_block_mask(T, Hg, Wg, SPATIAL, FRAME_MAJOR, blk, blk)
-    tp = rasterize_video_block_mask(T, Hg, Wg, TEMPORAL, TEMPORAL_MAJOR, blk, blk)
+    sp = rasterize_video_block_mask(T, Hg, Wg, SPATIAL, FRAME_MAJOR, bq, bk)
+    tp = rasterize_video_block_mask(T, Hg, Wg, TEMPORAL, TEMPORAL_MAJOR, bq, bk)
     w.block = np.stack([sp] * ns + [tp] * (H - ns))[None]
     w.head_layout = np.array([FRAME_MAJOR] * ns + [TEMPORAL_MAJOR] * (H - ns), np.uint8)
     return w
+
+
+def highres(H=24, T=21, Hg=90, Wg=160, d=128, blk=128, cfg=5) -> Workload:
+    """High-res: half the heads spatial (frame-major), half temporal
+    (temporal-major); 128x128 logical blocks rasterised from the patterns."""
+    return video_block_request("highres", cfg, blk, blk, H, T, Hg, Wg, d)
 
 
 # ----------------------------------------------------------------------------
