@@ -928,7 +928,22 @@ static MaskFeatures mask_features(const bsa_mask_desc_t &m, int32_t B, int32_t H
         std::vector<uint64_t> rowbuf((size_t)words), uni((size_t)words), uni2((size_t)words), tiles((size_t)twords);
         Acc a;
         // the non-empty 64-key tiles of a union of keep-bit rows
-        auto count_tiles = [&](const std::vector<uint64_t> &u) {
+        auto count_tiles = [&](const std::vector<uint64_t> &u) -> int64_t {
+            int64_t nt = 0;
+            if (bk == 32 || bk == 64) {
+                // a tile holds two key blocks (bit pairs) or one (bits)
+                for (int64_t w = 0; w < words; ++w)
+                    nt += __builtin_popcountll(bk == 64 ? u[w] : (u[w] | (u[w] >> 1)) & 0x5555555555555555ull);
+                return nt;
+            }
+            if (bk % kTileK == 0) {
+                // a block covers bk / 64 whole tiles; the last block only those before L
+                for (int64_t w = 0; w < words; ++w) nt += __builtin_popcountll(u[w]);
+                nt *= bk / kTileK;
+                if ((u[(nkb - 1) >> 6] >> ((nkb - 1) & 63)) & 1)
+                    nt -= bk / kTileK - (last_w + kTileK - 1) / kTileK;
+                return nt;
+            }
             std::fill(tiles.begin(), tiles.end(), 0ull);
             for (int64_t w = 0; w < words; ++w)
                 for (uint64_t x = u[w]; x; x &= x - 1) {
@@ -936,7 +951,6 @@ static MaskFeatures mask_features(const bsa_mask_desc_t &m, int32_t B, int32_t H
                     const int64_t k_lo = kb * bk, k_hi = std::min<int64_t>(k_lo + bk, L) - 1;
                     for (int64_t tk = k_lo / kTileK; tk <= k_hi / kTileK; ++tk) tiles[tk >> 6] |= 1ull << (tk & 63);
                 }
-            int64_t nt = 0;
             for (int64_t w = 0; w < twords; ++w) nt += __builtin_popcountll(tiles[w]);
             return nt;
         };
