@@ -184,29 +184,41 @@ static bool parse_lut(const std::string &text, std::vector<LutRule> &rules, std:
         const std::string &bq = tok[1], &bk = tok[2];
         r.f2lo = 0.0;
         r.f2hi = 1.0;
+        // every numeric field must be a whole number token
+        auto real = [](const std::string &t) {
+            size_t used = 0;
+            const double v = std::stod(t, &used);
+            if (used != t.size()) throw std::invalid_argument(t);
+            return v;
+        };
+        auto whole = [](const std::string &t) {
+            size_t used = 0;
+            const long long v = std::stoll(t, &used);
+            if (used != t.size()) throw std::invalid_argument(t);
+            return v;
+        };
         try {
             size_t i = 3;
-            r.dlo = std::stod(tok[i++]);
-            r.dhi = std::stod(tok[i++]);
-            r.flo = std::stod(tok[i++]);
-            r.fhi = std::stod(tok[i++]);
+            r.dlo = real(tok[i++]);
+            r.dhi = real(tok[i++]);
+            r.flo = real(tok[i++]);
+            r.fhi = real(tok[i++]);
             if (has_f2) {
-                r.f2lo = std::stod(tok[i++]);
-                r.f2hi = std::stod(tok[i++]);
+                r.f2lo = real(tok[i++]);
+                r.f2hi = real(tok[i++]);
             }
-            r.Llo = std::stoll(tok[i++]);
-            r.Lhi = std::stoll(tok[i++]);
-            size_t used = 0;
-            r.regime = std::stoi(tok[i], &used);
-            if (used != tok[i].size()) throw std::invalid_argument("regime");
+            r.Llo = whole(tok[i++]);
+            r.Lhi = whole(tok[i++]);
+            const long long reg = whole(tok[i]);
+            if (reg < 0 || reg >= kNumRegimes) {
+                err = "lookup table line " + std::to_string(ln) + ": regime out of range";
+                return false;
+            }
+            r.regime = (int)reg;
+            r.bq = bq == "*" ? 0 : (int)whole(bq);
+            r.bk = bk == "*" ? 0 : (int)whole(bk);
         } catch (const std::exception &) {
             err = "lookup table line " + std::to_string(ln) + " malformed";
-            return false;
-        }
-        r.bq = bq == "*" ? 0 : std::atoi(bq.c_str());
-        r.bk = bk == "*" ? 0 : std::atoi(bk.c_str());
-        if (r.regime < 0 || r.regime >= kNumRegimes) {
-            err = "lookup table line " + std::to_string(ln) + ": regime out of range";
             return false;
         }
         rules.push_back(r);

@@ -197,6 +197,11 @@ def test_lookup_table_file(tmp_path):
     f.write_text("block 64 64 0 1 0 1 0 1 0 99999\n")
     expect(bsa.ERR_INVALID_ARGUMENT, bsa.plan, bsa.MASK_BLOCK_U8, 1, 2, 256, 64, 64, 64, data=m, lut_path=str(f),
            device=-1, match="malformed")
+    for bad in ("block 64 64 0 1 0.5x 1 0 99999 1", "block 64x 64 0 1 0 1 0 99999 1", "block 64 64 0 1 0 1 0 99999 1.5",
+                "block 64 64 0 1 0 1 0 99999 7"):
+        f.write_text(bad + "\n")
+        expect(bsa.ERR_INVALID_ARGUMENT, bsa.plan, bsa.MASK_BLOCK_U8, 1, 2, 256, 64, 64, 64, data=m, lut_path=str(f),
+               device=-1, match="malformed|out of range")
     expect(bsa.ERR_INVALID_ARGUMENT, bsa.plan, bsa.MASK_BLOCK_U8, 1, 2, 256, 64, 64, 64, data=m,
            lut_path=str(tmp_path / "nope"), device=-1)
     # the optional order column; an explicit task_order option overrides it
