@@ -327,6 +327,9 @@ def main():
                          "fgattn_M64, fgattn_M128, tessera0..tessera47, highres)")
     ap.add_argument("--units", action="store_true",
                     help="instead of the headline, run the unit microbenchmarks (MFMA, vector, LDS, HBM rates)")
+    ap.add_argument("--occupancy", default=None, metavar="NAMES",
+                    help="instead of the headline, stamped forwards of the named configurations (comma list, as "
+                         "--configs): busy share of the workgroup slots, tail, shader clock per XCD class")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes 5 times (HBM counter calibration)")
     args = ap.parse_args()
@@ -362,6 +365,12 @@ def main():
     if args.units:
         for rec in unit_benchmarks():
             print(json.dumps(rec), flush=True)
+        return
+    if args.occupancy:
+        unknown = set(args.occupancy.split(",")) - KNOWN_CONFIGS
+        if unknown:
+            ap.error(f"--occupancy takes configuration names (unknown: {sorted(unknown)})")
+        occupancy(torch, wl, args.occupancy.split(","))
         return
 
     from bsa_helpers import to_device_bf16
@@ -601,6 +610,76 @@ def all_configs(torch, wl, only=None):
             total += rec["fwd_ms_median"]
     if only is None:
         print(json.dumps({"config": "tessera_request", "masks": 48, "sum_fwd_ms_median": round(total, 2)}), flush=True)
+
+
+# ---------------------------------------------------------------------------
+# launch occupancy from per-task clock stamps (--occupancy)
+# ---------------------------------------------------------------------------
+
+def config_workload(wl, name):
+    """The workload of a configuration name (the names --configs takes)."""
+    if name.startswith("tessera"):
+        return wl.tessera(int(name[7:]))
+    if name.startswith("fgattn_M"):
+        w = wl.fgattn(M=int(name[8:]))
+        w.name = name
+        return w
+    return {"tiny": wl.tiny, "svgA": lambda: wl.svg("A"), "svgB": lambda: wl.svg("B"), "highres": wl.highres}[name]()
+
+
+def occupancy(torch, wl, names, launches=3):
+    """Per configuration, `launches` stamped forwards (after four plain ones)
+    on device-random N(0,1) inputs: the launch span, the share of the
+    workgroup slots' time spent in tasks (slots = the most tasks ever running
+    at once), the share of the span at its end during which fewer than 90% of
+    the slots run, and per class of workgroup index mod 8 (the XCD the
+    hardware deals the workgroup to) the shader clock and the time its last
+    task ends. One JSON line per launch."""
+    import numpy as np
+    import block_sparse_attention_fwd_amd as bsa
+    from bsa_helpers import plan_workload
+    for name in names:
+        w = config_workload(wl, name)
+        g = torch.Generator(device="cuda:0")
+        g.manual_seed(5)
+        q, k, v = (torch.randn((w.B, w.H, w.L, w.d), generator=g, device="cuda:0").to(torch.bfloat16) for _ in range(3))
+        o = torch.empty_like(q)
+        p = plan_workload(w)
+        info = p.info()
+        n = info["workgroups"]
+        for _ in range(4):
+            bsa.forward(p, q, k, v, o)
+        for rep in range(launches):
+            stamps = torch.zeros(4 * n, dtype=torch.int64, device="cuda:0")
+            bsa.forward_stamped(p, q, k, v, o, stamps)
+            torch.cuda.synchronize()
+            s = stamps.cpu().numpy().reshape(-1, 4).astype(np.float64)
+            idx = np.arange(n)
+            ok = (s[:, 3] > s[:, 1]) & (s[:, 2] > s[:, 0])
+            s, idx = s[ok], idx[ok]
+            st, en = s[:, 1] / 100.0, s[:, 3] / 100.0  # microseconds
+            t0 = st.min()
+            st, en = st - t0, en - t0
+            span = float(en.max())
+            ev = np.concatenate([np.stack([st, np.ones_like(st)], 1), np.stack([en, -np.ones_like(en)], 1)])
+            ev = ev[np.lexsort((ev[:, 1], ev[:, 0]))]  # at equal times, ends before starts
+            running = np.cumsum(ev[:, 1])
+            slots = int(running.max())
+            busy = float((en - st).sum() / (slots * span))
+            full = np.where(running >= 0.9 * slots)[0]
+            tail = span - float(ev[full[-1], 0]) if full.size else span
+            cls = idx % 8
+            clk = [float((s[cls == c, 2] - s[cls == c, 0]).sum() / (s[cls == c, 3] - s[cls == c, 1]).sum() * 0.1)
+                   for c in range(8)]
+            rec = {"config": name, "launch": rep, "regime": info["regime"], "tasks": int(s.shape[0]),
+                   "span_ms": round(span / 1000, 4), "slots": slots, "busy_share": round(busy, 4),
+                   "tail_share_below_90pct": round(tail / span, 4),
+                   "clock_ghz_by_index_mod_8": [round(c, 3) for c in clk],
+                   "last_end_ms_by_index_mod_8": [round(float(en[cls == c].max()) / 1000, 3) for c in range(8)]}
+            print(json.dumps(rec), flush=True)
+        p.close()
+        del q, k, v, o
+        torch.cuda.empty_cache()
 
 
 if __name__ == "__main__":
