@@ -480,7 +480,7 @@ def main():
         "plan": r["plan_info"],
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": MI355X_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MI355X_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
-                     "kernel": "bsa_fwd_bf16<4,1,128,2>", "flops_per_launch": flops},
+                     "kernel": "bsa_fwd_bf16<4,1,128,2,kModeBlock>", "flops_per_launch": flops},
         "clock": dict(clock, mfma_peak_at_clock_tflops=round(MFMA_TFLOPS_PER_GHZ * clock["ghz"], 1),
                       frac_of_mfma_peak_at_clock=round(achieved / (MFMA_TFLOPS_PER_GHZ * clock["ghz"]), 4)),
         "classes": class_out,

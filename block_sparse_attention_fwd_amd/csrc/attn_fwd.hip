@@ -129,7 +129,9 @@ __device__ __forceinline__ bf16x8 load_bf16x8(const __bf16 *p)
 // Kernel: NW waves per workgroup, each wave owns RB consecutive blocks of 32
 // query rows. Every K operand read from LDS feeds RB score MFMAs and every V
 // operand read feeds RB output MFMAs, so LDS bytes per MFMA fall as 1/RB.
-template <int NW, int RB, int D, int NB = 2>
+// MODE is the plan's MaskMode: each mode gets its own build, free of the
+// others' record, copy and mask code.
+template <int NW, int RB, int D, int NB, int MODE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1 && (NW >= 4 || NB == 1) ? 2 : 1, RB == 1 ? 2 : 1))) void bsa_fwd_bf16(KernelArgs a)
 {
     using C = Cfg<NW, RB, D>;
@@ -188,8 +190,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1
     }
 
     const int ntile = task.te - task.tb;
-    const bool gather = a.mode == kModeGather;
-    const bool video = a.mode == kModeVideo;
+    constexpr bool gather = MODE == kModeGather;
+    constexpr bool video = MODE == kModeVideo;
 
     // Softmax reference: a row takes the maximum of its first kept scores as
     // reference and keeps it; the per-tile row maximum is computed only while
@@ -347,7 +349,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1
 
             // A PARTIAL tile may keep no pair of this wave's rows: the wave
             // skips it (and still takes its part in the copies and barriers)
-            if (!wave_skips_tile(a, rec.aux, w)) {
+            if (!wave_skips_tile(a, MODE, rec.aux, w)) {
             // ---- S^T = K Q^T: s0 = keys 0..31, s1 = keys 32..63 of each row block
             const unsigned char *kt = ksm[cur];
             f32x16 s0[RB], s1[RB];
@@ -371,7 +373,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1
             __builtin_amdgcn_sched_group_barrier(0x008, 4 * RB, 0);
 
             // ---- exact mask on PARTIAL tiles only
-            if (wave_masks_tile(a, rec.aux, w)) mask_partial_tile<RB>(s0, s1, a, rec.k0, rec.aux, video, pat, LDS_PTR(const int, &kcoord[cur][4 * hf]), qt, qwin, 32 * w * RB, hf);
+            if (wave_masks_tile(MODE, rec.aux, w)) mask_partial_tile<RB>(s0, s1, a, MODE, rec.k0, rec.aux, pat, LDS_PTR(const int, &kcoord[cur][4 * hf]), qt, qwin, 32 * w * RB, hf);
 
             // ---- online softmax per row block
             u32x4 pk[RB][4];  // bf16 pairs, one cvt_pk each
@@ -503,10 +505,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RB == 1
     }
 }
 
+// one kernel build per (NW, RB, D, NB, mask mode); the plan's mode picks it
 template <int NW, int RB, int D, int NB = 2>
 static hipError_t launch(const KernelArgs &a, hipStream_t stream)
 {
-    hipLaunchKernelGGL((bsa_fwd_bf16<NW, RB, D, NB>), dim3(a.ntasks), dim3(NW * 64), 0, stream, a);
+    const dim3 grid(a.ntasks), block(NW * 64);
+    if (a.mode == kModeVideo) {
+        hipLaunchKernelGGL((bsa_fwd_bf16<NW, RB, D, NB, kModeVideo>), grid, block, 0, stream, a);
+    } else if (a.mode == kModeGather) {
+        if constexpr (NB == 3) return hipErrorInvalidValue;  // gathered tiles keep two buffers at most
+        else hipLaunchKernelGGL((bsa_fwd_bf16<NW, RB, D, NB, kModeGather>), grid, block, 0, stream, a);
+    } else {
+        hipLaunchKernelGGL((bsa_fwd_bf16<NW, RB, D, NB, kModeBlock>), grid, block, 0, stream, a);
+    }
     return hipGetLastError();
 }
 

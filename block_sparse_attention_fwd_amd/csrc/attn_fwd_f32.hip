@@ -115,7 +115,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
             __syncthreads();
 
             // a PARTIAL tile may keep no pair of this wave's rows
-            if (wave_skips_tile(a, rec.aux, w)) continue;
+            if (wave_skips_tile(a, a.mode, rec.aux, w)) continue;
             // ---- S^T = K Q^T for keys 0..31 (s0) and 32..63 (s1)
             f32x16 s0[1], s1[1];
             s0[0] = zero16;
@@ -130,8 +130,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
             }
 
             // ---- exact mask on PARTIAL tiles only
-            if (wave_masks_tile(a, rec.aux, w))
-                mask_partial_tile<1>(s0, s1, a, rec.k0, rec.aux, video, pat, LDS_PTR(const int, &kcoord[4 * hf]), qt,
+            if (wave_masks_tile(a.mode, rec.aux, w))
+                mask_partial_tile<1>(s0, s1, a, a.mode, rec.k0, rec.aux, pat, LDS_PTR(const int, &kcoord[4 * hf]), qt,
                                      qwin, 32 * w, hf);
 
             // ---- online softmax (reference max moves only by more than kSlack)

@@ -139,26 +139,27 @@ struct RecordStream {
 };
 
 // Per-wave refinement of a PARTIAL tile for wave w (query rows 32w..32w+31 of
-// the task); both are wave-uniform.
+// the task); both are wave-uniform. `mode` is the plan's MaskMode (a
+// compile-time constant where the kernel is built for one mode).
 //  - skip: the wave's rows keep no pair of the tile. Video tiles carry the bit
 //    from the plan; block tiles whose sub-block rows are at least 32 queries
 //    tall read it from the sub-block keep bits of the wave's sub-block row.
 //  - mask: the wave's rows need the exact predicate (video tiles carry a bit
 //    for rows that keep every pair).
-__device__ __forceinline__ bool wave_skips_tile(const KernelArgs &a, uint32_t aux, int w)
+__device__ __forceinline__ bool wave_skips_tile(const KernelArgs &a, int mode, uint32_t aux, int w)
 {
     if (!(aux & kPartial)) return false;
-    if (a.mode == kModeVideo) return (aux >> w) & 1u;
-    if (a.mode == kModeBlock && a.bq_shift >= 5) {
+    if (mode == kModeVideo) return (aux >> w) & 1u;
+    if (mode == kModeBlock && a.bq_shift >= 5) {
         const int sq = (kWaveRows * w) >> a.bq_shift;
         return ((aux >> (sq * a.nsk)) & ((1u << a.nsk) - 1u)) == 0u;
     }
     return false;
 }
-__device__ __forceinline__ bool wave_masks_tile(const KernelArgs &a, uint32_t aux, int w)
+__device__ __forceinline__ bool wave_masks_tile(int mode, uint32_t aux, int w)
 {
     if (!(aux & kPartial)) return false;
-    if (a.mode == kModeVideo) return !((aux >> (kWaveFullShift + w)) & 1u);
+    if (mode == kModeVideo) return !((aux >> (kWaveFullShift + w)) & 1u);
     return true;
 }
 
@@ -174,11 +175,11 @@ __device__ __forceinline__ bool wave_masks_tile(const KernelArgs &a, uint32_t au
 //    key < L;
 //  - gather: key slot < the record's count.
 template <int RB>
-__device__ __forceinline__ void mask_partial_tile(f32x16 (&s0)[RB], f32x16 (&s1)[RB], const KernelArgs &a,
-                                                  int rec_k0, uint32_t rec_aux, bool video, int pat, const __attribute__((address_space(3))) int *kc,
+__device__ __forceinline__ void mask_partial_tile(f32x16 (&s0)[RB], f32x16 (&s1)[RB], const KernelArgs &a, int mode,
+                                                  int rec_k0, uint32_t rec_aux, int pat, const __attribute__((address_space(3))) int *kc,
                                                   const int (&qt)[RB], const unsigned (&qwin)[RB], int wrow0, int hf)
 {
-    if (video) {
+    if (mode == kModeVideo) {
         const unsigned win2 = 2u * (unsigned)a.radius;
         if (pat == 1) {
 #pragma unroll
@@ -224,7 +225,7 @@ __device__ __forceinline__ void mask_partial_tile(f32x16 (&s0)[RB], f32x16 (&s1)
         return;
     }
     // keep bits of key slots 0..31 (lo) and 32..63 (hi) for each row block
-    const int kmax = a.mode == kModeBlock ? a.L - rec_k0 : (int)(rec_aux & kAuxMask);
+    const int kmax = mode == kModeBlock ? a.L - rec_k0 : (int)(rec_aux & kAuxMask);
     uint32_t vlo = ~0u, vhi = ~0u;  // slots >= kmax: past the sequence / list end
     if (kmax < 64) {
         vlo = kmax >= 32 ? ~0u : ((1u << max(kmax, 0)) - 1u);
@@ -233,7 +234,7 @@ __device__ __forceinline__ void mask_partial_tile(f32x16 (&s0)[RB], f32x16 (&s1)
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         uint32_t lo = vlo, hi = vhi;
-        if (a.mode == kModeBlock) {
+        if (mode == kModeBlock) {
             // logical blocks are at least 32 queries tall, so a 32-row block
             // (rows wrow0 + 32 rb .. + 31 of the task) lies in one sub-block row
             const int sq = (wrow0 + 32 * rb) >> a.bq_shift;
