@@ -174,3 +174,35 @@ def sample_rows(w, per_head=64, seed=0, tile=128):
             rows.append(base + g.choice(w.L, per_head, replace=False))
             rows.append(base + np.array([0, w.L - 1]))
     return np.unique(np.concatenate(rows)).astype(np.int64)
+
+
+def short_cases():
+    """Sequences shorter than, equal to and just past one tile: BLOCK masks of
+    1 to 127 tokens (32x32, 64x64 and 128x32 blocks, the diagonal kept in one
+    head), video masks on 1x1x1, 2x3x5 and 3x1x7 grids (spatial, temporal in
+    temporal-major order, dense), slice lists of 1 to 65 tokens with an empty
+    list."""
+    g = np.random.default_rng(41)
+    out = []
+    for L in (1, 17, 40, 64, 65, 127):
+        for (bq, bk) in ((32, 32), (64, 64), (128, 32)):
+            w = wl.Workload(f"short_blk{bq}x{bk}_L{L}", 140 + L, 1, 2, L, 64, 0, 0, 0, wl.BLOCK, bq, bk)
+            w.block = (g.random((1, 2, w.nqb, w.nkb)) < 0.6).astype(np.uint8)
+            w.block[0, 0] |= np.eye(w.nqb, w.nkb, dtype=np.uint8)
+            out.append(w)
+    for (T, Hg, Wg) in ((1, 1, 1), (2, 3, 5), (3, 1, 7)):
+        w = wl.svg("B", H=3, T=T, Hg=Hg, Wg=Wg, d=64)
+        w.name = f"short_video_{T}x{Hg}x{Wg}"
+        w.head_pattern = np.array([wl.SPATIAL, wl.TEMPORAL, wl.DENSE], np.uint8)
+        w.head_layout = np.array([0, 1, 1], np.uint8)
+        w.radius = 1
+        out.append(w)
+    for L in (1, 40, 65):
+        for M in (64, 128):
+            w = wl.Workload(f"short_slice_M{M}_L{L}", 150 + L, 1, 2, L, 64, 0, 0, 0, wl.SLICE, M, 1)
+            lists = [np.flatnonzero(g.random(L) < 0.5).astype(np.int32) for _ in range(2 * w.nqb)]
+            lists[-1] = np.zeros(0, np.int32)  # a query block with an empty list
+            w.row_ptr = np.concatenate([[0], np.cumsum([x.size for x in lists])]).astype(np.int64)
+            w.col_idx = np.concatenate(lists).astype(np.int32)
+            out.append(w)
+    return out

@@ -22,7 +22,7 @@ def _gpu():
 
 import block_sparse_attention_fwd_amd as bsa  # noqa: E402
 from bsa_helpers import plan_workload  # noqa: E402
-from gpu_util import compare, log, run_gpu, sample_rows, thick_rows, to_device  # noqa: E402
+from gpu_util import compare, log, run_gpu, sample_rows, short_cases, thick_rows, to_device  # noqa: E402
 
 
 def _small_block_cases():
@@ -99,6 +99,15 @@ def test_batch_of_two(regime):
         log(f"[case] {w.name} regime={regime}")
         O, _ = run_gpu(w, Q, K, V, force_regime=regime)
         compare(w, Q, K, V, O, label=f"{w.name} r{regime}")
+
+
+@pytest.mark.parametrize("w", short_cases(), ids=lambda w: w.name)
+def test_short_sequences(w):
+    Q, K, V = wl.make_qkv(w)
+    for regime in ((-1,) if w.kind == wl.SLICE else (0, 1, 4)):
+        log(f"[case] {w.name} regime={regime}")
+        O, p = run_gpu(w, Q, K, V, force_regime=regime)
+        compare(w, Q, K, V, O, label=f"{w.name} r{p.info()['regime']}")
 
 
 @pytest.mark.parametrize("M", [64, 128])

@@ -20,7 +20,7 @@ def _gpu():
     bsa.lib()  # fail loudly if the library is missing
 
 
-from gpu_util import compare_f32, log, run_gpu, sample_rows, thick_rows  # noqa: E402
+from gpu_util import compare_f32, log, run_gpu, sample_rows, short_cases, thick_rows  # noqa: E402
 
 
 @pytest.mark.parametrize("regime", [-1, 0, 1, 4])
@@ -70,6 +70,16 @@ def test_small_slices_f32(M):
     log(f"[case] f32 slices M={M}")
     O, _ = run_gpu(w, Q, K, V)
     compare_f32(w, Q, K, V, O, label=f"f32 slice M{M}")
+
+
+@pytest.mark.parametrize("w", short_cases(), ids=lambda w: w.name)
+def test_short_sequences_f32(w):
+    """The short sequences of the bf16 suite in the fp32 build."""
+    Q, K, V = wl.make_qkv(w, "f32")
+    for regime in ((-1,) if w.kind == wl.SLICE else (0, 1)):
+        log(f"[case] f32 {w.name} regime={regime}")
+        O, p = run_gpu(w, Q, K, V, force_regime=regime)
+        compare_f32(w, Q, K, V, O, label=f"f32 {w.name} r{p.info()['regime']}")
 
 
 def test_all_empty_mask_f32():
